@@ -1,0 +1,55 @@
+"""Byte accounting against the figures the pages print (tests/golden/memory_identity.json)."""
+import json
+import os
+
+import pytest
+
+from oracle import memory as M
+import oracle
+from mixed_precision_zero_amd import workloads as W
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "memory_identity.json")))
+GB = 1e9
+
+
+def _compute(case):
+    q = case["quantity"]
+    psi = case.get("psi")
+    if q == "total_per_param":
+        return M.TOTAL_BYTES
+    if q == "opt_state_fraction":
+        return M.OPT_STATE_BYTES / M.TOTAL_BYTES
+    if q == "total":
+        return M.total_bytes(psi) / GB
+    if q == "opt_state":
+        return M.optimizer_state_bytes(psi) / GB
+    if q == "zero1_opt_state_per_rank":
+        return M.zero1_optimizer_state_per_rank(psi, case["dp"]) / GB
+    if q == "total_over_dp":
+        return M.total_bytes(psi) / case["dp"] / GB
+    raise KeyError(q)
+
+
+@pytest.mark.parametrize("case", GOLD["cases"], ids=[c["what"] for c in GOLD["cases"]])
+def test_printed_figure(case):
+    got = _compute(case)
+    if "value_gb" in case:
+        assert abs(got - case["value_gb"]) <= case["display_tol_gb"], (got, case["source"])
+    else:
+        assert got == case["value"], (got, case["source"])
+
+
+def test_split_is_two_two_twelve():
+    assert (M.WEIGHT_BYTES, M.GRAD_BYTES, M.OPT_STATE_BYTES) == (2, 2, 12)
+    # ZeRO-1 keeps weights and gradients whole: per rank 4 + 12/D bytes per parameter
+    assert M.zero1_total_per_rank(8e9, 8) == (4 + 12 / 8) * 8e9
+
+
+def test_7b_shard_state():
+    """The 7B workload's rank-3 shard holds 12 * L bytes of fp32 state."""
+    w = W.LLAMA_7B
+    _, ln = oracle.get().shard_plan(w.numel, w.dp_size, w.rank)
+    L = int(ln.sum())
+    assert L == 842_301_952
+    assert M.shard_state_bytes(L) == 12 * 842_301_952        # 10.11 GB
+    assert abs(M.optimizer_state_bytes(w.total_params) / GB - 80.86) < 0.01

@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in a copy of the oracle; each must trip a pin.
+
+Each mutant is a textual edit of ``oracle/z1_oracle.c`` compiled with the
+oracle's own gcc flags into a temporary library.  A mutant that passes every
+pin would mean the pins cannot tell that mistake from the correct oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "plan_extra_to_rank_eq_rho": [("len[i] = q + (rank < rho ? 1 : 0);",
+                                   "len[i] = q + (rank <= rho ? 1 : 0);")],
+    "plan_start_max": [("(rank < rho ? rank : rho)", "(rank < rho ? rho : rank)")],
+    "plan_extra_to_last_ranks": [
+        ("len[i] = q + (rank < rho ? 1 : 0);",
+         "len[i] = q + (dp_size - 1 - rank < rho ? 1 : 0);"),
+        ("start[i] = (int64_t)rank * q + (rank < rho ? rank : rho);",
+         "start[i] = (int64_t)rank * q + (rank > dp_size - rho ? rank - (dp_size - rho) : 0);")],
+    "rne_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
+    "rne_truncate": [("kept += 1u;", "kept += 0u;")],
+    "rne_nan_not_quieted": [("| 0x0040u", "| 0x0000u"),
+                            ("(u & 0x007FFFFFu) != 0)", "(u & 0x007FFFFFu) != 0 && 0)")],
+    "acc_in_double": [("float a = bf16_to_f32(g[e]);", "double a = bf16_to_f32(g[e]);")],
+    "acc_drops_first": [("float a = bf16_to_f32(g[e]);", "float a = 0.0f;")],
+    "acc_drops_last": [("for (int32_t k = 1; k < K; ++k)", "for (int32_t k = 1; k < K - 1; ++k)")],
+    "norm_no_square": [("double x = a * a;", "double x = a;")],
+    "norm_in_float": [("double t = s + x;", "double t = (float)(s + x);")],
+    "norm_uncompensated": [("return s + err;", "return s;")],
+    "clip_no_eps": [("(sqrt(S) + 1e-6)", "(sqrt(S))")],
+    "clip_no_min": [("return c < 1.0 ? c : 1.0;", "return c;")],
+    "clip_uses_S": [("(sqrt(S) + 1e-6)", "(S + 1e-6)")],
+    "adamw_decay_without_lr": [("(1.0 - hp->lr * hp->weight_decay)", "(1.0 - hp->weight_decay)")],
+    "adamw_decay_after_update": [
+        ("pe = pe * (1.0 - hp->lr * hp->weight_decay);", ""),
+        ("pe = pe - hp->lr * mhat / (sqrt(vhat) + hp->eps);",
+         "pe = (pe - hp->lr * mhat / (sqrt(vhat) + hp->eps)) * (1.0 - hp->lr * hp->weight_decay);")],
+    "adamw_l2_not_decoupled": [("pe = pe * (1.0 - hp->lr * hp->weight_decay);",
+                                "g = g + hp->weight_decay * pe;")],
+    "adamw_beta_swap_m": [("me = hp->beta1 * me + (1.0 - hp->beta1) * g;",
+                           "me = hp->beta2 * me + (1.0 - hp->beta2) * g;")],
+    "adamw_beta_swap_v": [("ve = hp->beta2 * ve + (1.0 - hp->beta2) * g * g;",
+                           "ve = hp->beta1 * ve + (1.0 - hp->beta1) * g * g;")],
+    "adamw_eps_inside_sqrt": [("(sqrt(vhat) + hp->eps)", "sqrt(vhat + hp->eps)")],
+    "adamw_no_bias_correction_v": [("double vhat = ve / bc2;", "double vhat = ve;")],
+    "adamw_no_bias_correction_m": [("double mhat = me / bc1;", "double mhat = me;")],
+    "adamw_bias_power_off_by_one": [("pow(hp->beta1, t)", "pow(hp->beta1, t + 1.0)")],
+    "adamw_update_sign": [("pe = pe - hp->lr * mhat", "pe = pe + hp->lr * mhat")],
+    "adamw_ignores_clip": [("double g = c * (double)acc[e];", "double g = (double)acc[e];")],
+    "adamw_weight_from_old_master": [("w[e] = z1o_bf16_rne(p[e]);",
+                                      "w[e] = z1o_bf16_rne((float)(double)acc[e] * 0.0f + p[e] * 0.999f);")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle.SOURCE).read()
+    for old, new in MUTANTS[name]:
+        assert old in src, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    path = tmp_path / f"{name}.c"
+    path.write_text(src)
+    lib = oracle.build(str(path), str(tmp_path / f"lib{name}.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for check in pins.ALL:
+        try:
+            check(o)
+        except (AssertionError, ValueError) as e:
+            caught.append(check.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"
