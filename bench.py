@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Throughput of the ZeRO-1 shard optimizer step on one MI355X.
+
+One step = the whole path over one batch of synthetic input: K accumulation
+passes (z1_accum_grads), the norm (z1_grad_norm_sq) and the clipped AdamW
+with the bf16 cast (z1_adamw_step), all through the C ABI.  The default
+workload is the 7B Llama-shaped list at dp_size 8, rank 3 (842,301,952 shard
+elements, K = 4).  Inputs are generated on the device before timing and stay
+resident in HBM; every timed step does all of the work.
+
+Prints ONE JSON line (rank 0).  Besides the driver's fields it carries
+  roofline      the dominant kernel (AdamW) against the 8 TB/s HBM peak, with
+                algorithmic bytes per launch / its mean duration measured with
+                events on the launch stream;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, vendor figure
+BYTES_ADAMW = 30                 # read acc, p, m, v (16); write p, m, v (12) + bf16 (2)
+BYTES_ACC_FIRST = 6              # read bf16 g (2); write acc (4)
+BYTES_ACC_NEXT = 10              # read bf16 g (2) + acc (4); write acc (4)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "z1_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_elems (0 = library default)")
+    ap.add_argument("--max-blocks", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time spent timing the oracle (0 = skip)")
+    ap.add_argument("--copy-gb", type=float, default=4.0, help="probe-copy size for the ceiling")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the kernel source as it is now (else None)."""
+    path = os.path.join(PROFILE_DIR, f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        print("bench.py: the ZeRO-1 shard step here runs on one GPU; multi-GPU runs "
+              "(reduce-scatter / all-gather over RCCL) are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixed_precision_zero_amd import binding as B
+    from mixed_precision_zero_amd import workloads as W
+    from mixed_precision_zero_amd.shard import ShardStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+
+    t0 = time.time()
+    st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev,
+                   chunk_elems=args.chunk, max_blocks=args.max_blocks)
+    L = int(st.plan.info.shard_elems)
+    master_full = W.make_master(w, seed=0, device=dev)
+    st.scatter_to_arena(st.master, master_full)
+    for wt, mt in zip(st.weights, master_full):
+        wt.copy_(mt)
+    # a bounded sample for the CPU oracle: the first slices, in packed order
+    sample_target = 1 << 23
+    sample_idx = []
+    n_s = 0
+    for i, s, ln, _ in st.slices():
+        if ln and n_s < sample_target:
+            take = min(ln, sample_target - n_s)
+            sample_idx.append((i, s, take))
+            n_s += take
+    p_sample = torch.cat([master_full[i].reshape(-1)[s:s + n] for i, s, n in sample_idx]).cpu().numpy()
+    del master_full
+    for k in range(w.n_micro):
+        W.make_micro_grads(w, 1, k, seed=0, device=dev, out=st.grads[k])
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: L={L} chunks={st.plan.info.n_chunks} setup {time.time() - t0:.1f}s")
+
+    hp = w.hp()
+    stream = torch.cuda.current_stream()
+
+    def one_step(t, ev=None):
+        for k in range(w.n_micro):
+            if ev is not None:
+                ev[k].record(stream)
+            st.accumulate(k)
+        if ev is not None:
+            ev[w.n_micro].record(stream)
+        st.norm()
+        if ev is not None:
+            ev[w.n_micro + 1].record(stream)
+        st.adamw(hp, step=t)
+        if ev is not None:
+            ev[w.n_micro + 2].record(stream)
+
+    for t in range(1, args.warmup + 1):
+        one_step(t)
+    torch.cuda.synchronize()
+
+    n_ev = w.n_micro + 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        one_step(args.warmup + 1 + s, evs[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+
+    acc_ms = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(w.n_micro)]
+                       for s in range(args.steps)])
+    norm_ms = np.array([evs[s][w.n_micro].elapsed_time(evs[s][w.n_micro + 1])
+                        for s in range(args.steps)])
+    adam_ms = np.array([evs[s][w.n_micro + 1].elapsed_time(evs[s][w.n_micro + 2])
+                        for s in range(args.steps)])
+    adam_avg = float(adam_ms.mean())
+    acc_first = float(acc_ms[:, 0].mean())
+    acc_next = float(acc_ms[:, 1:].mean()) if w.n_micro > 1 else None
+
+    value = L / (ms_step / 1e3)
+    adam_bytes = BYTES_ADAMW * L
+    achieved = adam_bytes / (adam_avg / 1e3) / 1e9
+    traffic = traffic_from_profiles(w.name, "adamw")
+    h3_bytes = (BYTES_ACC_FIRST + BYTES_ACC_NEXT * (w.n_micro - 1) + BYTES_ADAMW) * L
+
+    # probe copy: the achievable streaming ceiling on this machine
+    copy_gbps = None
+    if args.copy_gb > 0:
+        nbytes = int(args.copy_gb * 1e9) // 16 * 16
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            B.z1_probe_copy(src, dst, nbytes)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 10
+        for _ in range(reps):
+            B.z1_probe_copy(src, dst, nbytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        del src, dst
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        o = oracle.get()
+        g_sample = np.stack([torch.cat([st.grads[k][i].reshape(-1)[s:s + n]
+                                        for i, s, n in sample_idx]).view(torch.int16).cpu().numpy()
+                             for k in range(w.n_micro)]).view(np.uint16)
+        p = p_sample.astype(np.float32).copy()
+        m = np.zeros_like(p)
+        v = np.zeros_like(p)
+        acc = np.empty_like(p)
+        wb = np.empty(p.size, np.uint16)
+        c0 = time.perf_counter()
+        steps = 0
+        while True:
+            steps += 1
+            o.step(g_sample, p, m, v, step=steps, acc=acc, w=wb, **hp)
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cpu_s = (time.perf_counter() - c0) / steps
+        cpu = {"value": p.size / cpu_s, "unit": "params/s", "cores": o.num_threads(),
+               "kind": "oracle",
+               "sample": f"{p.size} shard elements (first slices of the {w.name} shard, "
+                         f"packed), K={w.n_micro}, {steps} full steps: accumulate, norm, "
+                         f"clip, AdamW, bf16; binary64 C oracle, not a tuned CPU optimizer",
+               "cpu_model": _cpu_model()}
+
+    out = {
+        "metric": "optimizer-step params/s (7B shard, full step: K accumulations + norm + "
+                  "clipped AdamW + bf16 cast)",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state, f64 update math, bf16 weights/grads",
+        "data": "synthetic",
+        "config": {"workload": w.name, "params": w.total_params, "shard_elems": L,
+                   "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
+                   "chunk_elems": int(st.plan.info.chunk_elems),
+                   "n_chunks": int(st.plan.info.n_chunks)},
+        "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
+                     "launch_ms": adam_avg},
+        "kernels_ms": {"accum_first": acc_first, "accum_next": acc_next,
+                       "norm_fin": float(norm_ms.mean()), "adamw": adam_avg},
+        "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
+        "step_bytes_per_param": h3_bytes // L if L else None,
+        "optimizer_step_params_per_s": L / ((adam_avg + float(norm_ms.mean())) / 1e3),
+        "adamw_34B_equivalent_GBps": 34 * L / (adam_avg / 1e3) / 1e9,
+        "copy_probe_GBps": copy_gbps,
+        "wall_s": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    st.close()
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,262 @@
+/*
+ * z1.h -- C ABI of the ZeRO-1 shard optimizer step for one data-parallel
+ * rank on one AMD Instinct MI355X (gfx950).
+ *
+ * The step (per optimizer step t, on this rank's shard of every parameter):
+ *   1. shard plan      each tensor's numel split evenly over dp_size ranks,
+ *                      rank r owning one contiguous slice
+ *                      ("ZeRO-1 风格的 Distributed Optimizer", §6.3 shard
+ *                      划分策略; §6.2: optimizer state only for the local
+ *                      slice)
+ *   2. accumulation    fp32 sum of K bf16 micro-batch gradients
+ *                      ("Distributed Training", How it works, §2 Gradient
+ *                      accumulation; tutorial §6.7; Nanotron Guide config
+ *                      accumulate_grad_in_fp32)
+ *   3. grad norm       S = sum of acc^2 over the shard, clip coefficient
+ *                      c = min(1, clip / (sqrt(S) + 1e-6)) (tutorial §6.6
+ *                      clip_grad: 1.0; the formula is torch's
+ *                      clip_grad_norm_, the pages give only the key)
+ *   4. AdamW           decoupled weight decay and bias-corrected moments on
+ *                      the fp32 master / m / v shard (tutorial §6.6
+ *                      adam_beta1 0.9, adam_beta2 0.95, adam_eps 1e-8,
+ *                      weight_decay 0.1; Nanotron Guide, ZeRO-1 Optimizer
+ *                      State Partitioning: fp32 master, m and v per parameter)
+ *   5. bf16 weights    round-to-nearest-even of the new master into this
+ *                      rank's slice of the full bf16 weight, which the
+ *                      all-gather would then distribute (tutorial §6.2 step
+ *                      4 and §6.3)
+ *
+ * Conventions
+ *   - "device pointer" means memory on the GPU that is current when the plan
+ *     is created (hipMalloc / PyTorch).  "host pointer" means ordinary CPU
+ *     memory.  The caller owns every buffer it passes; the library never
+ *     frees or reallocates caller memory.
+ *   - The library owns only what z1_plan_create allocates (the chunk table,
+ *     pointer tables and norm partials) and frees it in z1_plan_destroy.
+ *     z1_accum_grads, z1_grad_norm_sq and z1_adamw_step allocate nothing.
+ *   - Work is enqueued on the given stream and the calls return without
+ *     waiting for it; none of the step calls synchronises with the host.
+ *     A kernel fault surfaces at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued: a
+ *     call that returns an error has enqueued no work.
+ *   - A plan is used from one host thread and one stream at a time.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef Z1_H
+#define Z1_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Z1_ABI_VERSION 1
+
+typedef enum z1_status {
+    Z1_OK = 0,
+    Z1_EINVAL = 1, /* bad size, rank, micro-batch index, hyperparameter or null pointer */
+    Z1_EALIGN = 2, /* a device base pointer is not 16-byte aligned (8 for d_S) */
+    Z1_ENOMEM = 3, /* a library-owned allocation failed */
+    Z1_EHIP = 4,   /* the HIP runtime reported an error (launch or copy) */
+    Z1_ESTATE = 5  /* calls made out of order (see z1_accum_grads) */
+} z1_status;
+
+/* A hipStream_t (struct ihipStream_t*); NULL is the null stream. */
+typedef struct ihipStream_t *z1_stream;
+
+/* Opaque plan: the shard geometry of one parameter list on one rank, bound
+ * to the caller's device buffers. */
+typedef struct z1_plan z1_plan;
+
+/* Version of this interface (Z1_ABI_VERSION of the built library). */
+int32_t z1_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *z1_strerror(z1_status status);
+
+/* ------------------------------------------------------------------------
+ * z1_shard_plan -- host-only shard plan (no device work).
+ *
+ * For each tensor i with numel[i] = q*dp_size + rho (0 <= rho < dp_size):
+ *   len[i]   = q + (rank < rho ? 1 : 0)
+ *   start[i] = rank*q + min(rank, rho)
+ * so the dp_size slices of a tensor are contiguous, in rank order, cover it
+ * exactly and differ in size by at most one element, the first rho ranks
+ * holding the extra element ("ZeRO-1 风格的 Distributed Optimizer", §6.3:
+ * every parameter is split on its own, its numel divided evenly over the
+ * ranks; which ranks take the remainder is not on the page).
+ *
+ * arena_off[i] is where slice i lives in the fp32 arenas (master, m, v,
+ * acc): offsets increase with i, slices do not overlap, and
+ * arena_off[i] == start[i] (mod 8), so that element e of a slice sits at
+ * the same position within a 16-byte word in a bf16 tensor and within a
+ * 32-byte word in an fp32 arena.  *arena_elems is the arena length in
+ * elements (the shard size plus at most 7 padding elements per tensor).
+ *
+ *   n_tensors   >= 0 (0 gives *arena_elems = 0)
+ *   numel       host [n_tensors], each >= 0
+ *   dp_size     >= 1;  rank in [0, dp_size)
+ *   start, len, arena_off   host [n_tensors], written by the call
+ *   arena_elems host, written by the call
+ * Errors: Z1_EINVAL for a negative count or numel, a bad dp_size or rank,
+ * or a null pointer (numel/start/len/arena_off may be NULL only when
+ * n_tensors == 0).  Deterministic: same inputs, same outputs.
+ * ------------------------------------------------------------------------ */
+z1_status z1_shard_plan(int32_t n_tensors, const int64_t *numel, int32_t dp_size,
+                        int32_t rank, int64_t *start, int64_t *len, int64_t *arena_off,
+                        int64_t *arena_elems);
+
+/* Buffers and geometry bound to a plan.  All device buffers are caller-owned
+ * and must stay allocated until z1_plan_destroy. */
+typedef struct z1_bind {
+    int32_t n_tensors;      /* number of parameter tensors, >= 0            */
+    int32_t dp_size;        /* >= 1                                         */
+    int32_t rank;           /* in [0, dp_size)                              */
+    int32_t n_micro;        /* K, bf16 micro-batch gradients per step, >= 1 */
+    const int64_t *numel;   /* host [n_tensors]                             */
+    /* bf16 working weights: host array [n_tensors] of device pointers, each
+     * to element 0 of the FULL tensor (numel[i] bf16 values).  The step
+     * writes only elements [start[i], start[i]+len[i]).                  */
+    void *const *weights;
+    /* bf16 micro-batch gradients: host array [n_micro * n_tensors] of
+     * device pointers; grads[k*n_tensors + i] points to element 0 of the
+     * FULL gradient of tensor i for micro-batch k.  Only this rank's slice
+     * is read.                                                             */
+    const void *const *grads;
+    /* fp32 arenas, device, arena_elems floats each (see z1_shard_plan).
+     * master holds the fp32 master weights, exp_avg / exp_avg_sq the Adam
+     * moments (zero before the first step), acc receives the accumulated
+     * gradient.  Padding elements are never read or written.             */
+    float *master;
+    float *exp_avg;
+    float *exp_avg_sq;
+    float *acc;
+    int64_t arena_elems;    /* length the caller allocated; must be >= the
+                               value z1_shard_plan returns                  */
+    int64_t chunk_elems;    /* work unit in elements; 0 = library default
+                               (8192); otherwise a multiple of 1024 in
+                               [1024, 1048576]                              */
+    int32_t max_blocks;     /* 0 = one workgroup per chunk; otherwise the
+                               grid size of the accumulation and AdamW
+                               kernels (each workgroup loops over chunks)  */
+    int32_t reserved;       /* must be 0                                    */
+} z1_bind;
+
+/* Geometry of a created plan. */
+typedef struct z1_plan_info {
+    int32_t n_tensors;
+    int32_t n_micro;
+    int64_t shard_elems;  /* L = sum of len[i]                    */
+    int64_t arena_elems;  /* arena length required                */
+    int64_t chunk_elems;  /* work unit in elements                */
+    int64_t n_chunks;     /* entries of the device chunk table    */
+} z1_plan_info;
+
+/* ------------------------------------------------------------------------
+ * z1_plan_create -- validate the binding, compute the shard plan, build the
+ * chunk table (one entry per piece of a slice of at most chunk_elems
+ * elements, split at multiples of chunk_elems within the tensor; empty
+ * slices produce no entry) and upload it to the device once.
+ *
+ * Copies the pointer arrays; the caller may free bind's host arrays after
+ * the call.  The upload is enqueued on `stream` and the call waits for it
+ * (plan creation is not part of the step), so the plan is ready on return.
+ * Errors: Z1_EINVAL (bad geometry, null pointers, arena too small,
+ * bad chunk_elems, reserved != 0), Z1_EALIGN (a weight, gradient or arena
+ * pointer not 16-byte aligned), Z1_ENOMEM, Z1_EHIP.  *out is NULL on error.
+ * ------------------------------------------------------------------------ */
+z1_status z1_plan_create(z1_plan **out, const z1_bind *bind, z1_stream stream);
+
+/* Frees the plan's device and host memory (waits for the device to finish
+ * using it).  NULL is accepted and ignored. */
+z1_status z1_plan_destroy(z1_plan *plan);
+
+/* Fills *info.  Z1_EINVAL on NULL. */
+z1_status z1_plan_query(const z1_plan *plan, z1_plan_info *info);
+
+/* Copies the plan's start / len / arena_off arrays (host [n_tensors] each,
+ * any may be NULL).  Z1_EINVAL on a NULL plan. */
+z1_status z1_plan_layout(const z1_plan *plan, int64_t *start, int64_t *len,
+                         int64_t *arena_off);
+
+/* ------------------------------------------------------------------------
+ * z1_accum_grads -- fp32 accumulation of micro-batch k into the acc arena.
+ *
+ * k == 0:     acc[e] = (float)g_0[e]          (overwrites; may be called at
+ *                                              any time and restarts a step)
+ * 0 < k < K:  acc[e] = acc[e] + (float)g_k[e] (binary32 add, in order)
+ * where g_k[e] is element start[i]+e of gradient (k, i).  The sum is a sum,
+ * not a mean ("Distributed Training", §2: grad += backward(...) for each of
+ * the K micro-batches, one optimizer step after them).  When k == K-1 the
+ * same pass also writes, per chunk, the binary64 sum of acc^2 (a
+ * double-double pair), which z1_grad_norm_sq reduces.
+ *
+ * Order: k must be 0 or one more than the previous accumulation call of this
+ * step, else Z1_ESTATE.  Z1_EINVAL for k outside [0, K) or a NULL plan.
+ * ------------------------------------------------------------------------ */
+z1_status z1_accum_grads(z1_plan *plan, int32_t k, z1_stream stream);
+
+/* ------------------------------------------------------------------------
+ * z1_grad_norm_sq -- S = sum over the shard of acc^2.
+ *
+ * Writes S, the exact sum rounded to binary64 (double-double partials per
+ * chunk, reduced in a fixed order, so the value does not depend on the grid
+ * size or on timing), to the DEVICE double *d_S.  On more than one rank the
+ * caller would all-reduce S before z1_adamw_step; on one rank S is the
+ * global squared norm.
+ * Errors: Z1_ESTATE unless all K accumulation passes of this step have been
+ * enqueued; Z1_EINVAL for NULL; Z1_EALIGN if d_S is not 8-byte aligned.
+ * ------------------------------------------------------------------------ */
+z1_status z1_grad_norm_sq(z1_plan *plan, double *d_S, z1_stream stream);
+
+/* AdamW hyperparameters of one step (binary64, passed by value to the
+ * kernel; the library derives 1 - lr*wd, 1 - beta1, 1 - beta2 and the bias
+ * corrections 1 - beta^t on the host in binary64). */
+typedef struct z1_adamw_hp {
+    double lr;            /* > 0 is not required; finite                      */
+    double beta1;         /* in [0, 1)                                         */
+    double beta2;         /* in [0, 1)                                         */
+    double eps;           /* > 0                                               */
+    double weight_decay;  /* >= 0                                              */
+    double clip;          /* max global norm; <= 0 disables clipping (c = 1)   */
+    int64_t step;         /* t >= 1: this is the t-th optimizer step           */
+} z1_adamw_hp;
+
+/* ------------------------------------------------------------------------
+ * z1_adamw_step -- clip coefficient, AdamW and the bf16 cast, in one pass.
+ *
+ * Reads S from the DEVICE pointer d_S_global (no host round trip), forms
+ * c = min(1, clip / (sqrt(S) + 1e-6)) (c = 1 when clip <= 0), then for every
+ * shard element, in binary64 from the stored fp32 values:
+ *   g = c*acc;  p = p*(1 - lr*wd);  m = beta1*m + (1-beta1)*g;
+ *   v = beta2*v + (1-beta2)*g*g;  mhat = m/(1-beta1^t);  vhat = v/(1-beta2^t);
+ *   p = p - lr*mhat/(sqrt(vhat) + eps)
+ * stores p, m, v rounded to fp32 (nearest-even) and writes the bf16
+ * round-to-nearest-even of the new fp32 master into the weight slice.
+ * Decoupled decay, eps outside the square root and t starting at 1 follow
+ * torch.optim.AdamW; the pages give only the hyperparameter values.
+ *
+ * d_S_global may be NULL only when hp->clip <= 0.
+ * Errors: Z1_ESTATE unless all K accumulation passes have been enqueued
+ * since the last step and, when clipping is on, z1_grad_norm_sq as well;
+ * Z1_EINVAL for bad hyperparameters or NULL; Z1_EALIGN for a misaligned
+ * d_S_global.  After a successful call the plan expects k == 0 next.
+ * ------------------------------------------------------------------------ */
+z1_status z1_adamw_step(z1_plan *plan, const z1_adamw_hp *hp, const double *d_S_global,
+                        z1_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the step): a streaming copy of n_bytes
+ * (a multiple of 16, both pointers 16-byte aligned, non-overlapping) from
+ * device src to device dst with 16-byte loads and stores, used to measure
+ * the achievable HBM bandwidth and to calibrate byte counters.
+ * Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
+ * ------------------------------------------------------------------------ */
+z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Z1_H */

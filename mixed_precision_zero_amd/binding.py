@@ -1,0 +1,230 @@
+"""Thin ctypes binding of libz1 (include/z1.h): argument marshalling only.
+
+Every step of the optimizer runs in the HIP library; this module converts
+torch tensors to device pointers, torch streams to hipStream_t handles and
+status codes to exceptions.  There is no fallback: if the library is not
+built, importing the binding raises.
+
+torch is imported first so that libz1 binds to the HIP runtime torch has
+already loaded (both carry the soname libamdhip64.so.7), which makes torch's
+stream handles and device pointers valid inside the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libz1.so")
+
+Z1_OK, Z1_EINVAL, Z1_EALIGN, Z1_ENOMEM, Z1_EHIP, Z1_ESTATE = range(6)
+_NAMES = {0: "Z1_OK", 1: "Z1_EINVAL", 2: "Z1_EALIGN", 3: "Z1_ENOMEM", 4: "Z1_EHIP",
+          5: "Z1_ESTATE"}
+
+EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_plan_create",
+           "z1_plan_destroy", "z1_plan_query", "z1_plan_layout", "z1_accum_grads",
+           "z1_grad_norm_sq", "z1_adamw_step", "z1_probe_copy")
+
+
+class Z1Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_NAMES.get(status, status)} ({strerror(status)})")
+
+
+class Bind(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("dp_size", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("n_micro", ctypes.c_int32),
+                ("numel", ctypes.POINTER(ctypes.c_int64)),
+                ("weights", ctypes.POINTER(ctypes.c_void_p)),
+                ("grads", ctypes.POINTER(ctypes.c_void_p)),
+                ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("arena_elems", ctypes.c_int64), ("chunk_elems", ctypes.c_int64),
+                ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("n_micro", ctypes.c_int32),
+                ("shard_elems", ctypes.c_int64), ("arena_elems", ctypes.c_int64),
+                ("chunk_elems", ctypes.c_int64), ("n_chunks", ctypes.c_int64)]
+
+
+class AdamWHP(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("clip", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libz1 is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    PI64 = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "z1_abi_version": ([], I32),
+        "z1_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "z1_shard_plan": ([I32, PI64, I32, I32, PI64, PI64, PI64, PI64], ctypes.c_int),
+        "z1_plan_create": ([ctypes.POINTER(P), ctypes.POINTER(Bind), P], ctypes.c_int),
+        "z1_plan_destroy": ([P], ctypes.c_int),
+        "z1_plan_query": ([P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
+        "z1_plan_layout": ([P, PI64, PI64, PI64], ctypes.c_int),
+        "z1_accum_grads": ([P, I32, P], ctypes.c_int),
+        "z1_grad_norm_sq": ([P, P, P], ctypes.c_int),
+        "z1_adamw_step": ([P, ctypes.POINTER(AdamWHP), P, P], ctypes.c_int),
+        "z1_probe_copy": ([P, P, I64, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.z1_strerror(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != Z1_OK:
+        raise Z1Error(status, call)
+
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _p64(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _stream(stream) -> Optional[int]:
+    """hipStream_t of a torch stream (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _dptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def z1_abi_version() -> int:
+    return int(lib.z1_abi_version())
+
+
+def z1_shard_plan(numel: Sequence[int], dp_size: int, rank: int):
+    """(start, len, arena_off, arena_elems) of this rank's shard plan."""
+    n = _i64(numel)
+    start = np.zeros(n.size, np.int64)
+    ln = np.zeros(n.size, np.int64)
+    off = np.zeros(n.size, np.int64)
+    ae = np.zeros(1, np.int64)
+    _check(lib.z1_shard_plan(n.size, _p64(n), dp_size, rank, _p64(start), _p64(ln), _p64(off),
+                             _p64(ae)), "z1_shard_plan")
+    return start, ln, off, int(ae[0])
+
+
+class Plan:
+    """Owner of a z1_plan handle (destroyed with z1_plan_destroy)."""
+
+    def __init__(self, handle: int, info: PlanInfo, keep):
+        self.handle = handle
+        self.info = info
+        self._keep = keep   # host arrays the bind pointed at, for the plan's life
+
+    def close(self):
+        if self.handle:
+            _check(lib.z1_plan_destroy(self.handle), "z1_plan_destroy")
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Sequence,
+                   grads: Sequence[Sequence], master, exp_avg, exp_avg_sq, acc,
+                   chunk_elems: int = 0, max_blocks: int = 0, stream=None) -> Plan:
+    """Bind device buffers: weights[i] and grads[k][i] are full-size bf16
+    tensors (or raw device addresses), the four arenas fp32 of arena_elems."""
+    n = _i64(numel)
+    K = len(grads)
+    for gk in grads:
+        if len(gk) != n.size:
+            raise ValueError("grads[k] must list one tensor per parameter")
+    if len(weights) != n.size:
+        raise ValueError("weights must list one tensor per parameter")
+    wp = (ctypes.c_void_p * max(n.size, 1))(*[_dptr(w) for w in weights])
+    gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
+    arena = [master, exp_avg, exp_avg_sq, acc]
+    sizes = [a.numel() for a in arena if hasattr(a, "numel")]
+    b = Bind(n_tensors=n.size, dp_size=dp_size, rank=rank, n_micro=K, numel=_p64(n),
+             weights=ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
+             grads=ctypes.cast(gp, ctypes.POINTER(ctypes.c_void_p)),
+             master=_dptr(master), exp_avg=_dptr(exp_avg), exp_avg_sq=_dptr(exp_avg_sq),
+             acc=_dptr(acc), arena_elems=min(sizes) if sizes else 0,
+             chunk_elems=chunk_elems, max_blocks=max_blocks, reserved=0)
+    h = ctypes.c_void_p()
+    _check(lib.z1_plan_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)),
+           "z1_plan_create")
+    info = PlanInfo()
+    _check(lib.z1_plan_query(h, ctypes.byref(info)), "z1_plan_query")
+    return Plan(h.value, info, (n, wp, gp))
+
+
+def z1_plan_layout(plan: Plan):
+    n = plan.info.n_tensors
+    start = np.zeros(n, np.int64)
+    ln = np.zeros(n, np.int64)
+    off = np.zeros(n, np.int64)
+    _check(lib.z1_plan_layout(plan.handle, _p64(start), _p64(ln), _p64(off)), "z1_plan_layout")
+    return start, ln, off
+
+
+def z1_accum_grads(plan: Plan, k: int, stream=None) -> None:
+    _check(lib.z1_accum_grads(plan.handle, k, _stream(stream)), "z1_accum_grads")
+
+
+def z1_grad_norm_sq(plan: Plan, d_S, stream=None) -> None:
+    """Writes S into the device float64 tensor d_S (first element)."""
+    _check(lib.z1_grad_norm_sq(plan.handle, _dptr(d_S), _stream(stream)), "z1_grad_norm_sq")
+
+
+def z1_adamw_step(plan: Plan, *, lr, beta1, beta2, eps, weight_decay, clip, step,
+                  d_S=None, stream=None) -> None:
+    hp = AdamWHP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
+    _check(lib.z1_adamw_step(plan.handle, ctypes.byref(hp), _dptr(d_S), _stream(stream)),
+           "z1_adamw_step")
+
+
+def z1_probe_copy(src, dst, n_bytes: int, stream=None) -> None:
+    _check(lib.z1_probe_copy(_dptr(src), _dptr(dst), int(n_bytes), _stream(stream)),
+           "z1_probe_copy")
+
+
+def hip_runtimes_loaded() -> list:
+    """Paths of every libamdhip64 mapped into this process (should be one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)

@@ -1,0 +1,380 @@
+// z1_api.hip -- host side of the C ABI declared in include/z1.h: argument
+// validation, the shard plan, the chunk table, call-order state and the
+// kernel launches.  Everything device-side is in z1_kernels.hip.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "z1.h"
+#include "z1_internal.h"
+
+using z1::AdamConsts;
+using z1::Chunk;
+using z1::DD;
+
+struct z1_plan {
+    int32_t n = 0, K = 0, dp = 0, rank = 0;
+    int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
+    int grid = 0;
+    std::vector<int64_t> start, len, arena_off;
+    // device memory owned by the plan
+    Chunk *d_chunks = nullptr;
+    const uint16_t **d_grads = nullptr;  // [K][n]
+    uint16_t **d_weights = nullptr;      // [n]
+    DD *d_partials = nullptr;            // [n_chunks]
+    // caller's arenas
+    float *master = nullptr, *exp_avg = nullptr, *exp_avg_sq = nullptr, *acc = nullptr;
+    // call order: next micro-batch index expected; norm enqueued since the last pass
+    int32_t next_k = 0;
+    bool acc_complete = false;
+    bool norm_done = false;
+};
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+void free_plan_memory(z1_plan *p)
+{
+    if (p->d_chunks)
+        (void)hipFree(p->d_chunks);
+    if (p->d_grads)
+        (void)hipFree(p->d_grads);
+    if (p->d_weights)
+        (void)hipFree(p->d_weights);
+    if (p->d_partials)
+        (void)hipFree(p->d_partials);
+    p->d_chunks = nullptr;
+    p->d_grads = nullptr;
+    p->d_weights = nullptr;
+    p->d_partials = nullptr;
+}
+
+template <typename T>
+z1_status device_alloc(T **out, size_t count)
+{
+    *out = nullptr;
+    if (count == 0)
+        count = 1;  // keep a valid pointer for empty tables
+    void *p = nullptr;
+    if (hipMalloc(&p, count * sizeof(T)) != hipSuccess) {
+        (void)hipGetLastError();
+        return Z1_ENOMEM;
+    }
+    *out = static_cast<T *>(p);
+    return Z1_OK;
+}
+
+z1::LaunchGeom geom(const z1_plan *p) { return z1::LaunchGeom{p->d_chunks, p->n_chunks, p->grid}; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t z1_abi_version(void) { return Z1_ABI_VERSION; }
+
+const char *z1_strerror(z1_status s)
+{
+    switch (s) {
+    case Z1_OK: return "success";
+    case Z1_EINVAL: return "invalid argument";
+    case Z1_EALIGN: return "device pointer not aligned";
+    case Z1_ENOMEM: return "out of memory";
+    case Z1_EHIP: return "HIP runtime error";
+    case Z1_ESTATE: return "call out of order";
+    }
+    return "unknown status";
+}
+
+z1_status z1_shard_plan(int32_t n_tensors, const int64_t *numel, int32_t dp_size, int32_t rank,
+                        int64_t *start, int64_t *len, int64_t *arena_off, int64_t *arena_elems)
+{
+    if (n_tensors < 0 || dp_size < 1 || rank < 0 || rank >= dp_size || !arena_elems)
+        return Z1_EINVAL;
+    if (n_tensors > 0 && (!numel || !start || !len || !arena_off))
+        return Z1_EINVAL;
+    for (int32_t i = 0; i < n_tensors; ++i)
+        if (numel[i] < 0)
+            return Z1_EINVAL;
+    int64_t next = 0;  // first free arena element
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        const int64_t q = numel[i] / dp_size, rho = numel[i] % dp_size;
+        const int64_t extra = rank < rho ? 1 : 0;
+        start[i] = (int64_t)rank * q + (extra ? rank : rho);
+        len[i] = q + extra;
+        // smallest offset >= next with the same residue mod 8 as the slice start
+        const int64_t off = next + (((start[i] - next) % 8) + 8) % 8;
+        arena_off[i] = off;
+        next = off + len[i];
+    }
+    *arena_elems = next;
+    return Z1_OK;
+}
+
+z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
+{
+    if (!out)
+        return Z1_EINVAL;
+    *out = nullptr;
+    if (!b || b->n_tensors < 0 || b->n_micro < 1 || b->dp_size < 1 || b->rank < 0 ||
+        b->rank >= b->dp_size || b->reserved != 0 || b->max_blocks < 0)
+        return Z1_EINVAL;
+    const int32_t n = b->n_tensors, K = b->n_micro;
+    if (n > 0 && (!b->numel || !b->weights || !b->grads))
+        return Z1_EINVAL;
+    if (!b->master || !b->exp_avg || !b->exp_avg_sq || !b->acc)
+        return Z1_EINVAL;
+    int64_t chunk = b->chunk_elems ? b->chunk_elems : z1::kDefaultChunk;
+    if (chunk < 1024 || chunk > z1::kMaxChunk || chunk % 1024 != 0)
+        return Z1_EINVAL;
+
+    z1_plan *p = new (std::nothrow) z1_plan();
+    if (!p)
+        return Z1_ENOMEM;
+    p->n = n;
+    p->K = K;
+    p->dp = b->dp_size;
+    p->rank = b->rank;
+    p->chunk_elems = chunk;
+    p->start.resize(n);
+    p->len.resize(n);
+    p->arena_off.resize(n);
+    z1_status st = z1_shard_plan(n, b->numel, b->dp_size, b->rank, p->start.data(),
+                                 p->len.data(), p->arena_off.data(), &p->arena_elems);
+    if (st != Z1_OK) {
+        delete p;
+        return st;
+    }
+    if (b->arena_elems < p->arena_elems) {
+        delete p;
+        return Z1_EINVAL;
+    }
+
+    // pointers: non-null for tensors this rank touches, 16-byte aligned
+    std::vector<uint16_t *> wptr(n);
+    std::vector<const uint16_t *> gptr((size_t)K * n);
+    for (int32_t i = 0; i < n; ++i) {
+        wptr[i] = static_cast<uint16_t *>(b->weights[i]);
+        for (int32_t k = 0; k < K; ++k)
+            gptr[(size_t)k * n + i] = static_cast<const uint16_t *>(b->grads[(size_t)k * n + i]);
+        if (p->len[i] == 0)
+            continue;
+        if (!wptr[i]) {
+            delete p;
+            return Z1_EINVAL;
+        }
+        if (!aligned(wptr[i], 16)) {
+            delete p;
+            return Z1_EALIGN;
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            const void *g = gptr[(size_t)k * n + i];
+            if (!g) {
+                delete p;
+                return Z1_EINVAL;
+            }
+            if (!aligned(g, 16)) {
+                delete p;
+                return Z1_EALIGN;
+            }
+        }
+    }
+    if (!aligned(b->master, 16) || !aligned(b->exp_avg, 16) || !aligned(b->exp_avg_sq, 16) ||
+        !aligned(b->acc, 16)) {
+        delete p;
+        return Z1_EALIGN;
+    }
+    p->master = b->master;
+    p->exp_avg = b->exp_avg;
+    p->exp_avg_sq = b->exp_avg_sq;
+    p->acc = b->acc;
+
+    // chunk table: pieces cut at multiples of `chunk` inside each tensor
+    std::vector<Chunk> chunks;
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t s0 = p->start[i], s1 = p->start[i] + p->len[i];
+        p->L += p->len[i];
+        int64_t s = s0;
+        while (s < s1) {
+            const int64_t cut = (s / chunk + 1) * chunk;
+            const int64_t e = cut < s1 ? cut : s1;
+            Chunk c;
+            c.src = s;
+            c.dst = p->arena_off[i] + (s - s0);
+            c.tensor = i;
+            c.count = (int32_t)(e - s);
+            c.pad = 0;
+            chunks.push_back(c);
+            s = e;
+        }
+    }
+    p->n_chunks = (int64_t)chunks.size();
+    if (p->n_chunks > INT32_MAX) {
+        delete p;
+        return Z1_EINVAL;
+    }
+    int64_t grid = p->n_chunks;
+    if (b->max_blocks > 0 && grid > b->max_blocks)
+        grid = b->max_blocks;
+    p->grid = (int)(grid > 0 ? grid : 1);
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
+        (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||
+        (st = device_alloc(&p->d_weights, wptr.size())) != Z1_OK ||
+        (st = device_alloc(&p->d_partials, (size_t)p->n_chunks)) != Z1_OK) {
+        free_plan_memory(p);
+        delete p;
+        return st;
+    }
+    hipError_t e = hipSuccess;
+    if (!chunks.empty())
+        e = hipMemcpyAsync(p->d_chunks, chunks.data(), chunks.size() * sizeof(Chunk),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !gptr.empty())
+        e = hipMemcpyAsync(p->d_grads, gptr.data(), gptr.size() * sizeof(void *),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !wptr.empty())
+        e = hipMemcpyAsync(p->d_weights, wptr.data(), wptr.size() * sizeof(void *),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);  // host staging vectors die with this call
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        free_plan_memory(p);
+        delete p;
+        return Z1_EHIP;
+    }
+    *out = p;
+    return Z1_OK;
+}
+
+z1_status z1_plan_destroy(z1_plan *p)
+{
+    if (!p)
+        return Z1_OK;
+    (void)hipDeviceSynchronize();
+    free_plan_memory(p);
+    delete p;
+    return Z1_OK;
+}
+
+z1_status z1_plan_query(const z1_plan *p, z1_plan_info *info)
+{
+    if (!p || !info)
+        return Z1_EINVAL;
+    info->n_tensors = p->n;
+    info->n_micro = p->K;
+    info->shard_elems = p->L;
+    info->arena_elems = p->arena_elems;
+    info->chunk_elems = p->chunk_elems;
+    info->n_chunks = p->n_chunks;
+    return Z1_OK;
+}
+
+z1_status z1_plan_layout(const z1_plan *p, int64_t *start, int64_t *len, int64_t *arena_off)
+{
+    if (!p)
+        return Z1_EINVAL;
+    const size_t bytes = (size_t)p->n * sizeof(int64_t);
+    if (start && bytes)
+        memcpy(start, p->start.data(), bytes);
+    if (len && bytes)
+        memcpy(len, p->len.data(), bytes);
+    if (arena_off && bytes)
+        memcpy(arena_off, p->arena_off.data(), bytes);
+    return Z1_OK;
+}
+
+z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
+{
+    if (!p || k < 0 || k >= p->K)
+        return Z1_EINVAL;
+    if (k != 0 && k != p->next_k)
+        return Z1_ESTATE;
+    const bool first = k == 0, last = k == p->K - 1;
+    hipError_t e = z1::launch_accum(geom(p), p->d_grads + (size_t)k * p->n, p->acc,
+                                    p->d_partials, first, last,
+                                    reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        p->next_k = 0;
+        p->acc_complete = false;
+        p->norm_done = false;
+        return Z1_EHIP;
+    }
+    p->next_k = k + 1;
+    p->acc_complete = last;
+    p->norm_done = false;
+    return Z1_OK;
+}
+
+z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
+{
+    if (!p || !d_S)
+        return Z1_EINVAL;
+    if (!aligned(d_S, 8))
+        return Z1_EALIGN;
+    if (!p->acc_complete)
+        return Z1_ESTATE;
+    if (z1::launch_norm_fin(p->d_partials, p->n_chunks, d_S,
+                            reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return Z1_EHIP;
+    p->norm_done = true;
+    return Z1_OK;
+}
+
+z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_global,
+                        z1_stream stream)
+{
+    if (!p || !hp)
+        return Z1_EINVAL;
+    if (!isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !isfinite(hp->eps) ||
+        !(hp->weight_decay >= 0.0) || !isfinite(hp->weight_decay) || isnan(hp->clip) ||
+        hp->step < 1)
+        return Z1_EINVAL;
+    const bool clipping = hp->clip > 0.0;
+    if (clipping && !d_S_global)
+        return Z1_EINVAL;
+    if (d_S_global && !aligned(d_S_global, 8))
+        return Z1_EALIGN;
+    if (!p->acc_complete || (clipping && !p->norm_done))
+        return Z1_ESTATE;
+
+    AdamConsts k;
+    const double t = (double)hp->step;
+    k.lr = hp->lr;
+    k.beta1 = hp->beta1;
+    k.beta2 = hp->beta2;
+    k.omb1 = 1.0 - hp->beta1;
+    k.omb2 = 1.0 - hp->beta2;
+    k.eps = hp->eps;
+    k.decay = 1.0 - hp->lr * hp->weight_decay;
+    k.bc1 = 1.0 - pow(hp->beta1, t);
+    k.bc2 = 1.0 - pow(hp->beta2, t);
+    k.clip = clipping ? hp->clip : 0.0;
+    hipError_t e = z1::launch_adamw(geom(p), p->d_weights, p->acc, p->master, p->exp_avg,
+                                    p->exp_avg_sq, k, d_S_global,
+                                    reinterpret_cast<hipStream_t>(stream));
+    p->next_k = 0;
+    p->acc_complete = false;
+    p->norm_done = false;
+    return e == hipSuccess ? Z1_OK : Z1_EHIP;
+}
+
+z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream)
+{
+    if (!src || !dst || n_bytes < 0 || n_bytes % 16 != 0)
+        return Z1_EINVAL;
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return Z1_EALIGN;
+    return z1::launch_copy(src, dst, n_bytes, reinterpret_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? Z1_OK
+               : Z1_EHIP;
+}
+
+}  // extern "C"

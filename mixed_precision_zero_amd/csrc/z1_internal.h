@@ -1,0 +1,61 @@
+// z1_internal.h -- types shared by the host API (z1_api.hip) and the kernels
+// (z1_kernels.hip) of the ZeRO-1 shard optimizer step.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace z1 {
+
+// Workgroup of four wave64s; every lane moves 4 elements per vector
+// (16-byte fp32 accesses, 8-byte bf16 accesses), so one workgroup touches
+// 1024 consecutive elements per vector step.
+constexpr int kBlock = 256;
+constexpr int kVec = 4;
+constexpr int64_t kDefaultChunk = 8192;
+constexpr int64_t kMaxChunk = 1 << 20;
+constexpr int kFinBlock = 1024;
+
+// One unit of work: a piece of one tensor's slice of at most chunk_elems
+// elements.  Pieces are cut at multiples of chunk_elems inside the tensor,
+// so every piece except a slice's first one starts 8-aligned.
+struct alignas(32) Chunk {
+    int64_t src;     // first element of the piece inside the full tensor
+    int64_t dst;     // same element's index inside the fp32 arenas
+    int32_t tensor;  // parameter index (selects the bf16 pointers)
+    int32_t count;   // elements in the piece, 1..chunk_elems
+    int64_t pad;
+};
+static_assert(sizeof(Chunk) == 32, "chunk descriptor is 32 bytes");
+
+// Unevaluated sum hi + lo with |lo| <= ulp(hi)/2 (a double-double).
+struct alignas(16) DD {
+    double hi, lo;
+};
+
+// Per-step AdamW constants, all binary64, derived on the host.
+struct AdamConsts {
+    double lr;
+    double beta1, beta2;
+    double omb1, omb2;  // 1 - beta1, 1 - beta2
+    double eps;
+    double decay;       // 1 - lr * weight_decay
+    double bc1, bc2;    // 1 - beta1^t, 1 - beta2^t
+    double clip;        // <= 0: no clipping
+};
+
+struct LaunchGeom {
+    const Chunk *chunks;  // device
+    int64_t n_chunks;
+    int grid;             // workgroups for the chunk kernels
+};
+
+hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,
+                        DD *partials, bool first, bool last, hipStream_t s);
+hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, double *S, hipStream_t s);
+hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const float *acc,
+                        float *master, float *m, float *v, const AdamConsts &k,
+                        const double *S, hipStream_t s);
+hipError_t launch_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
+
+}  // namespace z1

@@ -1,0 +1,88 @@
+"""One rank's device buffers for the ZeRO-1 shard step, wired to a libz1 plan.
+
+This is memory plumbing: it allocates the fp32 arenas (master, m, v, acc),
+the full-size bf16 weights and micro-gradient slots and the device norm
+scalar with torch, creates the plan, and calls the four library entry points
+in step order.  No arithmetic of the step happens here.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+class ShardStep:
+    def __init__(self, shapes: Sequence[Sequence[int]], dp_size: int, rank: int, n_micro: int,
+                 device="cuda", chunk_elems: int = 0, max_blocks: int = 0,
+                 weights: Optional[List[torch.Tensor]] = None,
+                 grads: Optional[List[List[torch.Tensor]]] = None,
+                 arena_pad: int = 0):
+        self.shapes = [tuple(s) for s in shapes]
+        self.numel = [int(torch.Size(s).numel()) for s in self.shapes]
+        self.dp_size, self.rank, self.n_micro = dp_size, rank, n_micro
+        self.device = torch.device(device)
+        self.start, self.len, self.arena_off, self.arena_elems = B.z1_shard_plan(
+            self.numel, dp_size, rank)
+        n = self.arena_elems + arena_pad
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.master = torch.zeros(n, **f32)
+        self.exp_avg = torch.zeros(n, **f32)
+        self.exp_avg_sq = torch.zeros(n, **f32)
+        self.acc = torch.zeros(n, **f32)
+        bf = dict(dtype=torch.bfloat16, device=self.device)
+        self.weights = weights if weights is not None else [torch.zeros(s, **bf) for s in self.shapes]
+        self.grads = grads if grads is not None else [
+            [torch.zeros(s, **bf) for s in self.shapes] for _ in range(n_micro)]
+        self.d_S = torch.zeros(1, dtype=torch.float64, device=self.device)
+        self.plan = B.z1_plan_create(self.numel, dp_size, rank, self.weights, self.grads,
+                                     self.master, self.exp_avg, self.exp_avg_sq, self.acc,
+                                     chunk_elems=chunk_elems, max_blocks=max_blocks)
+        self.t = 0
+
+    # -- layout helpers (torch copies; initialisation and inspection only) --
+    def slices(self):
+        for i in range(len(self.numel)):
+            yield i, int(self.start[i]), int(self.len[i]), int(self.arena_off[i])
+
+    def scatter_to_arena(self, arena: torch.Tensor, full: Sequence[torch.Tensor]) -> None:
+        """arena[off_i : off_i+len_i] = full_i.flatten()[start_i : start_i+len_i]"""
+        for i, s, ln, off in self.slices():
+            if ln:
+                arena[off:off + ln].copy_(full[i].reshape(-1)[s:s + ln])
+
+    def packed(self, arena: torch.Tensor) -> torch.Tensor:
+        """The shard in packed order: the slices of every tensor concatenated."""
+        parts = [arena[off:off + ln] for _, _, ln, off in self.slices() if ln]
+        if not parts:
+            return arena[:0].clone()
+        return torch.cat(parts)
+
+    def packed_weights(self) -> torch.Tensor:
+        parts = [self.weights[i].reshape(-1)[s:s + ln] for i, s, ln, _ in self.slices() if ln]
+        if not parts:
+            return torch.zeros(0, dtype=torch.bfloat16, device=self.device)
+        return torch.cat(parts)
+
+    # -- the step ------------------------------------------------------------
+    def accumulate(self, k: int, stream=None) -> None:
+        B.z1_accum_grads(self.plan, k, stream)
+
+    def norm(self, stream=None) -> None:
+        B.z1_grad_norm_sq(self.plan, self.d_S, stream)
+
+    def adamw(self, hp: dict, step: Optional[int] = None, stream=None) -> None:
+        t = self.t + 1 if step is None else step
+        B.z1_adamw_step(self.plan, d_S=self.d_S, step=t, stream=stream, **hp)
+        self.t = t
+
+    def step(self, hp: dict, stream=None) -> None:
+        for k in range(self.n_micro):
+            self.accumulate(k, stream)
+        self.norm(stream)
+        self.adamw(hp, stream=stream)
+
+    def close(self) -> None:
+        self.plan.close()

@@ -1,0 +1,197 @@
+"""GPU-vs-oracle parity driver shared by the GPU tests.
+
+Inputs come from ``mixed_precision_zero_amd.workloads`` (seeded, full-size,
+generated on the device by torch); the HIP library reads the bound device
+tensors, the oracle reads the same bytes copied to the host and cut with the
+oracle's own shard plan.  Nothing the HIP path computes is ever fed to the
+oracle.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+from mixed_precision_zero_amd import workloads as W
+from mixed_precision_zero_amd.shard import ShardStep
+
+CANARY = float.fromhex("0x1.5a5a5ap+77")   # a value no step can produce by chance
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def rel_rms_err(x: np.ndarray, y: np.ndarray) -> float:
+    """max_e |x_e - y_e| / max(|y_e|, rms(y)): the fp32-state parity metric."""
+    if y.size == 0:
+        return 0.0
+    x = x.astype(np.float64)
+    y = y.astype(np.float64)
+    rms = math.sqrt(float(np.mean(y * y)))
+    den = np.maximum(np.abs(y), rms)
+    den[den == 0] = 1.0
+    return float(np.max(np.abs(x - y) / den))
+
+
+def bf16_ord(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns mapped to integers that are ordered like the values."""
+    h = h.astype(np.int64)
+    return np.where(h & 0x8000, -(h & 0x7FFF), h)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclass
+class StepReport:
+    step: int
+    acc_mismatch: int
+    S_gpu: float
+    S_ref: float
+    S_rel: float
+    rel: dict = field(default_factory=dict)          # buffer -> rel_rms_err
+    not_bitexact: dict = field(default_factory=dict)  # buffer -> count
+    bf16_max_ulp: int = 0
+    bf16_self_mismatch: int = 0
+
+
+class Parity:
+    """Runs a workload on the GPU and the oracle side by side."""
+
+    def __init__(self, w: W.Workload, device="cuda", chunk_elems=0, max_blocks=0,
+                 seed=0, canaries=True):
+        self.w = w
+        self.dev = torch.device(device)
+        self.o = oracle.get()
+        self.seed = seed
+        t0 = time.time()
+        self.st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=self.dev,
+                            chunk_elems=chunk_elems, max_blocks=max_blocks,
+                            arena_pad=64 if canaries else 0)
+        self.o_start, self.o_len = self.o.shard_plan(w.numel, w.dp_size, w.rank)
+        self.L = int(self.o_len.sum())
+        # canaries in every arena element outside a slice (gaps and tail)
+        self.free_mask = None
+        if canaries:
+            used = torch.zeros(self.st.master.numel(), dtype=torch.bool, device=self.dev)
+            for _, _, ln, off in self.st.slices():
+                if ln:
+                    used[off:off + ln] = True
+            self.free_mask = ~used
+            for a in (self.st.master, self.st.exp_avg, self.st.exp_avg_sq, self.st.acc):
+                a[self.free_mask] = CANARY
+        master = W.make_master(w, seed=seed, device=self.dev)
+        self.st.scatter_to_arena(self.st.master, master)
+        for wt, mt in zip(self.st.weights, master):
+            wt.copy_(mt)     # torch's own cast: the weights before any step
+        self.p = self._packed_host_f32(master)
+        del master
+        self.m = np.zeros(self.L, np.float32)
+        self.v = np.zeros(self.L, np.float32)
+        self.wbits = np.zeros(self.L, np.uint16)
+        self.acc = np.zeros(self.L, np.float32)
+        self.w_before = None
+        if w.dp_size > 1:
+            self.w_before = [x.clone() for x in self.st.weights]
+        self.t = 0
+        log(f"[parity] {w.name}: L={self.L} chunks={self.st.plan.info.n_chunks} "
+            f"setup {time.time() - t0:.1f}s")
+
+    def _packed_host_f32(self, full) -> np.ndarray:
+        parts = [full[i].reshape(-1)[s:s + n] for i, (s, n) in
+                 enumerate(zip(self.o_start, self.o_len)) if n]
+        if not parts:
+            return np.zeros(0, np.float32)
+        return torch.cat(parts).cpu().numpy().astype(np.float32)
+
+    def _packed_host_bf16(self, full) -> np.ndarray:
+        parts = [full[i].reshape(-1)[s:s + n] for i, (s, n) in
+                 enumerate(zip(self.o_start, self.o_len)) if n]
+        if not parts:
+            return np.zeros(0, np.uint16)
+        return bf16_bits(torch.cat(parts))
+
+    def plan_matches(self) -> bool:
+        return bool((self.st.start == self.o_start).all() and (self.st.len == self.o_len).all())
+
+    def step(self, check=True) -> Optional[StepReport]:
+        w, st = self.w, self.st
+        self.t += 1
+        t = self.t
+        t0 = time.time()
+        g = np.empty((w.n_micro, self.L), np.uint16)
+        for k in range(w.n_micro):
+            W.make_micro_grads(w, t, k, seed=self.seed, device=self.dev, out=st.grads[k])
+            g[k] = self._packed_host_bf16(st.grads[k])
+        t1 = time.time()
+        st.step(w.hp())
+        torch.cuda.synchronize()
+        t2 = time.time()
+        S, c, _ = self.o.step(g, self.p, self.m, self.v, step=t, acc=self.acc, w=self.wbits,
+                              **w.hp())
+        del g
+        t3 = time.time()
+        log(f"[parity] {w.name} step {t}: inputs {t1 - t0:.1f}s gpu {t2 - t1:.2f}s "
+            f"oracle {t3 - t2:.1f}s (S={S:.6g}, c={c:.4g})")
+        if not check:
+            return None
+        return self.compare(S)
+
+    def compare(self, S_ref: float) -> StepReport:
+        st = self.st
+        acc_g = st.packed(st.acc).cpu().numpy()
+        S_g = float(st.d_S.item())
+        rep = StepReport(step=self.t, acc_mismatch=int((acc_g != self.acc).sum()),
+                         S_gpu=S_g, S_ref=S_ref,
+                         S_rel=abs(S_g - S_ref) / S_ref if S_ref else abs(S_g))
+        for name, gpu, ref in (("master", st.master, self.p), ("exp_avg", st.exp_avg, self.m),
+                               ("exp_avg_sq", st.exp_avg_sq, self.v)):
+            x = st.packed(gpu).cpu().numpy()
+            rep.rel[name] = rel_rms_err(x, ref)
+            rep.not_bitexact[name] = int((x.view(np.uint32) != ref.view(np.uint32)).sum())
+            if name == "master":
+                # the GPU's bf16 must be torch's RNE cast of the GPU's own master
+                own = bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+        wb = bf16_bits(st.packed_weights())
+        rep.bf16_max_ulp = int(np.max(np.abs(bf16_ord(wb) - bf16_ord(self.wbits)))) if wb.size else 0
+        rep.bf16_self_mismatch = int((wb != own).sum()) if wb.size else 0
+        rep.not_bitexact["bf16"] = int((wb != self.wbits).sum())
+        return rep
+
+    def canaries_intact(self) -> bool:
+        if self.free_mask is None:
+            return True
+        ok = True
+        for a in (self.st.master, self.st.exp_avg, self.st.exp_avg_sq, self.st.acc):
+            ok &= bool((a[self.free_mask] == CANARY).all())
+        return ok
+
+    def weights_outside_slices_intact(self) -> bool:
+        if self.w_before is None:
+            return True
+        for i, s, ln, _ in self.st.slices():
+            a = self.st.weights[i].reshape(-1)
+            b = self.w_before[i].reshape(-1)
+            if not (torch.equal(a[:s], b[:s]) and torch.equal(a[s + ln:], b[s + ln:])):
+                return False
+        return True
+
+    def close(self):
+        self.st.close()
+
+
+def assert_report(rep: StepReport, tol_state=1e-6, tol_S=1e-5) -> None:
+    assert rep.acc_mismatch == 0, f"step {rep.step}: {rep.acc_mismatch} acc elements differ"
+    assert rep.S_rel <= tol_S, f"step {rep.step}: S rel err {rep.S_rel:.3g}"
+    for name, e in rep.rel.items():
+        assert e <= tol_state, f"step {rep.step}: {name} rel err {e:.3g} > {tol_state}"
+    assert rep.bf16_max_ulp <= 1, f"step {rep.step}: bf16 off by {rep.bf16_max_ulp} ulp"
+    assert rep.bf16_self_mismatch == 0, f"step {rep.step}: bf16 != RNE(own master)"

@@ -1,0 +1,147 @@
+"""Host-side checks of libz1 (no GPU needed): symbols, shard plan, errors."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from mixed_precision_zero_amd import binding as B
+from mixed_precision_zero_amd import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "z1.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(z1_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "z1_shard_plan" in names and "z1_adamw_step" in names
+    for name in names:
+        assert hasattr(B.lib, name), f"{name} declared in z1.h but not exported"
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_abi_version_and_strerror():
+    assert B.z1_abi_version() == 1
+    for s in range(6):
+        assert B.strerror(s)
+    assert B.strerror(99) == "unknown status"
+
+
+def test_single_hip_runtime():
+    """libz1 binds to the HIP runtime torch already loaded."""
+    rts = B.hip_runtimes_loaded()
+    assert len(rts) == 1, rts
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_plan_bitexact_vs_oracle(name):
+    w = W.WORKLOADS[name]
+    start, ln, off, arena = B.z1_shard_plan(w.numel, w.dp_size, w.rank)
+    o_start, o_len = oracle.get().shard_plan(w.numel, w.dp_size, w.rank)
+    assert (start == o_start).all() and (ln == o_len).all()
+    _check_arena(start, ln, off, arena)
+
+
+def _check_arena(start, ln, off, arena):
+    assert (off % 8 == start % 8).all(), "arena offset must share the slice's residue mod 8"
+    end = off + ln
+    assert (off[1:] >= end[:-1]).all(), "arena slices overlap or go backwards"
+    assert (off >= 0).all() and (end <= arena).all()
+    assert arena - int(ln.sum()) <= 7 * len(ln), "more padding than 7 per tensor"
+    if len(ln):
+        assert arena == int(end[-1])
+
+
+def test_plan_bruteforce_vs_oracle():
+    o = oracle.get()
+    n = np.arange(300, dtype=np.int64)
+    for D in range(1, 18):
+        for r in range(D):
+            s, l, off, arena = B.z1_shard_plan(n, D, r)
+            os_, ol = o.shard_plan(n, D, r)
+            assert (s == os_).all() and (l == ol).all()
+            _check_arena(s, l, off, arena)
+
+
+def test_plan_large_numel():
+    numel = [2 ** 40 + 3, 2 ** 33 - 1, 7, 0, 1]
+    for D in (1, 7, 8, 1000):
+        for r in (0, D // 2, D - 1):
+            s, l, _, _ = B.z1_shard_plan(numel, D, r)
+            os_, ol = oracle.get().shard_plan(numel, D, r)
+            assert (s == os_).all() and (l == ol).all()
+
+
+def test_plan_errors():
+    P = ctypes.POINTER(ctypes.c_int64)
+    buf = (ctypes.c_int64 * 4)()
+    ae = ctypes.c_int64()
+    numel = (ctypes.c_int64 * 2)(5, 7)
+    cast = lambda a: ctypes.cast(a, P)  # noqa: E731
+    L = B.lib
+    assert L.z1_shard_plan(2, cast(numel), 0, 0, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(2, cast(numel), 4, 4, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(2, cast(numel), 4, -1, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(-1, cast(numel), 4, 0, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(2, None, 4, 0, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(2, cast(numel), 4, 0, cast(buf), cast(buf), cast(buf), None) == B.Z1_EINVAL
+    neg = (ctypes.c_int64 * 2)(5, -1)
+    assert L.z1_shard_plan(2, cast(neg), 4, 0, cast(buf), cast(buf), cast(buf), ctypes.byref(ae)) == B.Z1_EINVAL
+    assert L.z1_shard_plan(0, None, 1, 0, None, None, None, ctypes.byref(ae)) == B.Z1_OK and ae.value == 0
+
+
+def _bind(**over):
+    numel = (ctypes.c_int64 * 1)(1024)
+    w = (ctypes.c_void_p * 1)(0x10000)
+    g = (ctypes.c_void_p * 2)(0x20000, 0x30000)
+    b = B.Bind(n_tensors=1, dp_size=1, rank=0, n_micro=2,
+               numel=ctypes.cast(numel, ctypes.POINTER(ctypes.c_int64)),
+               weights=ctypes.cast(w, ctypes.POINTER(ctypes.c_void_p)),
+               grads=ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)),
+               master=0x40000, exp_avg=0x50000, exp_avg_sq=0x60000, acc=0x70000,
+               arena_elems=1024, chunk_elems=0, max_blocks=0, reserved=0)
+    for k, v in over.items():
+        if k in ("w0", "g1"):
+            (w if k == "w0" else g)[0 if k == "w0" else 1] = v
+        else:
+            setattr(b, k, v)
+    return b, (numel, w, g)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_micro=0), B.Z1_EINVAL), (dict(dp_size=0), B.Z1_EINVAL),
+    (dict(rank=1), B.Z1_EINVAL), (dict(reserved=1), B.Z1_EINVAL),
+    (dict(chunk_elems=1000), B.Z1_EINVAL), (dict(chunk_elems=1 << 21), B.Z1_EINVAL),
+    (dict(arena_elems=1023), B.Z1_EINVAL), (dict(max_blocks=-1), B.Z1_EINVAL),
+    (dict(master=0), B.Z1_EINVAL), (dict(w0=0), B.Z1_EINVAL), (dict(g1=0), B.Z1_EINVAL),
+    (dict(w0=0x10008), B.Z1_EALIGN), (dict(g1=0x30002), B.Z1_EALIGN),
+    (dict(acc=0x70004), B.Z1_EALIGN),
+])
+def test_plan_create_rejects_before_device_work(over, status):
+    """Validation happens on the host: fake addresses never reach the device."""
+    b, keep = _bind(**over)
+    h = ctypes.c_void_p(1)
+    assert B.lib.z1_plan_create(ctypes.byref(h), ctypes.byref(b), None) == status
+    assert h.value is None
+
+
+def test_null_plan_calls():
+    L = B.lib
+    assert L.z1_plan_create(None, None, None) == B.Z1_EINVAL
+    assert L.z1_accum_grads(None, 0, None) == B.Z1_EINVAL
+    assert L.z1_grad_norm_sq(None, None, None) == B.Z1_EINVAL
+    hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
+    assert L.z1_adamw_step(None, ctypes.byref(hp), None, None) == B.Z1_EINVAL
+    assert L.z1_plan_query(None, None) == B.Z1_EINVAL
+    assert L.z1_plan_destroy(None) == B.Z1_OK
+    assert L.z1_probe_copy(None, None, 16, None) == B.Z1_EINVAL
+    assert L.z1_probe_copy(0x1000, 0x2000, 15, None) == B.Z1_EINVAL
+    assert L.z1_probe_copy(0x1008, 0x2000, 16, None) == B.Z1_EALIGN
