@@ -135,7 +135,7 @@ typedef struct z1_bind {
     int64_t arena_elems;    /* length the caller allocated; must be >= the
                                value z1_shard_plan returns                  */
     int64_t chunk_elems;    /* work unit in elements; 0 = library default
-                               (8192); otherwise a multiple of 1024 in
+                               (4096); otherwise a multiple of 1024 in
                                [1024, 1048576]                              */
     int32_t max_blocks;     /* 0 = one workgroup per chunk; otherwise the
                                grid size of the accumulation and AdamW

@@ -12,7 +12,7 @@ namespace z1 {
 // 1024 consecutive elements per vector step.
 constexpr int kBlock = 256;
 constexpr int kVec = 4;
-constexpr int64_t kDefaultChunk = 8192;
+constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxChunk = 1 << 20;
 constexpr int kFinBlock = 1024;
 

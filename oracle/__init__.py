@@ -12,6 +12,8 @@ tensor, concatenated in tensor order.
 
 Parity status of each function (what pins it, see ``tests/pins.py``):
   shard_plan   brute force + numpy.array_split boundaries + invariants
+  shard_plan_flat  brute force vs numpy.array_split of the concatenation
+  shard_plan_dim0  brute force vs torch.chunk along dim 0
   bf16_rne     torch CPU cast on non-NaN patterns + nearest/ties-to-even check
   accumulate   exact binary64 sums rounded once to binary32, per add
   norm_sq      closed form for constant input + math.fsum error bound
@@ -64,6 +66,11 @@ class Oracle:
         P = ctypes.c_void_p
         L.z1o_shard_plan.argtypes = [ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, P, P]
         L.z1o_shard_plan.restype = ctypes.c_int
+        L.z1o_shard_plan_flat.argtypes = [ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32, P, P]
+        L.z1o_shard_plan_flat.restype = ctypes.c_int
+        L.z1o_shard_plan_dim0.argtypes = [ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32,
+                                          P, P]
+        L.z1o_shard_plan_dim0.restype = ctypes.c_int
         L.z1o_bf16_rne.argtypes = [ctypes.c_float]
         L.z1o_bf16_rne.restype = ctypes.c_uint16
         L.z1o_bf16_rne_array.argtypes = [ctypes.c_int64, P, P]
@@ -96,6 +103,37 @@ class Oracle:
         if rc != 0:
             raise ValueError("invalid shard plan arguments")
         return start, ln
+
+    def shard_plan_flat(self, numel: Sequence[int], dp_size: int, rank: int
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+        """Flatten-then-split: the rank's range of the concatenation, per tensor."""
+        n = np.ascontiguousarray(np.asarray(numel, dtype=np.int64))
+        start = np.zeros(len(n), np.int64)
+        ln = np.zeros(len(n), np.int64)
+        if self.lib.z1o_shard_plan_flat(len(n), _ptr(n), dp_size, rank, _ptr(start), _ptr(ln)):
+            raise ValueError("invalid shard plan arguments")
+        return start, ln
+
+    def shard_plan_dim0(self, numel: Sequence[int], rows: Sequence[int], dp_size: int,
+                        rank: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Dim-0 sharding: ceil(rows/D) rows per rank, in rank order."""
+        n = np.ascontiguousarray(np.asarray(numel, dtype=np.int64))
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        start = np.zeros(len(n), np.int64)
+        ln = np.zeros(len(n), np.int64)
+        if self.lib.z1o_shard_plan_dim0(len(n), _ptr(n), _ptr(r), dp_size, rank, _ptr(start),
+                                        _ptr(ln)):
+            raise ValueError("invalid shard plan arguments")
+        return start, ln
+
+    def plan(self, kind: str, numel, rows, dp_size, rank):
+        if kind == "per_tensor":
+            return self.shard_plan(numel, dp_size, rank)
+        if kind == "flat":
+            return self.shard_plan_flat(numel, dp_size, rank)
+        if kind == "dim0":
+            return self.shard_plan_dim0(numel, rows, dp_size, rank)
+        raise ValueError(kind)
 
     # O2e -----------------------------------------------------------------
     def bf16_rne(self, x: np.ndarray) -> np.ndarray:

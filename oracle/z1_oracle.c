@@ -57,6 +57,72 @@ Z1O_EXPORT int z1o_shard_plan(int32_t n_tensors, const int64_t *numel,
     return 0;
 }
 
+/* Flatten-then-split (the DeepSpeed layout [T6] §6.3 contrasts with
+ * nanotron's): all tensors concatenated in order form one vector of
+ * total = sum(numel) elements, split evenly like a single tensor (first
+ * total mod dp_size ranks one element longer); a tensor's slice is the
+ * intersection of its range in the concatenation with the rank's range.
+ * Tensors that miss the rank's range get len 0 (start 0). */
+Z1O_EXPORT int z1o_shard_plan_flat(int32_t n_tensors, const int64_t *numel,
+                                   int32_t dp_size, int32_t rank,
+                                   int64_t *start, int64_t *len)
+{
+    if (n_tensors < 0 || dp_size < 1 || rank < 0 || rank >= dp_size)
+        return -1;
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (numel[i] < 0)
+            return -1;
+        total += numel[i];
+    }
+    int64_t q = total / dp_size, rho = total % dp_size;
+    int64_t lo = (int64_t)rank * q + (rank < rho ? rank : rho);
+    int64_t hi = lo + q + (rank < rho ? 1 : 0);
+    int64_t base = 0; /* first element of tensor i in the concatenation */
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        int64_t a = lo > base ? lo : base;
+        int64_t b = hi < base + numel[i] ? hi : base + numel[i];
+        if (a < b) {
+            start[i] = a - base;
+            len[i] = b - a;
+        } else {
+            start[i] = 0;
+            len[i] = 0;
+        }
+        base += numel[i];
+    }
+    return 0;
+}
+
+/* Dim-0 sharding of every tensor ("TorchTitan 生产级预训练方案", appendix
+ * B.1: FSDP2 represents each parameter as a DTensor sharded on dimension 0).
+ * READING: the rows are cut like torch.chunk -- every rank takes
+ * ceil(rows / dp_size) rows in rank order, so the last ranks may hold fewer
+ * rows or none; a rank's slice is its rows times the row length. */
+Z1O_EXPORT int z1o_shard_plan_dim0(int32_t n_tensors, const int64_t *numel,
+                                   const int64_t *rows, int32_t dp_size, int32_t rank,
+                                   int64_t *start, int64_t *len)
+{
+    if (n_tensors < 0 || dp_size < 1 || rank < 0 || rank >= dp_size)
+        return -1;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (numel[i] < 0 || rows[i] < 0 || (rows[i] == 0 && numel[i] != 0) ||
+            (rows[i] > 0 && numel[i] % rows[i] != 0))
+            return -1;
+        int64_t row_len = rows[i] ? numel[i] / rows[i] : 0;
+        int64_t per = (rows[i] + dp_size - 1) / dp_size;
+        int64_t r0 = (int64_t)rank * per;
+        int64_t r1 = r0 + per;
+        if (r0 > rows[i])
+            r0 = rows[i];
+        if (r1 > rows[i])
+            r1 = rows[i];
+        start[i] = r0 * row_len;
+        len[i] = (r1 - r0) * row_len;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* bf16 <-> fp32                                                       */
 /* ------------------------------------------------------------------ */

@@ -92,6 +92,40 @@ def check_plan_large(o):
         assert (tot == numel).all()
 
 
+def check_plan_flat_bruteforce(o):
+    """Flatten-then-split equals numpy.array_split of the concatenated indices,
+    read back per tensor."""
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        n_t = int(rng.integers(1, 9))
+        numel = rng.integers(0, 40, size=n_t).astype(np.int64)
+        total = int(numel.sum())
+        base = np.concatenate([[0], np.cumsum(numel)[:-1]])
+        for D in range(1, 12):
+            parts = np.array_split(np.arange(total), D)
+            for r in range(D):
+                s, ln = o.shard_plan_flat(numel, D, r)
+                got = np.concatenate([base[i] + s[i] + np.arange(ln[i]) for i in range(n_t)]) \
+                    if ln.sum() else np.zeros(0, np.int64)
+                assert np.array_equal(got, parts[r]), (numel, D, r)
+                assert ((s >= 0) & (s + ln <= numel)).all()
+
+
+def check_plan_dim0_bruteforce(o):
+    """Dim-0 sharding equals torch.chunk along dim 0 (rank r takes chunk r,
+    or nothing when torch.chunk returns fewer than D chunks)."""
+    for rows in range(0, 40):
+        for cols in (1, 3):
+            x = torch.arange(rows * cols).reshape(rows, cols)
+            for D in range(1, 12):
+                chunks = torch.chunk(x, D, dim=0) if rows else ()
+                for r in range(D):
+                    s, ln = o.shard_plan_dim0([rows * cols], [rows], D, r)
+                    want = chunks[r].reshape(-1).numpy() if r < len(chunks) else np.zeros(0)
+                    got = np.arange(s[0], s[0] + ln[0])
+                    assert np.array_equal(got, want), (rows, cols, D, r)
+
+
 # ---------------------------------------------------------------------------
 # O2e bf16 round-to-nearest-even
 # ---------------------------------------------------------------------------
@@ -385,7 +419,8 @@ def check_step_vs_torch_tiny(o):
         assert (wbits == tw).all(), "bf16 weights differ from torch's cast of the master"
 
 
-ALL = [check_plan_bruteforce, check_plan_large, check_rne_ties, check_rne_nan,
+ALL = [check_plan_bruteforce, check_plan_large, check_plan_flat_bruteforce,
+       check_plan_dim0_bruteforce, check_rne_ties, check_rne_nan,
        check_rne_vs_torch, check_rne_nearest, check_accumulate_rounding,
        check_accumulate_exact_small, check_norm_constant, check_norm_fsum,
        check_clip_vs_torch, check_adamw_step1_closed_form, check_adamw_constant_gradient,

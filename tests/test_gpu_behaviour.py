@@ -1,0 +1,162 @@
+"""GPU behaviour beyond parity: determinism, call order, resume."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mixed_precision_zero_amd import binding as B
+from mixed_precision_zero_amd import workloads as W
+from mixed_precision_zero_amd.shard import ShardStep
+
+pytestmark = pytest.mark.gpu
+
+RAGGED_SMALL = dataclasses.replace(
+    W.RAGGED, name="ragged_small", shapes=W.ragged_shapes(300, 14, seed=5), n_micro=3,
+    hot_tensors=(3, 50), steps=3)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _fresh(w, **kw):
+    st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device="cuda", **kw)
+    master = W.make_master(w, seed=0, device="cuda")
+    st.scatter_to_arena(st.master, master)
+    for wt, mt in zip(st.weights, master):
+        wt.copy_(mt)
+    return st
+
+
+def _run_steps(st, w, t0, t1):
+    for t in range(t0, t1):
+        for k in range(w.n_micro):
+            W.make_micro_grads(w, t, k, seed=0, device="cuda", out=st.grads[k])
+        st.step(w.hp())
+    torch.cuda.synchronize()
+
+
+def _state(st):
+    return [st.packed(a).cpu().numpy().view(np.uint32) for a in
+            (st.master, st.exp_avg, st.exp_avg_sq, st.acc)] + \
+           [st.packed_weights().view(torch.int16).cpu().numpy(),
+            np.array([st.d_S.item()]).view(np.uint64)]
+
+
+@pytest.mark.parametrize("w", [W.TINY, RAGGED_SMALL], ids=["tiny", "ragged_small"])
+def test_bitwise_deterministic_across_launch_shapes(w):
+    """Same inputs, different chunk sizes and grids: identical bits, S included."""
+    ref = None
+    for chunk, mb in ((0, 0), (1024, 0), (4096, 7), (65536, 1), (0, 1)):
+        st = _fresh(w, chunk_elems=chunk, max_blocks=mb)
+        _run_steps(st, w, 1, 3)
+        got = _state(st)
+        st.close()
+        if ref is None:
+            ref = got
+            continue
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), f"chunk={chunk} max_blocks={mb} changed the result"
+
+
+def test_repeat_runs_identical():
+    w = RAGGED_SMALL
+    outs = []
+    for _ in range(3):
+        st = _fresh(w)
+        _run_steps(st, w, 1, 3)
+        outs.append(_state(st))
+        st.close()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+def test_resume_is_bitexact():
+    """T steps straight equal T1 steps, save caller-owned state, new plan, reload, T-T1 steps."""
+    w = RAGGED_SMALL
+    st = _fresh(w)
+    _run_steps(st, w, 1, 5)
+    straight = _state(st)
+    st.close()
+
+    st = _fresh(w)
+    _run_steps(st, w, 1, 3)
+    saved = {k: getattr(st, k).cpu().clone() for k in ("master", "exp_avg", "exp_avg_sq")}
+    saved_w = [x.cpu().clone() for x in st.weights]
+    st.close()
+    del st
+    st = _fresh(w)
+    for k, v in saved.items():
+        getattr(st, k).copy_(v)
+    for x, v in zip(st.weights, saved_w):
+        x.copy_(v)
+    st.t = 2
+    _run_steps(st, w, 3, 5)
+    resumed = _state(st)
+    st.close()
+    for a, b in zip(straight, resumed):
+        assert np.array_equal(a, b)
+
+
+def test_call_order_errors():
+    w = W.TINY
+    st = _fresh(w)
+    hp = dict(w.hp())
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_accum_grads(st.plan, 1)
+    assert e.value.status == B.Z1_ESTATE
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_grad_norm_sq(st.plan, st.d_S)
+    assert e.value.status == B.Z1_ESTATE
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_adamw_step(st.plan, d_S=st.d_S, step=1, **hp)
+    assert e.value.status == B.Z1_ESTATE
+    st.accumulate(0)
+    with pytest.raises(B.Z1Error) as e:          # norm before the last pass
+        st.norm()
+    assert e.value.status == B.Z1_ESTATE
+    st.accumulate(0)                            # k = 0 restarts the step
+    st.accumulate(1)
+    with pytest.raises(B.Z1Error) as e:          # clipping on: norm first
+        B.z1_adamw_step(st.plan, d_S=st.d_S, step=1, **hp)
+    assert e.value.status == B.Z1_ESTATE
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_accum_grads(st.plan, 2)             # k out of range
+    assert e.value.status == B.Z1_EINVAL
+    st.norm()
+    bad = dict(hp, beta1=1.0)
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_adamw_step(st.plan, d_S=st.d_S, step=1, **bad)
+    assert e.value.status == B.Z1_EINVAL
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_adamw_step(st.plan, d_S=st.d_S, step=0, **hp)
+    assert e.value.status == B.Z1_EINVAL
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_adamw_step(st.plan, d_S=None, step=1, **hp)
+    assert e.value.status == B.Z1_EINVAL
+    with pytest.raises(B.Z1Error) as e:
+        B.z1_grad_norm_sq(st.plan, st.d_S.data_ptr() + 4)
+    assert e.value.status == B.Z1_EALIGN
+    B.z1_adamw_step(st.plan, d_S=st.d_S, step=1, **hp)
+    with pytest.raises(B.Z1Error) as e:          # a new step starts at k = 0
+        B.z1_accum_grads(st.plan, 1)
+    assert e.value.status == B.Z1_ESTATE
+    # clipping off: the norm is optional
+    st.accumulate(0)
+    st.accumulate(1)
+    B.z1_adamw_step(st.plan, d_S=None, step=2, **dict(hp, clip=0.0))
+    torch.cuda.synchronize()
+    st.close()
+
+
+def test_probe_copy():
+    n = (1 << 24) + 48
+    src = torch.randn(n // 4, device="cuda")
+    dst = torch.zeros_like(src)
+    B.z1_probe_copy(src, dst, n)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)

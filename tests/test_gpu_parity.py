@@ -86,3 +86,19 @@ def test_clip_disabled():
 
 def test_smollm135m():
     _run(W.SMOLLM_135M, 3)
+
+
+def test_ragged_full():
+    """4096 tensors, 533 empty and 181 single-element slices on rank 6 of 7, K=16,
+    41 hot tensors: heavy clipping (c ~ 2e-5)."""
+    _run(W.RAGGED, 3)
+
+
+def test_llama1p7b():
+    _run(W.LLAMA_1P7B, 3)
+
+
+def test_llama7b_headline_shape():
+    """The benchmarked workload and launch configuration (842,301,952 shard
+    elements), every element compared."""
+    _run(W.LLAMA_7B, 2, canaries=False)

@@ -20,6 +20,14 @@ MUTANTS = {
          "len[i] = q + (dp_size - 1 - rank < rho ? 1 : 0);"),
         ("start[i] = (int64_t)rank * q + (rank < rho ? rank : rho);",
          "start[i] = (int64_t)rank * q + (rank > dp_size - rho ? rank - (dp_size - rho) : 0);")],
+    "flat_extra_to_last": [("int64_t lo = (int64_t)rank * q + (rank < rho ? rank : rho);",
+                            "int64_t lo = (int64_t)rank * q + (rank > rho ? rank - rho : 0);"),
+                           ("int64_t hi = lo + q + (rank < rho ? 1 : 0);",
+                            "int64_t hi = lo + q + (rank >= dp_size - rho ? 1 : 0);")],
+    "flat_off_by_one": [("int64_t b = hi < base + numel[i] ? hi : base + numel[i];",
+                         "int64_t b = hi <= base + numel[i] ? hi : base + numel[i] - 1;")],
+    "dim0_floor_rows": [("int64_t per = (rows[i] + dp_size - 1) / dp_size;",
+                         "int64_t per = rows[i] / dp_size;")],
     "rne_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
     "rne_truncate": [("kept += 1u;", "kept += 0u;")],
     "rne_nan_not_quieted": [("| 0x0040u", "| 0x0000u"),
