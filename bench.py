@@ -37,8 +37,8 @@ KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "z1_kernels.
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems (0 = library default)")
     ap.add_argument("--max-blocks", type=int, default=0)
@@ -158,6 +158,10 @@ def main():
     adam_ms = np.array([evs[s][w.n_micro + 1].elapsed_time(evs[s][w.n_micro + 2])
                         for s in range(args.steps)])
     adam_avg = float(adam_ms.mean())
+    step_ms = [evs[s][0].elapsed_time(evs[s][n_ev - 1]) for s in range(args.steps)]
+    log("[bench] per-step ms: " + " ".join(f"{x:.3f}" for x in step_ms))
+    log(f"[bench] k_adamw ms: mean {adam_avg:.4f} median {float(np.median(adam_ms)):.4f} "
+        f"min {float(adam_ms.min()):.4f} max {float(adam_ms.max()):.4f}")
     acc_first = float(acc_ms[:, 0].mean())
     acc_next = float(acc_ms[:, 1:].mean()) if w.n_micro > 1 else None
 
@@ -235,7 +239,8 @@ def main():
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
                      "launch_ms": adam_avg},
         "kernels_ms": {"accum_first": acc_first, "accum_next": acc_next,
-                       "norm_fin": float(norm_ms.mean()), "adamw": adam_avg},
+                       "norm_fin": float(norm_ms.mean()), "adamw": adam_avg,
+                       "adamw_median": float(np.median(adam_ms))},
         "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
         "step_bytes_per_param": h3_bytes // L if L else None,
         "optimizer_step_params_per_s": L / ((adam_avg + float(norm_ms.mean())) / 1e3),

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 1
+#define Z1_ABI_VERSION 2
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -107,6 +107,39 @@ z1_status z1_shard_plan(int32_t n_tensors, const int64_t *numel, int32_t dp_size
                         int32_t rank, int64_t *start, int64_t *len, int64_t *arena_off,
                         int64_t *arena_elems);
 
+/* How a tensor list is cut into per-rank slices.  Every kind gives each
+ * tensor one contiguous slice [start, start+len) per rank (possibly empty),
+ * so the step itself is the same for all of them. */
+typedef enum z1_plan_kind {
+    /* each tensor split evenly on its own (z1_shard_plan above; nanotron,
+     * "ZeRO-1 风格的 Distributed Optimizer" §6.3) */
+    Z1_PLAN_PER_TENSOR = 0,
+    /* all tensors concatenated in order and the concatenation split evenly,
+     * first (total mod dp_size) ranks one element longer; a tensor's slice is
+     * its overlap with the rank's range (the flatten-first layout §6.3
+     * contrasts nanotron with) */
+    Z1_PLAN_FLAT = 1,
+    /* each tensor's rows (dimension 0) split like torch.chunk: ceil(rows /
+     * dp_size) rows per rank in rank order, the last ranks possibly short or
+     * empty ("TorchTitan 生产级预训练方案", appendix B.1: FSDP2 shards every
+     * parameter on dimension 0; the rounding is not on the page) */
+    Z1_PLAN_DIM0 = 2
+} z1_plan_kind;
+
+/* ------------------------------------------------------------------------
+ * z1_shard_plan_kind -- z1_shard_plan for any z1_plan_kind.
+ *
+ * rows: host [n_tensors] dimension-0 sizes, read only for Z1_PLAN_DIM0
+ * (numel[i] must be a multiple of rows[i]; rows[i] == 0 only with
+ * numel[i] == 0); may be NULL otherwise.  Empty slices report start 0.
+ * Arena offsets follow the same rule as z1_shard_plan.
+ * Errors: as z1_shard_plan, plus Z1_EINVAL for an unknown kind or bad rows.
+ * ------------------------------------------------------------------------ */
+z1_status z1_shard_plan_kind(int32_t kind, int32_t n_tensors, const int64_t *numel,
+                             const int64_t *rows, int32_t dp_size, int32_t rank,
+                             int64_t *start, int64_t *len, int64_t *arena_off,
+                             int64_t *arena_elems);
+
 /* Buffers and geometry bound to a plan.  All device buffers are caller-owned
  * and must stay allocated until z1_plan_destroy. */
 typedef struct z1_bind {
@@ -140,7 +173,16 @@ typedef struct z1_bind {
     int32_t max_blocks;     /* 0 = one workgroup per chunk; otherwise the
                                grid size of the accumulation and AdamW
                                kernels (each workgroup loops over chunks)  */
-    int32_t reserved;       /* must be 0                                    */
+    int32_t plan_kind;      /* z1_plan_kind (0 = per tensor)                */
+    const int64_t *rows;    /* host [n_tensors] dim-0 sizes for
+                               Z1_PLAN_DIM0, else NULL                      */
+    /* Per-tensor multipliers, host [n_tensors] each, NULL = all 1.0:
+     * tensor i steps with lr*lr_scale[i] and weight_decay*wd_scale[i]
+     * (Nanotron Guide, Spectral muTransfer: eta_hidden = eta_0 / d_model;
+     * wd_scale 0 keeps a tensor out of weight decay).  Copied at creation;
+     * must be finite, wd_scale >= 0.                                       */
+    const double *lr_scale;
+    const double *wd_scale;
 } z1_bind;
 
 /* Geometry of a created plan. */
@@ -163,7 +205,7 @@ typedef struct z1_plan_info {
  * the call.  The upload is enqueued on `stream` and the call waits for it
  * (plan creation is not part of the step), so the plan is ready on return.
  * Errors: Z1_EINVAL (bad geometry, null pointers, arena too small,
- * bad chunk_elems, reserved != 0), Z1_EALIGN (a weight, gradient or arena
+ * bad chunk_elems, bad plan_kind / rows / multipliers), Z1_EALIGN (a weight, gradient or arena
  * pointer not 16-byte aligned), Z1_ENOMEM, Z1_EHIP.  *out is NULL on error.
  * ------------------------------------------------------------------------ */
 z1_status z1_plan_create(z1_plan **out, const z1_bind *bind, z1_stream stream);
@@ -228,7 +270,8 @@ typedef struct z1_adamw_hp {
  *
  * Reads S from the DEVICE pointer d_S_global (no host round trip), forms
  * c = min(1, clip / (sqrt(S) + 1e-6)) (c = 1 when clip <= 0), then for every
- * shard element, in binary64 from the stored fp32 values:
+ * shard element of tensor i, in binary64 from the stored fp32 values, with
+ * lr = hp->lr * lr_scale[i] and wd = hp->weight_decay * wd_scale[i]:
  *   g = c*acc;  p = p*(1 - lr*wd);  m = beta1*m + (1-beta1)*g;
  *   v = beta2*v + (1-beta2)*g*g;  mhat = m/(1-beta1^t);  vhat = v/(1-beta2^t);
  *   p = p - lr*mhat/(sqrt(vhat) + eps)
@@ -245,6 +288,36 @@ typedef struct z1_adamw_hp {
  * ------------------------------------------------------------------------ */
 z1_status z1_adamw_step(z1_plan *plan, const z1_adamw_hp *hp, const double *d_S_global,
                         z1_stream stream);
+
+/* Learning-rate schedule (host only).  Nanotron Guide, config.yaml:
+ * learning_rate (peak), lr_warmup_steps, lr_decay_steps, min_decay_lr; the
+ * decay shape is not on the page. */
+typedef enum z1_decay_style {
+    Z1_DECAY_NONE = 0,    /* peak after warmup                              */
+    Z1_DECAY_LINEAR = 1,  /* straight line from peak to minimum             */
+    Z1_DECAY_COSINE = 2   /* half cosine from peak to minimum               */
+} z1_decay_style;
+
+typedef struct z1_lr_schedule {
+    double lr_max;          /* peak learning rate                           */
+    double lr_min;          /* learning rate after the decay                */
+    int64_t warmup_steps;   /* >= 0                                         */
+    int64_t decay_steps;    /* >= 0, counted from the end of warmup         */
+    int32_t decay_style;    /* z1_decay_style                               */
+    int32_t reserved;       /* must be 0                                    */
+} z1_lr_schedule;
+
+/* ------------------------------------------------------------------------
+ * z1_lr_at -- learning rate of step t (t >= 0), in binary64:
+ *   t <= warmup_steps (warmup > 0):  lr_max * t / warmup_steps
+ *   after warmup, d = t - warmup_steps:
+ *     NONE: lr_max;  d >= decay_steps: lr_min;  else tau = d / decay_steps,
+ *     LINEAR: lr_max + (lr_min - lr_max) * tau,
+ *     COSINE: lr_min + (lr_max - lr_min) * 0.5 * (1 + cos(pi * tau)).
+ * The caller passes the result as z1_adamw_hp.lr.
+ * Errors: Z1_EINVAL for NULL, negative counts, unknown style, t < 0.
+ * ------------------------------------------------------------------------ */
+z1_status z1_lr_at(const z1_lr_schedule *schedule, int64_t step, double *lr);
 
 /* ------------------------------------------------------------------------
  * Measurement aid (not part of the step): a streaming copy of n_bytes

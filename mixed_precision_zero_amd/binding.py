@@ -25,9 +25,12 @@ Z1_OK, Z1_EINVAL, Z1_EALIGN, Z1_ENOMEM, Z1_EHIP, Z1_ESTATE = range(6)
 _NAMES = {0: "Z1_OK", 1: "Z1_EINVAL", 2: "Z1_EALIGN", 3: "Z1_ENOMEM", 4: "Z1_EHIP",
           5: "Z1_ESTATE"}
 
-EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_plan_create",
-           "z1_plan_destroy", "z1_plan_query", "z1_plan_layout", "z1_accum_grads",
-           "z1_grad_norm_sq", "z1_adamw_step", "z1_probe_copy")
+EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind",
+           "z1_plan_create", "z1_plan_destroy", "z1_plan_query", "z1_plan_layout",
+           "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy")
+
+PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
+DECAY_STYLES = {"none": 0, "linear": 1, "cosine": 2}
 
 
 class Z1Error(RuntimeError):
@@ -45,7 +48,16 @@ class Bind(ctypes.Structure):
                 ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
                 ("exp_avg_sq", ctypes.c_void_p), ("acc", ctypes.c_void_p),
                 ("arena_elems", ctypes.c_int64), ("chunk_elems", ctypes.c_int64),
-                ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_blocks", ctypes.c_int32), ("plan_kind", ctypes.c_int32),
+                ("rows", ctypes.POINTER(ctypes.c_int64)),
+                ("lr_scale", ctypes.POINTER(ctypes.c_double)),
+                ("wd_scale", ctypes.POINTER(ctypes.c_double))]
+
+
+class LRSchedule(ctypes.Structure):
+    _fields_ = [("lr_max", ctypes.c_double), ("lr_min", ctypes.c_double),
+                ("warmup_steps", ctypes.c_int64), ("decay_steps", ctypes.c_int64),
+                ("decay_style", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -71,6 +83,10 @@ def _load():
         "z1_abi_version": ([], I32),
         "z1_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "z1_shard_plan": ([I32, PI64, I32, I32, PI64, PI64, PI64, PI64], ctypes.c_int),
+        "z1_shard_plan_kind": ([I32, I32, PI64, PI64, I32, I32, PI64, PI64, PI64, PI64],
+                               ctypes.c_int),
+        "z1_lr_at": ([ctypes.POINTER(LRSchedule), I64, ctypes.POINTER(ctypes.c_double)],
+                     ctypes.c_int),
         "z1_plan_create": ([ctypes.POINTER(P), ctypes.POINTER(Bind), P], ctypes.c_int),
         "z1_plan_destroy": ([P], ctypes.c_int),
         "z1_plan_query": ([P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
@@ -128,16 +144,32 @@ def z1_abi_version() -> int:
     return int(lib.z1_abi_version())
 
 
-def z1_shard_plan(numel: Sequence[int], dp_size: int, rank: int):
+def z1_shard_plan(numel: Sequence[int], dp_size: int, rank: int, kind: str = "per_tensor",
+                  rows: Optional[Sequence[int]] = None):
     """(start, len, arena_off, arena_elems) of this rank's shard plan."""
     n = _i64(numel)
     start = np.zeros(n.size, np.int64)
     ln = np.zeros(n.size, np.int64)
     off = np.zeros(n.size, np.int64)
     ae = np.zeros(1, np.int64)
-    _check(lib.z1_shard_plan(n.size, _p64(n), dp_size, rank, _p64(start), _p64(ln), _p64(off),
-                             _p64(ae)), "z1_shard_plan")
+    if kind == "per_tensor" and rows is None:
+        _check(lib.z1_shard_plan(n.size, _p64(n), dp_size, rank, _p64(start), _p64(ln),
+                                 _p64(off), _p64(ae)), "z1_shard_plan")
+    else:
+        r = _i64(rows) if rows is not None else None
+        _check(lib.z1_shard_plan_kind(PLAN_KINDS[kind], n.size, _p64(n),
+                                      _p64(r) if r is not None else None, dp_size, rank,
+                                      _p64(start), _p64(ln), _p64(off), _p64(ae)),
+               "z1_shard_plan_kind")
     return start, ln, off, int(ae[0])
+
+
+def z1_lr_at(step: int, *, lr_max: float, lr_min: float, warmup_steps: int, decay_steps: int,
+             decay_style: str = "cosine") -> float:
+    sc = LRSchedule(lr_max, lr_min, warmup_steps, decay_steps, DECAY_STYLES[decay_style], 0)
+    out = ctypes.c_double()
+    _check(lib.z1_lr_at(ctypes.byref(sc), int(step), ctypes.byref(out)), "z1_lr_at")
+    return out.value
 
 
 class Plan:
@@ -162,7 +194,10 @@ class Plan:
 
 def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Sequence,
                    grads: Sequence[Sequence], master, exp_avg, exp_avg_sq, acc,
-                   chunk_elems: int = 0, max_blocks: int = 0, stream=None) -> Plan:
+                   chunk_elems: int = 0, max_blocks: int = 0, stream=None,
+                   kind: str = "per_tensor", rows: Optional[Sequence[int]] = None,
+                   lr_scale: Optional[Sequence[float]] = None,
+                   wd_scale: Optional[Sequence[float]] = None) -> Plan:
     """Bind device buffers: weights[i] and grads[k][i] are full-size bf16
     tensors (or raw device addresses), the four arenas fp32 of arena_elems."""
     n = _i64(numel)
@@ -176,18 +211,28 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
     gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
     arena = [master, exp_avg, exp_avg_sq, acc]
     sizes = [a.numel() for a in arena if hasattr(a, "numel")]
+    r = _i64(rows) if rows is not None else None
+    ls = np.ascontiguousarray(np.asarray(lr_scale, np.float64)) if lr_scale is not None else None
+    ws = np.ascontiguousarray(np.asarray(wd_scale, np.float64)) if wd_scale is not None else None
+    for a in (r, ls, ws):
+        if a is not None and a.size != n.size:
+            raise ValueError("rows / lr_scale / wd_scale need one entry per parameter")
+    PD = ctypes.POINTER(ctypes.c_double)
     b = Bind(n_tensors=n.size, dp_size=dp_size, rank=rank, n_micro=K, numel=_p64(n),
              weights=ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
              grads=ctypes.cast(gp, ctypes.POINTER(ctypes.c_void_p)),
              master=_dptr(master), exp_avg=_dptr(exp_avg), exp_avg_sq=_dptr(exp_avg_sq),
              acc=_dptr(acc), arena_elems=min(sizes) if sizes else 0,
-             chunk_elems=chunk_elems, max_blocks=max_blocks, reserved=0)
+             chunk_elems=chunk_elems, max_blocks=max_blocks, plan_kind=PLAN_KINDS[kind],
+             rows=_p64(r) if r is not None else None,
+             lr_scale=ls.ctypes.data_as(PD) if ls is not None else None,
+             wd_scale=ws.ctypes.data_as(PD) if ws is not None else None)
     h = ctypes.c_void_p()
     _check(lib.z1_plan_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)),
            "z1_plan_create")
     info = PlanInfo()
     _check(lib.z1_plan_query(h, ctypes.byref(info)), "z1_plan_query")
-    return Plan(h.value, info, (n, wp, gp))
+    return Plan(h.value, info, (n, wp, gp, r, ls, ws))
 
 
 def z1_plan_layout(plan: Plan):

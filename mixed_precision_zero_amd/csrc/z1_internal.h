@@ -14,7 +14,9 @@ constexpr int kBlock = 256;
 constexpr int kVec = 4;
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxChunk = 1 << 20;
-constexpr int kFinBlock = 1024;
+constexpr int kInterleave = 8;  // chunk issue order: 8 interleaved regions
+constexpr int kFinBlock = 256;
+constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
 
 // One unit of work: a piece of one tensor's slice of at most chunk_elems
 // elements.  Pieces are cut at multiples of chunk_elems inside the tensor,
@@ -37,11 +39,16 @@ struct alignas(16) DD {
 struct AdamConsts {
     double lr;
     double beta1, beta2;
-    double omb1, omb2;  // 1 - beta1, 1 - beta2
+    double omb1, omb2;     // 1 - beta1, 1 - beta2
     double eps;
-    double decay;       // 1 - lr * weight_decay
-    double bc1, bc2;    // 1 - beta1^t, 1 - beta2^t
-    double clip;        // <= 0: no clipping
+    double weight_decay;
+    double bc1, bc2;       // 1 - beta1^t, 1 - beta2^t
+    double clip;           // <= 0: no clipping
+};
+
+// Per-tensor multipliers of lr and weight decay.
+struct alignas(16) Scale {
+    double lr, wd;
 };
 
 struct LaunchGeom {
@@ -52,10 +59,11 @@ struct LaunchGeom {
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,
                         DD *partials, bool first, bool last, hipStream_t s);
-hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, double *S, hipStream_t s);
-hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const float *acc,
-                        float *master, float *m, float *v, const AdamConsts &k,
-                        const double *S, hipStream_t s);
+hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
+                           unsigned int *counter, double *S, hipStream_t s);
+hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
+                        const float *acc, float *master, float *m, float *v,
+                        const AdamConsts &k, const double *S, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
 
 }  // namespace z1

@@ -275,18 +275,49 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
 }
 
 // ------------------------------------------------------ norm finalise ----
+// Two levels in one launch: workgroup b sums the per-chunk partials of a
+// fixed contiguous range, writes its double-double to stage[b], and the
+// workgroup that finishes last (a device-scope counter) sums stage[0..G) in
+// index order and writes S.  Every range and every order is fixed by n alone,
+// so S does not depend on timing; nothing waits on another workgroup.
 __global__ __launch_bounds__(kFinBlock) void k_norm_fin(const DD *__restrict__ partials,
-                                                        int64_t n, double *__restrict__ S)
+                                                        int64_t n, DD *__restrict__ stage,
+                                                        unsigned int *__restrict__ counter,
+                                                        double *__restrict__ S)
 {
     __shared__ DD lds[kFinBlock / 64];
+    __shared__ bool is_last;
+    const int64_t G = gridDim.x;
+    const int64_t per = (n + G - 1) / G;
+    const int64_t lo_i = (int64_t)blockIdx.x * per;
+    const int64_t hi_i = lo_i + per < n ? lo_i + per : n;
     double hi = 0.0, lo = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += kFinBlock) {
+    for (int64_t i = lo_i + threadIdx.x; i < hi_i; i += kFinBlock) {
         const DD p = partials[i];
         dd_add(hi, lo, p.hi, p.lo);
     }
     block_reduce_dd<kFinBlock>(hi, lo, lds);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
+        stage[blockIdx.x] = DD{hi, lo};
+        __threadfence();
+        const unsigned int done = atomicAdd(counter, 1u);
+        is_last = done == (unsigned int)(G - 1);
+    }
+    __syncthreads();
+    if (!is_last)
+        return;
+    __threadfence();
+    hi = 0.0;
+    lo = 0.0;
+    for (int64_t i = threadIdx.x; i < G; i += kFinBlock) {
+        const DD p = stage[i];
+        dd_add(hi, lo, p.hi, p.lo);
+    }
+    block_reduce_dd<kFinBlock>(hi, lo, lds);
+    if (threadIdx.x == 0) {
         S[0] = hi + lo;
+        counter[0] = 0u;  // ready for the next launch on this plan
+    }
 }
 
 // -------------------------------------------------------------- AdamW ----
@@ -294,35 +325,48 @@ struct Elem {
     float p, m, v;
 };
 
+// This tensor's learning rate and decay factor (uniform per chunk).
+struct TensorRate {
+    double lr;     // lr * lr_scale
+    double decay;  // 1 - lr_i * (weight_decay * wd_scale)
+};
+
+__device__ __forceinline__ TensorRate tensor_rate(const AdamConsts &k, Scale sc)
+{
+    const double lr = k.lr * sc.lr;
+    const double wd = k.weight_decay * sc.wd;
+    return TensorRate{lr, 1.0 - lr * wd};
+}
+
 // One element of the step in binary64 (see the header comment of z1.h for
 // the formula); the operation order matches the definition term by term.
 __device__ __forceinline__ Elem adamw_elem(float acc, float p32, float m32, float v32,
-                                           const AdamConsts &k, double c)
+                                           const AdamConsts &k, const TensorRate &tr, double c)
 {
     const double g = c * (double)acc;
     double p = (double)p32;
     double m = (double)m32;
     double v = (double)v32;
-    p = p * k.decay;
+    p = p * tr.decay;
     m = k.beta1 * m + k.omb1 * g;
     v = k.beta2 * v + k.omb2 * g * g;
     const double mhat = m / k.bc1;
     const double vhat = v / k.bc2;
-    p = p - k.lr * mhat / (sqrt(vhat) + k.eps);
+    p = p - tr.lr * mhat / (sqrt(vhat) + k.eps);
     return Elem{(float)p, (float)m, (float)v};
 }
 
 __device__ __forceinline__ void adamw_vec(f32x4 a, f32x4 &p, f32x4 &m, f32x4 &v, u32x2 &w,
-                                          const AdamConsts &k, double c)
+                                          const AdamConsts &k, const TensorRate &tr, double c)
 {
     Elem r;
-    r = adamw_elem(a.x, p.x, m.x, v.x, k, c);
+    r = adamw_elem(a.x, p.x, m.x, v.x, k, tr, c);
     p.x = r.p; m.x = r.m; v.x = r.v;
-    r = adamw_elem(a.y, p.y, m.y, v.y, k, c);
+    r = adamw_elem(a.y, p.y, m.y, v.y, k, tr, c);
     p.y = r.p; m.y = r.m; v.y = r.v;
-    r = adamw_elem(a.z, p.z, m.z, v.z, k, c);
+    r = adamw_elem(a.z, p.z, m.z, v.z, k, tr, c);
     p.z = r.p; m.z = r.m; v.z = r.v;
-    r = adamw_elem(a.w, p.w, m.w, v.w, k, c);
+    r = adamw_elem(a.w, p.w, m.w, v.w, k, tr, c);
     p.w = r.p; m.w = r.m; v.w = r.v;
     w.x = bf16_rne(p.x) | (bf16_rne(p.y) << 16);
     w.y = bf16_rne(p.z) | (bf16_rne(p.w) << 16);
@@ -332,6 +376,7 @@ template <int U>
 __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chunks,
                                                   int64_t n_chunks,
                                                   uint16_t *const *__restrict__ wtab,
+                                                  const Scale *__restrict__ scales,
                                                   const float *__restrict__ acc,
                                                   float *__restrict__ master,
                                                   float *__restrict__ exp_avg,
@@ -348,6 +393,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
     for (int64_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
         const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
+        const TensorRate tr = tensor_rate(k, scales[ch.tensor]);
         uint16_t *w = wtab[ch.tensor] + (ch.src - sp.lead);
         const int64_t off = ch.dst - sp.lead;
         const float *a = acc + off;
@@ -375,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
             for (int u = 0; u < U; ++u) {
                 const int q = q0 + u * kBlock + t;
                 u32x2 wb;
-                adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, c);
+                adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
                 st_stream(pv + q, pr[u]);
                 st_stream(mv + q, mr[u]);
                 st_stream(vv + q, vr[u]);
@@ -385,14 +431,14 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
         for (int q = q0 + t; q < sp.qe; q += kBlock) {
             f32x4 pr = ld_stream(pv + q), mr = ld_stream(mv + q), vr = ld_stream(vv + q);
             u32x2 wb;
-            adamw_vec(ld_stream(av + q), pr, mr, vr, wb, k, c);
+            adamw_vec(ld_stream(av + q), pr, mr, vr, wb, k, tr, c);
             st_stream(pv + q, pr);
             st_stream(mv + q, mr);
             st_stream(vv + q, vr);
             st_stream(wv + q, wb);
         }
         for_partial_elems(sp, [&](int e) {
-            const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, c);
+            const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
             p[e] = r.p;
             m[e] = r.m;
             v[e] = r.v;
@@ -448,20 +494,29 @@ hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, 
     return hipGetLastError();
 }
 
-hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, double *S, hipStream_t s)
+hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
+                           unsigned int *counter, double *S, hipStream_t s)
 {
-    k_norm_fin<<<dim3(1), dim3(kFinBlock), 0, s>>>(partials, n_chunks, S);
+    // about 8 partials per thread per stage-1 workgroup, at most kFinStages
+    int64_t g = (n_chunks + 8 * kFinBlock - 1) / (8 * kFinBlock);
+    if (g < 1)
+        g = 1;
+    if (g > kFinStages)
+        g = kFinStages;
+    k_norm_fin<<<dim3((unsigned)g), dim3(kFinBlock), 0, s>>>(partials, n_chunks, stage, counter,
+                                                             S);
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const float *acc,
-                        float *master, float *m, float *v, const AdamConsts &k,
-                        const double *S, hipStream_t s)
+hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
+                        const float *acc, float *master, float *m, float *v,
+                        const AdamConsts &k, const double *S, hipStream_t s)
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
     k_adamw<Z1_UNROLL_ADAM><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(geo.chunks, geo.n_chunks,
-                                                             weight_tab, acc, master, m, v, k, S);
+                                                             weight_tab, scales, acc, master, m, v,
+                                                             k, S);
     return hipGetLastError();
 }
 

@@ -19,13 +19,17 @@ class ShardStep:
                  device="cuda", chunk_elems: int = 0, max_blocks: int = 0,
                  weights: Optional[List[torch.Tensor]] = None,
                  grads: Optional[List[List[torch.Tensor]]] = None,
-                 arena_pad: int = 0):
+                 arena_pad: int = 0, kind: str = "per_tensor",
+                 lr_scale: Optional[Sequence[float]] = None,
+                 wd_scale: Optional[Sequence[float]] = None):
         self.shapes = [tuple(s) for s in shapes]
         self.numel = [int(torch.Size(s).numel()) for s in self.shapes]
+        self.rows = [int(s[0]) if len(s) else 1 for s in self.shapes]
         self.dp_size, self.rank, self.n_micro = dp_size, rank, n_micro
+        self.kind = kind
         self.device = torch.device(device)
         self.start, self.len, self.arena_off, self.arena_elems = B.z1_shard_plan(
-            self.numel, dp_size, rank)
+            self.numel, dp_size, rank, kind=kind, rows=self.rows if kind == "dim0" else None)
         n = self.arena_elems + arena_pad
         f32 = dict(dtype=torch.float32, device=self.device)
         self.master = torch.zeros(n, **f32)
@@ -39,7 +43,9 @@ class ShardStep:
         self.d_S = torch.zeros(1, dtype=torch.float64, device=self.device)
         self.plan = B.z1_plan_create(self.numel, dp_size, rank, self.weights, self.grads,
                                      self.master, self.exp_avg, self.exp_avg_sq, self.acc,
-                                     chunk_elems=chunk_elems, max_blocks=max_blocks)
+                                     chunk_elems=chunk_elems, max_blocks=max_blocks, kind=kind,
+                                     rows=self.rows if kind == "dim0" else None,
+                                     lr_scale=lr_scale, wd_scale=wd_scale)
         self.t = 0
 
     # -- layout helpers (torch copies; initialisation and inspection only) --

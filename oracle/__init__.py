@@ -58,6 +58,16 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data
 
 
+def _segments(segments, L):
+    """(n_seg, seg_len, lr_scale, wd_scale) arrays for the C side."""
+    if segments is None:
+        return 0, None, None, None
+    sl, ls, ws = (np.ascontiguousarray(np.asarray(x, dt)) for x, dt in
+                  zip(segments, (np.int64, np.float64, np.float64)))
+    assert sl.size == ls.size == ws.size and int(sl.sum()) == L
+    return sl.size, sl, ls, ws
+
+
 class Oracle:
     """ctypes view of one compiled oracle library."""
 
@@ -87,6 +97,16 @@ class Oracle:
         L.z1o_step.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P,
                                ctypes.POINTER(_HP), ctypes.POINTER(ctypes.c_double)]
         L.z1o_step.restype = ctypes.c_double
+        L.z1o_adamw_seg.argtypes = [ctypes.c_int64, P, P, P, P, P, ctypes.c_double,
+                                    ctypes.POINTER(_HP), ctypes.c_int32, P, P, P]
+        L.z1o_adamw_seg.restype = None
+        L.z1o_step_seg.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P,
+                                   ctypes.POINTER(_HP), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.c_int32, P, P, P]
+        L.z1o_step_seg.restype = ctypes.c_double
+        L.z1o_lr_at.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+                                ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
+        L.z1o_lr_at.restype = ctypes.c_double
         L.z1o_num_threads.argtypes = []
         L.z1o_num_threads.restype = ctypes.c_int
         self.lib = L
@@ -165,21 +185,23 @@ class Oracle:
 
     # O2d / O2e -----------------------------------------------------------
     def adamw(self, acc, p, m, v, c, *, lr, beta1, beta2, eps, weight_decay, step,
-              clip=0.0, w: Optional[np.ndarray] = None) -> None:
-        """In place on fp32 p, m, v (and the bf16 bits w when given)."""
+              clip=0.0, w: Optional[np.ndarray] = None, segments=None) -> None:
+        """In place on fp32 p, m, v (and the bf16 bits w when given).
+        segments = (seg_len, lr_scale, wd_scale) per tensor, or None."""
         hp = _HP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
         for a in (acc, p, m, v):
             assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == p.size
         if w is not None:
             assert w.dtype == np.uint16 and w.size == p.size and w.flags["C_CONTIGUOUS"]
-        self.lib.z1o_adamw(p.size, _ptr(acc), _ptr(p), _ptr(m), _ptr(v), _ptr(w), c,
-                           ctypes.byref(hp))
+        n_seg, sl, ls, ws = _segments(segments, p.size)
+        self.lib.z1o_adamw_seg(p.size, _ptr(acc), _ptr(p), _ptr(m), _ptr(v), _ptr(w), c,
+                               ctypes.byref(hp), n_seg, _ptr(sl), _ptr(ls), _ptr(ws))
 
     # whole step ------------------------------------------------------------
     def step(self, g: np.ndarray, p: np.ndarray, m: np.ndarray, v: np.ndarray, *, lr,
              beta1, beta2, eps, weight_decay, clip, step,
-             acc: Optional[np.ndarray] = None, w: Optional[np.ndarray] = None
-             ) -> Tuple[float, float, np.ndarray]:
+             acc: Optional[np.ndarray] = None, w: Optional[np.ndarray] = None,
+             segments=None) -> Tuple[float, float, np.ndarray]:
         """O2a..O2e on the packed shard; returns (S, c, acc); p, m, v, w in place."""
         g = np.ascontiguousarray(g, dtype=np.uint16)
         K, L = g.shape
@@ -191,9 +213,15 @@ class Oracle:
             assert w.dtype == np.uint16 and w.size == L and w.flags["C_CONTIGUOUS"]
         hp = _HP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
         c = ctypes.c_double(0.0)
-        S = self.lib.z1o_step(L, K, _ptr(g), _ptr(acc), _ptr(p), _ptr(m), _ptr(v), _ptr(w),
-                              ctypes.byref(hp), ctypes.byref(c))
+        n_seg, sl, ls, ws = _segments(segments, L)
+        S = self.lib.z1o_step_seg(L, K, _ptr(g), _ptr(acc), _ptr(p), _ptr(m), _ptr(v), _ptr(w),
+                                  ctypes.byref(hp), ctypes.byref(c), n_seg, _ptr(sl), _ptr(ls),
+                                  _ptr(ws))
         return float(S), float(c.value), acc
+
+    def lr_at(self, lr_max, lr_min, warmup, decay, style, t) -> float:
+        """Learning rate at step t (style 0 none, 1 linear, 2 cosine decay)."""
+        return float(self.lib.z1o_lr_at(lr_max, lr_min, warmup, decay, style, t))
 
     def num_threads(self) -> int:
         return int(self.lib.z1o_num_threads())

@@ -24,6 +24,7 @@
  * computed independently, so thread count never changes a result.  The norm
  * is a single sequential compensated binary64 sum.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -240,48 +241,103 @@ typedef struct z1o_hp {
  * square root.  Each element is computed in binary64 from the stored fp32
  * values and stored back rounded to binary32 (C's double->float conversion
  * rounds to nearest-even).  [T6] §6.3 / [NG]: the updated master is cast to
- * the bf16 working weight that the all-gather later distributes. */
-Z1O_EXPORT void z1o_adamw(int64_t L, const float *acc, float *p, float *m, float *v,
-                          uint16_t *w, double c, const z1o_hp *hp)
+ * the bf16 working weight that the all-gather later distributes.
+ *
+ * Per-tensor multipliers: the packed shard is n_seg consecutive segments
+ * (seg_len[j] elements each, summing to L); segment j uses
+ * lr_j = lr * lr_scale[j] and wd_j = weight_decay * wd_scale[j]
+ * ([NG] Spectral muP: eta_hidden = eta_0 / d_model; a zero wd_scale keeps a
+ * tensor out of weight decay).  n_seg == 0 means one segment with both
+ * multipliers 1. */
+Z1O_EXPORT void z1o_adamw_seg(int64_t L, const float *acc, float *p, float *m, float *v,
+                              uint16_t *w, double c, const z1o_hp *hp, int32_t n_seg,
+                              const int64_t *seg_len, const double *lr_scale,
+                              const double *wd_scale)
 {
     const double t = (double)hp->step;
     const double bc1 = 1.0 - pow(hp->beta1, t);
     const double bc2 = 1.0 - pow(hp->beta2, t);
+    int64_t seg_start = 0;
+    for (int32_t j = 0; j < (n_seg > 0 ? n_seg : 1); ++j) {
+        const int64_t seg_end = n_seg > 0 ? seg_start + seg_len[j] : L;
+        const double lr = hp->lr * (n_seg > 0 ? lr_scale[j] : 1.0);
+        const double wd = hp->weight_decay * (n_seg > 0 ? wd_scale[j] : 1.0);
 #pragma omp parallel for schedule(static)
-    for (int64_t e = 0; e < L; ++e) {
-        double g = c * (double)acc[e];
-        double pe = (double)p[e];
-        double me = (double)m[e];
-        double ve = (double)v[e];
-        pe = pe * (1.0 - hp->lr * hp->weight_decay);
-        me = hp->beta1 * me + (1.0 - hp->beta1) * g;
-        ve = hp->beta2 * ve + (1.0 - hp->beta2) * g * g;
-        double mhat = me / bc1;
-        double vhat = ve / bc2;
-        pe = pe - hp->lr * mhat / (sqrt(vhat) + hp->eps);
-        p[e] = (float)pe;
-        m[e] = (float)me;
-        v[e] = (float)ve;
-        if (w)
-            w[e] = z1o_bf16_rne(p[e]);
+        for (int64_t e = seg_start; e < seg_end; ++e) {
+            double g = c * (double)acc[e];
+            double pe = (double)p[e];
+            double me = (double)m[e];
+            double ve = (double)v[e];
+            pe = pe * (1.0 - lr * wd);
+            me = hp->beta1 * me + (1.0 - hp->beta1) * g;
+            ve = hp->beta2 * ve + (1.0 - hp->beta2) * g * g;
+            double mhat = me / bc1;
+            double vhat = ve / bc2;
+            pe = pe - lr * mhat / (sqrt(vhat) + hp->eps);
+            p[e] = (float)pe;
+            m[e] = (float)me;
+            v[e] = (float)ve;
+            if (w)
+                w[e] = z1o_bf16_rne(p[e]);
+        }
+        seg_start = seg_end;
     }
+}
+
+Z1O_EXPORT void z1o_adamw(int64_t L, const float *acc, float *p, float *m, float *v,
+                          uint16_t *w, double c, const z1o_hp *hp)
+{
+    z1o_adamw_seg(L, acc, p, m, v, w, c, hp, 0, 0, 0, 0);
+}
+
+/* ------------------------------------------------------------------ */
+/* Learning-rate schedule                                              */
+/* ------------------------------------------------------------------ */
+/* [NG] config: learning_rate (peak), lr_warmup_steps, lr_decay_steps,
+ * min_decay_lr.  READING (the decay shape is not on the page): a linear
+ * warmup reaching the peak at t = warmup, then over decay_steps a linear or
+ * half-cosine decay to the minimum, then the minimum.  style: 0 none (peak
+ * after warmup), 1 linear, 2 cosine. */
+Z1O_EXPORT double z1o_lr_at(double lr_max, double lr_min, int64_t warmup, int64_t decay,
+                            int32_t style, int64_t t)
+{
+    if (warmup > 0 && t <= warmup)
+        return lr_max * (double)t / (double)warmup;
+    if (style == 0)
+        return lr_max;
+    int64_t d = t - (warmup > 0 ? warmup : 0);
+    if (d >= decay)
+        return lr_min;
+    double tau = (double)d / (double)decay;
+    if (style == 1)
+        return lr_max + (lr_min - lr_max) * tau;
+    return lr_min + (lr_max - lr_min) * 0.5 * (1.0 + cos(M_PI * tau));
 }
 
 /* ------------------------------------------------------------------ */
 /* One whole step: O2a -> O2b -> O2c -> O2d -> O2e                      */
 /* ------------------------------------------------------------------ */
 /* Returns S (before clipping); *c_out receives the clip coefficient. */
-Z1O_EXPORT double z1o_step(int64_t L, int32_t K, const uint16_t *g, float *acc,
-                           float *p, float *m, float *v, uint16_t *w,
-                           const z1o_hp *hp, double *c_out)
+Z1O_EXPORT double z1o_step_seg(int64_t L, int32_t K, const uint16_t *g, float *acc,
+                               float *p, float *m, float *v, uint16_t *w,
+                               const z1o_hp *hp, double *c_out, int32_t n_seg,
+                               const int64_t *seg_len, const double *lr_scale,
+                               const double *wd_scale)
 {
     z1o_accumulate(L, K, g, acc);
     double S = z1o_norm_sq(L, acc);
     double c = z1o_clip_coef(S, hp->clip);
-    z1o_adamw(L, acc, p, m, v, w, c, hp);
+    z1o_adamw_seg(L, acc, p, m, v, w, c, hp, n_seg, seg_len, lr_scale, wd_scale);
     if (c_out)
         *c_out = c;
     return S;
+}
+
+Z1O_EXPORT double z1o_step(int64_t L, int32_t K, const uint16_t *g, float *acc,
+                           float *p, float *m, float *v, uint16_t *w,
+                           const z1o_hp *hp, double *c_out)
+{
+    return z1o_step_seg(L, K, g, acc, p, m, v, w, hp, c_out, 0, 0, 0, 0);
 }
 
 Z1O_EXPORT int z1o_num_threads(void)

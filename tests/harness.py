@@ -67,7 +67,7 @@ class Parity:
     """Runs a workload on the GPU and the oracle side by side."""
 
     def __init__(self, w: W.Workload, device="cuda", chunk_elems=0, max_blocks=0,
-                 seed=0, canaries=True):
+                 seed=0, canaries=True, kind="per_tensor", lr_scale=None, wd_scale=None):
         self.w = w
         self.dev = torch.device(device)
         self.o = oracle.get()
@@ -75,8 +75,15 @@ class Parity:
         t0 = time.time()
         self.st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=self.dev,
                             chunk_elems=chunk_elems, max_blocks=max_blocks,
-                            arena_pad=64 if canaries else 0)
-        self.o_start, self.o_len = self.o.shard_plan(w.numel, w.dp_size, w.rank)
+                            arena_pad=64 if canaries else 0, kind=kind,
+                            lr_scale=lr_scale, wd_scale=wd_scale)
+        rows = [s[0] if len(s) else 1 for s in w.shapes]
+        self.o_start, self.o_len = self.o.plan(kind, w.numel, rows, w.dp_size, w.rank)
+        self.segments = None
+        if lr_scale is not None or wd_scale is not None:
+            n = len(w.shapes)
+            self.segments = (self.o_len, lr_scale if lr_scale is not None else [1.0] * n,
+                             wd_scale if wd_scale is not None else [1.0] * n)
         self.L = int(self.o_len.sum())
         # canaries in every arena element outside a slice (gaps and tail)
         self.free_mask = None
@@ -120,7 +127,9 @@ class Parity:
         return bf16_bits(torch.cat(parts))
 
     def plan_matches(self) -> bool:
-        return bool((self.st.start == self.o_start).all() and (self.st.len == self.o_len).all())
+        nz = self.o_len > 0
+        return bool((self.st.len == self.o_len).all() and
+                    (self.st.start[nz] == self.o_start[nz]).all())
 
     def step(self, check=True) -> Optional[StepReport]:
         w, st = self.w, self.st
@@ -136,7 +145,7 @@ class Parity:
         torch.cuda.synchronize()
         t2 = time.time()
         S, c, _ = self.o.step(g, self.p, self.m, self.v, step=t, acc=self.acc, w=self.wbits,
-                              **w.hp())
+                              segments=self.segments, **w.hp())
         del g
         t3 = time.time()
         log(f"[parity] {w.name} step {t}: inputs {t1 - t0:.1f}s gpu {t2 - t1:.2f}s "
@@ -188,10 +197,17 @@ class Parity:
         self.st.close()
 
 
-def assert_report(rep: StepReport, tol_state=1e-6, tol_S=1e-5) -> None:
+def assert_report(rep: StepReport, tol_state=1e-6, tol_S=1e-5, exact=True) -> None:
+    """The contract's tolerances, then (exact=True) bit-exactness: the GPU
+    evaluates the oracle's IEEE operation sequence and both round S once, so
+    every buffer is expected to match bit for bit."""
     assert rep.acc_mismatch == 0, f"step {rep.step}: {rep.acc_mismatch} acc elements differ"
     assert rep.S_rel <= tol_S, f"step {rep.step}: S rel err {rep.S_rel:.3g}"
     for name, e in rep.rel.items():
         assert e <= tol_state, f"step {rep.step}: {name} rel err {e:.3g} > {tol_state}"
     assert rep.bf16_max_ulp <= 1, f"step {rep.step}: bf16 off by {rep.bf16_max_ulp} ulp"
     assert rep.bf16_self_mismatch == 0, f"step {rep.step}: bf16 != RNE(own master)"
+    if exact:
+        assert rep.S_gpu == rep.S_ref, f"step {rep.step}: S not bit-exact"
+        bad = {k: v for k, v in rep.not_bitexact.items() if v}
+        assert not bad, f"step {rep.step}: elements not bit-exact: {bad}"

@@ -381,6 +381,76 @@ def check_adamw_vs_torch(o):
         assert_rel_rms(v, tv, 1e-6, f"v vs torch AdamW t={t}")
 
 
+def check_adamw_segments_vs_torch(o):
+    """Per-tensor lr / weight-decay multipliers: torch.optim.AdamW with one
+    parameter group per segment (lr * lr_scale, wd * wd_scale), binary64;
+    all-ones multipliers give the unsegmented result bit for bit."""
+    rng = np.random.default_rng(12)
+    seg = np.array([3000, 1, 0, 4096, 777], np.int64)
+    lr_s = np.array([1.0, 0.5, 2.0, 1.0 / 4096, 3.0])
+    wd_s = np.array([1.0, 0.0, 1.0, 1.0, 0.0])
+    n = int(seg.sum())
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(4)]
+    # all-ones multipliers == no segments
+    a, b = p0.copy(), p0.copy()
+    ma, va = _zeros(n)
+    mb, vb = _zeros(n)
+    for t, g in enumerate(grads, start=1):
+        o.adamw(g, a, ma, va, 1.0, step=t, **HP)
+        o.adamw(g, b, mb, vb, 1.0, step=t, segments=(seg, np.ones(5), np.ones(5)), **HP)
+    assert np.array_equal(a, b) and np.array_equal(ma, mb) and np.array_equal(va, vb)
+    # against torch parameter groups
+    bounds = np.concatenate([[0], np.cumsum(seg)])
+    params = [torch.nn.Parameter(torch.from_numpy(p0[bounds[j]:bounds[j + 1]].astype(np.float64)))
+              for j in range(len(seg))]
+    groups = [dict(params=[params[j]], lr=HP["lr"] * lr_s[j],
+                   weight_decay=HP["weight_decay"] * wd_s[j]) for j in range(len(seg))]
+    opt = torch.optim.AdamW(groups, betas=(HP["beta1"], HP["beta2"]), eps=HP["eps"],
+                            foreach=False, fused=False)
+    p = p0.copy()
+    m, v = _zeros(n)
+    for t, g in enumerate(grads, start=1):
+        for j, q in enumerate(params):
+            q.grad = torch.from_numpy(g[bounds[j]:bounds[j + 1]].astype(np.float64))
+        opt.step()
+        with torch.no_grad():
+            for q in params:
+                st = opt.state[q]
+                for x in (q, st["exp_avg"], st["exp_avg_sq"]):
+                    x.copy_(x.float().double())
+        o.adamw(g, p, m, v, 1.0, step=t, segments=(seg, lr_s, wd_s), **HP)
+        tp = np.concatenate([q.detach().numpy() for q in params])
+        assert_rel_rms(p, tp, 1e-6, f"segmented p vs torch groups t={t}")
+
+
+def check_lr_schedule(o):
+    """Warmup/decay closed forms at their boundary points; cosine decay
+    against torch's CosineAnnealingLR (closed form in its documentation)."""
+    lmax, lmin, W_, D = 3e-3, 3e-4, 2000, 100000
+    for style in (1, 2):
+        lr = lambda t: o.lr_at(lmax, lmin, W_, D, style, t)  # noqa: E731
+        assert lr(W_) == lmax and lr(W_ // 2) == lmax / 2 and lr(1) == lmax / W_
+        assert lr(W_ + D) == lmin and lr(W_ + D + 12345) == lmin
+        mid = lr(W_ + D // 2)
+        assert abs(mid - (lmax + lmin) / 2) <= 1e-15 * lmax, (style, mid)
+        dec = [lr(t) for t in range(W_, W_ + D + 1, 997)]
+        assert all(x >= y for x, y in zip(dec, dec[1:])), "decay must not increase"
+        assert lr(W_ + 1) < lmax
+    assert o.lr_at(lmax, lmin, W_, D, 0, W_ + 5) == lmax
+    assert o.lr_at(lmax, lmin, 0, D, 2, 0) == lmax and o.lr_at(lmax, lmin, 0, 0, 2, 1) == lmin
+    # cosine phase vs torch (decay counted from the end of warmup)
+    opt = torch.optim.SGD([torch.nn.Parameter(torch.zeros(1))], lr=lmax)
+    Dsmall = 50
+    sch = torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=Dsmall, eta_min=lmin)
+    for k in range(1, Dsmall + 1):
+        opt.step()
+        sch.step()
+        ref = sch.get_last_lr()[0]
+        got = o.lr_at(lmax, lmin, 10, Dsmall, 2, 10 + k)
+        assert abs(got - ref) <= 1e-12 * lmax, (k, got, ref)
+
+
 def check_step_vs_torch_tiny(o):
     """The whole composition on the Tiny workload: in-order fp32 sum of the
     bf16 micro-gradients (torch), clip_grad_norm_ + AdamW in binary64."""
@@ -424,4 +494,5 @@ ALL = [check_plan_bruteforce, check_plan_large, check_plan_flat_bruteforce,
        check_rne_vs_torch, check_rne_nearest, check_accumulate_rounding,
        check_accumulate_exact_small, check_norm_constant, check_norm_fsum,
        check_clip_vs_torch, check_adamw_step1_closed_form, check_adamw_constant_gradient,
-       check_adamw_zero_gradient, check_adamw_vs_torch, check_step_vs_torch_tiny]
+       check_adamw_zero_gradient, check_adamw_vs_torch, check_adamw_segments_vs_torch,
+       check_lr_schedule, check_step_vs_torch_tiny]

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 1
+    assert B.z1_abi_version() == 2
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -107,7 +107,7 @@ def _bind(**over):
                weights=ctypes.cast(w, ctypes.POINTER(ctypes.c_void_p)),
                grads=ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)),
                master=0x40000, exp_avg=0x50000, exp_avg_sq=0x60000, acc=0x70000,
-               arena_elems=1024, chunk_elems=0, max_blocks=0, reserved=0)
+               arena_elems=1024, chunk_elems=0, max_blocks=0, plan_kind=0)
     for k, v in over.items():
         if k in ("w0", "g1"):
             (w if k == "w0" else g)[0 if k == "w0" else 1] = v
@@ -118,7 +118,8 @@ def _bind(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(n_micro=0), B.Z1_EINVAL), (dict(dp_size=0), B.Z1_EINVAL),
-    (dict(rank=1), B.Z1_EINVAL), (dict(reserved=1), B.Z1_EINVAL),
+    (dict(rank=1), B.Z1_EINVAL), (dict(plan_kind=3), B.Z1_EINVAL),
+    (dict(plan_kind=2), B.Z1_EINVAL),  # dim0 without rows
     (dict(chunk_elems=1000), B.Z1_EINVAL), (dict(chunk_elems=1 << 21), B.Z1_EINVAL),
     (dict(arena_elems=1023), B.Z1_EINVAL), (dict(max_blocks=-1), B.Z1_EINVAL),
     (dict(master=0), B.Z1_EINVAL), (dict(w0=0), B.Z1_EINVAL), (dict(g1=0), B.Z1_EINVAL),
@@ -145,3 +146,60 @@ def test_null_plan_calls():
     assert L.z1_probe_copy(None, None, 16, None) == B.Z1_EINVAL
     assert L.z1_probe_copy(0x1000, 0x2000, 15, None) == B.Z1_EINVAL
     assert L.z1_probe_copy(0x1008, 0x2000, 16, None) == B.Z1_EALIGN
+
+
+@pytest.mark.parametrize("kind", ["flat", "dim0"])
+@pytest.mark.parametrize("name", ["tiny", "smollm135m", "llama7b", "ragged"])
+def test_plan_kinds_bitexact_vs_oracle(kind, name):
+    w = W.WORKLOADS[name]
+    rows = [s[0] for s in w.shapes]
+    for D, r in ((w.dp_size, w.rank), (7, 6), (8, 0), (3, 1)):
+        start, ln, off, arena = B.z1_shard_plan(w.numel, D, r, kind=kind,
+                                                rows=rows if kind == "dim0" else None)
+        o_start, o_len = oracle.get().plan(kind, w.numel, rows, D, r)
+        assert (ln == o_len).all()
+        assert (start[ln > 0] == o_start[ln > 0]).all()
+        _check_arena(start, ln, off, arena)
+
+
+def test_plan_kinds_bruteforce_vs_oracle():
+    o = oracle.get()
+    rng = np.random.default_rng(3)
+    for _ in range(40):
+        rows = rng.integers(0, 30, size=6)
+        cols = rng.integers(1, 5, size=6)
+        numel = rows * cols
+        for D in range(1, 10):
+            for r in range(D):
+                for kind in ("flat", "dim0"):
+                    s, l, off, arena = B.z1_shard_plan(numel, D, r, kind=kind, rows=rows)
+                    os_, ol = o.plan(kind, numel, rows, D, r)
+                    assert (l == ol).all() and (s[l > 0] == os_[l > 0]).all(), (kind, numel, D, r)
+                    _check_arena(s, l, off, arena)
+
+
+def test_plan_kind_errors():
+    with pytest.raises(B.Z1Error):
+        B.z1_shard_plan([6, 4], 2, 0, kind="dim0", rows=[4, 2])    # 6 not a multiple of 4
+    with pytest.raises(B.Z1Error):
+        B.z1_shard_plan([6, 0], 2, 0, kind="dim0", rows=[3, 2])    # rows without elements
+    with pytest.raises(B.Z1Error):
+        B.z1_shard_plan([6, 4], 2, 0, kind="dim0")                 # rows missing
+
+
+@pytest.mark.parametrize("style", ["linear", "cosine", "none"])
+def test_lr_schedule_bitexact_vs_oracle(style):
+    o = oracle.get()
+    code = {"none": 0, "linear": 1, "cosine": 2}[style]
+    for (lmax, lmin, W_, D) in ((3e-3, 3e-4, 2000, 100000), (1e-3, 0.0, 0, 10), (5e-4, 1e-5, 7, 0)):
+        for t in list(range(0, 40)) + [W_, W_ + 1, W_ + D // 2, W_ + D, W_ + D + 9, 123456]:
+            got = B.z1_lr_at(t, lr_max=lmax, lr_min=lmin, warmup_steps=W_, decay_steps=D,
+                             decay_style=style)
+            assert got == o.lr_at(lmax, lmin, W_, D, code, t), (style, t)
+
+
+def test_lr_schedule_errors():
+    with pytest.raises(B.Z1Error):
+        B.z1_lr_at(-1, lr_max=1.0, lr_min=0.0, warmup_steps=1, decay_steps=1)
+    with pytest.raises(B.Z1Error):
+        B.z1_lr_at(1, lr_max=1.0, lr_min=0.0, warmup_steps=-1, decay_steps=1)

@@ -88,6 +88,34 @@ def test_smollm135m():
     _run(W.SMOLLM_135M, 3)
 
 
+def test_plan_flat_ragged_small():
+    """Flatten-then-split plan: slices start and end anywhere in a tensor."""
+    shapes = W.ragged_shapes(300, 12, seed=4)
+    w = dataclasses.replace(W.RAGGED, name="ragged_small_flat", shapes=shapes, n_micro=2,
+                            hot_tensors=(), steps=3)
+    _run(w, 3, kind="flat")
+
+
+def test_plan_dim0_smollm():
+    """FSDP2-style dim-0 plan on SmolLM shapes at dp 8 (ceil rows per rank)."""
+    w = dataclasses.replace(W.SMOLLM_135M, name="smollm_dim0", dp_size=8, rank=5, n_micro=2)
+    _run(w, 2, kind="dim0")
+
+
+def test_plan_dim0_last_rank_short():
+    """Rows not divisible by dp: the last ranks get fewer rows or none."""
+    w = dataclasses.replace(W.TINY, name="tiny_dim0", shapes=((7, 33), (5,), (3, 1000)),
+                            dp_size=4, rank=3)
+    _run(w, 2, kind="dim0")
+
+
+def test_mup_multipliers_smollm():
+    """Per-tensor lr (1/d_model on hidden matrices) and no decay on norms."""
+    w = W.SMOLLM_135M
+    lr_s, wd_s = W.mup_multipliers(w.shapes, 576)
+    _run(w, 2, lr_scale=lr_s, wd_scale=wd_s)
+
+
 def test_ragged_full():
     """4096 tensors, 533 empty and 181 single-element slices on rank 6 of 7, K=16,
     41 hot tensors: heavy clipping (c ~ 2e-5)."""

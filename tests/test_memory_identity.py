@@ -53,3 +53,13 @@ def test_7b_shard_state():
     assert L == 842_301_952
     assert M.shard_state_bytes(L) == 12 * 842_301_952        # 10.11 GB
     assert abs(M.optimizer_state_bytes(w.total_params) / GB - 80.86) < 0.01
+
+
+def test_workload_hyperparameters_are_the_tutorials():
+    """Every workload uses the optimizer block printed in tests/golden/hyperparams.json."""
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hyperparams.json")))
+    t = gold["tutorial_6_6"]
+    for w in W.WORKLOADS.values():
+        assert (w.beta1, w.beta2, w.eps, w.weight_decay, w.clip) == \
+            (t["beta1"], t["beta2"], t["eps"], t["weight_decay"], t["clip"]), w.name
+        assert w.init_sigma == gold["guide_config"]["initializer_range"]

@@ -28,6 +28,14 @@ MUTANTS = {
                          "int64_t b = hi <= base + numel[i] ? hi : base + numel[i] - 1;")],
     "dim0_floor_rows": [("int64_t per = (rows[i] + dp_size - 1) / dp_size;",
                          "int64_t per = rows[i] / dp_size;")],
+    "seg_lr_scale_ignored": [("const double lr = hp->lr * (n_seg > 0 ? lr_scale[j] : 1.0);",
+                              "const double lr = hp->lr;")],
+    "seg_wd_scale_ignored": [("const double wd = hp->weight_decay * (n_seg > 0 ? wd_scale[j] : 1.0);",
+                              "const double wd = hp->weight_decay;")],
+    "lr_warmup_off_by_one": [("return lr_max * (double)t / (double)warmup;",
+                              "return lr_max * (double)(t - 1) / (double)warmup;")],
+    "lr_cosine_sign": [("(1.0 + cos(M_PI * tau))", "(1.0 - cos(M_PI * tau))")],
+    "lr_linear_wrong_end": [("return lr_max + (lr_min - lr_max) * tau;", "return lr_max - lr_max * tau;")],
     "rne_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
     "rne_truncate": [("kept += 1u;", "kept += 0u;")],
     "rne_nan_not_quieted": [("| 0x0040u", "| 0x0000u"),
@@ -41,13 +49,12 @@ MUTANTS = {
     "clip_no_eps": [("(sqrt(S) + 1e-6)", "(sqrt(S))")],
     "clip_no_min": [("return c < 1.0 ? c : 1.0;", "return c;")],
     "clip_uses_S": [("(sqrt(S) + 1e-6)", "(S + 1e-6)")],
-    "adamw_decay_without_lr": [("(1.0 - hp->lr * hp->weight_decay)", "(1.0 - hp->weight_decay)")],
+    "adamw_decay_without_lr": [("(1.0 - lr * wd)", "(1.0 - wd)")],
     "adamw_decay_after_update": [
-        ("pe = pe * (1.0 - hp->lr * hp->weight_decay);", ""),
-        ("pe = pe - hp->lr * mhat / (sqrt(vhat) + hp->eps);",
-         "pe = (pe - hp->lr * mhat / (sqrt(vhat) + hp->eps)) * (1.0 - hp->lr * hp->weight_decay);")],
-    "adamw_l2_not_decoupled": [("pe = pe * (1.0 - hp->lr * hp->weight_decay);",
-                                "g = g + hp->weight_decay * pe;")],
+        ("pe = pe * (1.0 - lr * wd);", ""),
+        ("pe = pe - lr * mhat / (sqrt(vhat) + hp->eps);",
+         "pe = (pe - lr * mhat / (sqrt(vhat) + hp->eps)) * (1.0 - lr * wd);")],
+    "adamw_l2_not_decoupled": [("pe = pe * (1.0 - lr * wd);", "g = g + wd * pe;")],
     "adamw_beta_swap_m": [("me = hp->beta1 * me + (1.0 - hp->beta1) * g;",
                            "me = hp->beta2 * me + (1.0 - hp->beta2) * g;")],
     "adamw_beta_swap_v": [("ve = hp->beta2 * ve + (1.0 - hp->beta2) * g * g;",
@@ -56,7 +63,7 @@ MUTANTS = {
     "adamw_no_bias_correction_v": [("double vhat = ve / bc2;", "double vhat = ve;")],
     "adamw_no_bias_correction_m": [("double mhat = me / bc1;", "double mhat = me;")],
     "adamw_bias_power_off_by_one": [("pow(hp->beta1, t)", "pow(hp->beta1, t + 1.0)")],
-    "adamw_update_sign": [("pe = pe - hp->lr * mhat", "pe = pe + hp->lr * mhat")],
+    "adamw_update_sign": [("pe = pe - lr * mhat", "pe = pe + lr * mhat")],
     "adamw_ignores_clip": [("double g = c * (double)acc[e];", "double g = (double)acc[e];")],
     "adamw_weight_from_old_master": [("w[e] = z1o_bf16_rne(p[e]);",
                                       "w[e] = z1o_bf16_rne((float)(double)acc[e] * 0.0f + p[e] * 0.999f);")],
