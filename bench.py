@@ -45,6 +45,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time spent timing the oracle (0 = skip)")
     ap.add_argument("--copy-gb", type=float, default=4.0, help="probe-copy size for the ceiling")
+    ap.add_argument("--plan", default="per_tensor", choices=["per_tensor", "flat", "dim0"],
+                    help="shard plan kind")
+    ap.add_argument("--mup", action="store_true",
+                    help="per-tensor muP lr multipliers and no decay on norms")
+    ap.add_argument("--mode", default="step", choices=["step", "pack"],
+                    help="step: the shard step (default); pack: full-tensor accumulation into "
+                         "the reduce-scatter send buffer, every element of the model")
     return ap.parse_args()
 
 
@@ -90,10 +97,16 @@ def main():
     torch.cuda.set_device(dev)
     w = W.WORKLOADS[args.workload]
     log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+    if args.mode == "pack":
+        return bench_pack(args, w, dev, log)
 
     t0 = time.time()
+    lr_s = wd_s = None
+    if args.mup:
+        lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
     st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev,
-                   chunk_elems=args.chunk, max_blocks=args.max_blocks)
+                   chunk_elems=args.chunk, max_blocks=args.max_blocks, kind=args.plan,
+                   lr_scale=lr_s, wd_scale=wd_s)
     L = int(st.plan.info.shard_elems)
     master_full = W.make_master(w, seed=0, device=dev)
     st.scatter_to_arena(st.master, master_full)
@@ -233,7 +246,8 @@ def main():
         "config": {"workload": w.name, "params": w.total_params, "shard_elems": L,
                    "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
                    "chunk_elems": int(st.plan.info.chunk_elems),
-                   "n_chunks": int(st.plan.info.n_chunks)},
+                   "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
+                   "mup": bool(args.mup)},
         "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
@@ -251,6 +265,69 @@ def main():
     }
     print(json.dumps(out), flush=True)
     st.close()
+
+
+def bench_pack(args, w, dev, log):
+    """Full-tensor accumulation into the reduce-scatter send buffer (the step
+    before the shard path): every element of the model, K passes, the last
+    dividing by dp_size."""
+    import numpy as np
+    import torch
+
+    from mixed_precision_zero_amd import binding as B
+    from mixed_precision_zero_amd import workloads as W
+    rows = [s[0] for s in w.shapes] if args.plan == "dim0" else None
+    seg = B.z1_pack_layout(w.numel, w.dp_size, args.plan, rows)
+    send = torch.zeros(w.dp_size * seg, dtype=torch.float32, device=dev)
+    grads = []
+    for k in range(w.n_micro):
+        gk = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in w.shapes]
+        W.make_micro_grads(w, 1, k, seed=0, device=dev, out=gk)
+        grads.append(gk)
+    pack = B.z1_pack_create(w.numel, w.dp_size, grads, send, kind=args.plan, rows=rows,
+                            divide=True, chunk_elems=args.chunk)
+    stream = torch.cuda.current_stream()
+    K = w.n_micro
+
+    def one(ev=None):
+        for k in range(K):
+            if ev is not None:
+                ev[k].record(stream)
+            B.z1_pack_accum(pack, k)
+        if ev is not None:
+            ev[K].record(stream)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        one(evs[s])
+    torch.cuda.synchronize()
+    per = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(K)]
+                    for s in range(args.steps)])
+    step_ms = float(per.sum(1).mean())
+    psi = w.total_params
+    first_ms = float(per[:, 0].mean())
+    next_ms = float(per[:, 1:].mean()) if K > 1 else None
+    byts = (6 + 10 * (K - 1)) * psi
+    out = {"metric": "pack params/s (full-tensor fp32 accumulation into the reduce-scatter "
+                     "send buffer, last pass / dp_size)",
+           "value": psi / (step_ms / 1e3), "unit": "params/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32 accumulate of bf16 grads", "data": "synthetic",
+           "config": {"workload": w.name, "params": psi, "dp_size": w.dp_size,
+                      "micro_batches": K, "plan": args.plan, "seg_elems": seg},
+           "kernels_ms": {"pack_first": first_ms, "pack_next": next_ms},
+           "roofline": {"bound": "hbm", "kernel": "k_accum (pack, k>=1)",
+                        "achieved": (10 * psi / (next_ms / 1e3) / 1e9) if next_ms else
+                        (6 * psi / (first_ms / 1e3) / 1e9),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None},
+           "step_hbm_GBps": byts / (step_ms / 1e3) / 1e9}
+    out["roofline"]["frac"] = out["roofline"]["achieved"] / HBM_PEAK_GBPS
+    print(json.dumps(out), flush=True)
+    pack.close()
 
 
 def _cpu_model() -> str:

@@ -320,6 +320,72 @@ typedef struct z1_lr_schedule {
 z1_status z1_lr_at(const z1_lr_schedule *schedule, int64_t step, double *lr);
 
 /* ------------------------------------------------------------------------
+ * z1_grad_norm_sq_acc -- S from an acc arena the caller filled itself.
+ *
+ * For the order in which every micro-batch is first accumulated into full
+ * fp32 gradients and reduced over DP once ("ZeRO-1 风格的 Distributed
+ * Optimizer", §6.7), the reduce-scatter delivers this rank's summed
+ * gradient straight into the plan's acc arena (see z1_pack_*): this call
+ * reads it once, writes the same per-chunk double-double partials as the
+ * last accumulation pass and reduces them to the DEVICE double *d_S.  It
+ * marks the accumulation complete, so z1_adamw_step may follow.
+ * Errors: Z1_EINVAL for NULL; Z1_EALIGN if d_S is not 8-byte aligned.
+ * ------------------------------------------------------------------------ */
+z1_status z1_grad_norm_sq_acc(z1_plan *plan, double *d_S, z1_stream stream);
+
+/* ------------------------------------------------------------------------
+ * The step before the shard path: full-tensor accumulation into the
+ * reduce-scatter send buffer.
+ *
+ * Nanotron adds each micro-batch's gradient into full fp32 gradients and
+ * reduces over DP after the last one ([T6] §6.7); under ZeRO-1 that is a
+ * reduce-scatter ([NG] ZeRO-1 section; [T6] §6.3).  Here the accumulation
+ * itself writes the send buffer: segment r (seg_elems floats at r*seg_elems)
+ * holds rank r's slice of every tensor at rank r's arena offsets
+ * (z1_shard_plan_kind for that rank), so an equal-count reduce-scatter of
+ * `send` leaves each rank its acc arena, ready for z1_grad_norm_sq_acc and
+ * z1_adamw_step.  Padding elements of the segments are never written.
+ * ------------------------------------------------------------------------ */
+typedef struct z1_pack z1_pack;
+
+/* Segment length: the largest arena of any rank, rounded up to a multiple of
+ * 8 elements.  Errors as z1_shard_plan_kind. */
+z1_status z1_pack_layout(int32_t kind, int32_t n_tensors, const int64_t *numel,
+                         const int64_t *rows, int32_t dp_size, int64_t *seg_elems);
+
+typedef struct z1_pack_bind {
+    int32_t n_tensors;
+    int32_t dp_size;
+    int32_t n_micro;        /* K >= 1                                        */
+    int32_t plan_kind;      /* z1_plan_kind                                  */
+    const int64_t *numel;   /* host [n_tensors]                              */
+    const int64_t *rows;    /* host [n_tensors] for Z1_PLAN_DIM0, else NULL  */
+    /* host [n_micro * n_tensors] device pointers to FULL bf16 gradients,
+     * 16-byte aligned; every element is read                               */
+    const void *const *grads;
+    float *send;            /* device, 16-byte aligned, send_elems floats    */
+    int64_t send_elems;     /* >= dp_size * seg_elems                        */
+    int64_t chunk_elems;    /* 0 = default; else multiple of 1024 in
+                               [1024, 1048576]                               */
+    int32_t divide;         /* nonzero: the last pass divides by dp_size in
+                               binary32 ("TorchTitan 生产级预训练方案",
+                               appendix B.1: one division of the fp32
+                               gradients by the world size)                  */
+    int32_t reserved;       /* must be 0                                     */
+} z1_pack_bind;
+
+/* Validates, builds and uploads the chunk table (all ranks' slices); waits
+ * for the upload.  Errors: Z1_EINVAL, Z1_EALIGN, Z1_ENOMEM, Z1_EHIP. */
+z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *bind, z1_stream stream);
+z1_status z1_pack_destroy(z1_pack *pack);
+
+/* Micro-batch k: send = (k == 0 ? 0 : send) + (float)g_k in binary32, in
+ * order; the last pass (k == K-1) divides by dp_size when divide is set.
+ * Order as z1_accum_grads (k == 0 restarts; otherwise k must follow the
+ * previous call), else Z1_ESTATE.  No norm is computed here. */
+z1_status z1_pack_accum(z1_pack *pack, int32_t k, z1_stream stream);
+
+/* ------------------------------------------------------------------------
  * Measurement aid (not part of the step): a streaming copy of n_bytes
  * (a multiple of 16, both pointers 16-byte aligned, non-overlapping) from
  * device src to device dst with 16-byte loads and stores, used to measure

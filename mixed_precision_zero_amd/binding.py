@@ -27,7 +27,9 @@ _NAMES = {0: "Z1_OK", 1: "Z1_EINVAL", 2: "Z1_EALIGN", 3: "Z1_ENOMEM", 4: "Z1_EHI
 
 EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind",
            "z1_plan_create", "z1_plan_destroy", "z1_plan_query", "z1_plan_layout",
-           "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy")
+           "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy",
+           "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
+           "z1_pack_accum")
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
 DECAY_STYLES = {"none": 0, "linear": 1, "cosine": 2}
@@ -58,6 +60,15 @@ class LRSchedule(ctypes.Structure):
     _fields_ = [("lr_max", ctypes.c_double), ("lr_min", ctypes.c_double),
                 ("warmup_steps", ctypes.c_int64), ("decay_steps", ctypes.c_int64),
                 ("decay_style", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class PackBind(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("dp_size", ctypes.c_int32),
+                ("n_micro", ctypes.c_int32), ("plan_kind", ctypes.c_int32),
+                ("numel", ctypes.POINTER(ctypes.c_int64)), ("rows", ctypes.POINTER(ctypes.c_int64)),
+                ("grads", ctypes.POINTER(ctypes.c_void_p)), ("send", ctypes.c_void_p),
+                ("send_elems", ctypes.c_int64), ("chunk_elems", ctypes.c_int64),
+                ("divide", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -95,6 +106,11 @@ def _load():
         "z1_grad_norm_sq": ([P, P, P], ctypes.c_int),
         "z1_adamw_step": ([P, ctypes.POINTER(AdamWHP), P, P], ctypes.c_int),
         "z1_probe_copy": ([P, P, I64, P], ctypes.c_int),
+        "z1_grad_norm_sq_acc": ([P, P, P], ctypes.c_int),
+        "z1_pack_layout": ([I32, I32, PI64, PI64, I32, PI64], ctypes.c_int),
+        "z1_pack_create": ([ctypes.POINTER(P), ctypes.POINTER(PackBind), P], ctypes.c_int),
+        "z1_pack_destroy": ([P], ctypes.c_int),
+        "z1_pack_accum": ([P, I32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -258,6 +274,69 @@ def z1_adamw_step(plan: Plan, *, lr, beta1, beta2, eps, weight_decay, clip, step
     hp = AdamWHP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
     _check(lib.z1_adamw_step(plan.handle, ctypes.byref(hp), _dptr(d_S), _stream(stream)),
            "z1_adamw_step")
+
+
+def z1_grad_norm_sq_acc(plan: Plan, d_S, stream=None) -> None:
+    """S of the acc arena as the caller filled it (e.g. by a reduce-scatter)."""
+    _check(lib.z1_grad_norm_sq_acc(plan.handle, _dptr(d_S), _stream(stream)),
+           "z1_grad_norm_sq_acc")
+
+
+def z1_pack_layout(numel: Sequence[int], dp_size: int, kind: str = "per_tensor",
+                   rows: Optional[Sequence[int]] = None) -> int:
+    """Per-rank segment length of the reduce-scatter send buffer."""
+    n = _i64(numel)
+    r = _i64(rows) if rows is not None else None
+    seg = np.zeros(1, np.int64)
+    _check(lib.z1_pack_layout(PLAN_KINDS[kind], n.size, _p64(n),
+                              _p64(r) if r is not None else None, dp_size, _p64(seg)),
+           "z1_pack_layout")
+    return int(seg[0])
+
+
+class Pack:
+    """Owner of a z1_pack handle."""
+
+    def __init__(self, handle: int, seg: int, keep):
+        self.handle = handle
+        self.seg = seg
+        self._keep = keep
+
+    def close(self):
+        if self.handle:
+            _check(lib.z1_pack_destroy(self.handle), "z1_pack_destroy")
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def z1_pack_create(numel: Sequence[int], dp_size: int, grads: Sequence[Sequence], send,
+                   kind: str = "per_tensor", rows: Optional[Sequence[int]] = None,
+                   divide: bool = False, chunk_elems: int = 0, stream=None) -> Pack:
+    n = _i64(numel)
+    K = len(grads)
+    for gk in grads:
+        if len(gk) != n.size:
+            raise ValueError("grads[k] must list one tensor per parameter")
+    r = _i64(rows) if rows is not None else None
+    gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
+    b = PackBind(n_tensors=n.size, dp_size=dp_size, n_micro=K, plan_kind=PLAN_KINDS[kind],
+                 numel=_p64(n), rows=_p64(r) if r is not None else None,
+                 grads=ctypes.cast(gp, ctypes.POINTER(ctypes.c_void_p)), send=_dptr(send),
+                 send_elems=send.numel() if hasattr(send, "numel") else 0,
+                 chunk_elems=chunk_elems, divide=int(bool(divide)), reserved=0)
+    h = ctypes.c_void_p()
+    _check(lib.z1_pack_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)), "z1_pack_create")
+    seg = z1_pack_layout(n, dp_size, kind, r)
+    return Pack(h.value, seg, (n, r, gp))
+
+
+def z1_pack_accum(pack: Pack, k: int, stream=None) -> None:
+    _check(lib.z1_pack_accum(pack.handle, k, _stream(stream)), "z1_pack_accum")
 
 
 def z1_probe_copy(src, dst, n_bytes: int, stream=None) -> None:

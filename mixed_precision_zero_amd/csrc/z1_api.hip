@@ -37,6 +37,16 @@ struct z1_plan {
     bool norm_done = false;
 };
 
+struct z1_pack {
+    int32_t n = 0, K = 0, dp = 0;
+    int64_t seg = 0, n_chunks = 0;
+    bool divide = false;
+    float *send = nullptr;
+    Chunk *d_chunks = nullptr;
+    const uint16_t **d_grads = nullptr;  // [K][n]
+    int32_t next_k = 0;
+};
+
 namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -82,6 +92,52 @@ z1_status device_alloc(T **out, size_t count)
 }
 
 z1::LaunchGeom geom(const z1_plan *p) { return z1::LaunchGeom{p->d_chunks, p->n_chunks, p->grid}; }
+
+// Appends the pieces of slices [start[i], start[i]+len[i]) of tensors 0..n-1,
+// cut at multiples of `chunk` inside each tensor; element e of slice i lands
+// at dst_base + arena_off[i] + e.
+void append_chunks(std::vector<Chunk> &chunks, int32_t n, const int64_t *start, const int64_t *len,
+                   const int64_t *arena_off, int64_t dst_base, int64_t chunk)
+{
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t s0 = start[i], s1 = start[i] + len[i];
+        int64_t s = s0;
+        while (s < s1) {
+            const int64_t cut = (s / chunk + 1) * chunk;
+            const int64_t e = cut < s1 ? cut : s1;
+            Chunk c;
+            c.src = s;
+            c.dst = dst_base + arena_off[i] + (s - s0);
+            c.tensor = i;
+            c.count = (int32_t)(e - s);
+            c.pad = 0;
+            chunks.push_back(c);
+            s = e;
+        }
+    }
+}
+
+// Issue order: consecutive workgroups alternate between kInterleave distant
+// parts of the table (entry j is piece (j % P) * m + j / P).  Measured on the
+// 7B shard, P = 8 takes the accumulation pass from 1.44 to 1.38 ms; results
+// do not depend on the order (elements are independent, the norm is exactly
+// rounded).
+void interleave_chunks(std::vector<Chunk> &chunks)
+{
+    if (chunks.size() <= (size_t)z1::kInterleave)
+        return;
+    const size_t P = z1::kInterleave, N = chunks.size(), m = (N + P - 1) / P;
+    std::vector<Chunk> re;
+    re.reserve(N);
+    for (size_t i = 0; i < m; ++i)
+        for (size_t j = 0; j < P; ++j)
+            if (j * m + i < N)
+                re.push_back(chunks[j * m + i]);
+    chunks.swap(re);
+}
+
+int64_t chunk_or_default(int64_t c) { return c ? c : z1::kDefaultChunk; }
+bool chunk_ok(int64_t c) { return c >= 1024 && c <= z1::kMaxChunk && c % 1024 == 0; }
 
 }  // namespace
 
@@ -217,8 +273,8 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
         return Z1_EINVAL;
     if (!b->master || !b->exp_avg || !b->exp_avg_sq || !b->acc)
         return Z1_EINVAL;
-    int64_t chunk = b->chunk_elems ? b->chunk_elems : z1::kDefaultChunk;
-    if (chunk < 1024 || chunk > z1::kMaxChunk || chunk % 1024 != 0)
+    const int64_t chunk = chunk_or_default(b->chunk_elems);
+    if (!chunk_ok(chunk))
         return Z1_EINVAL;
 
     z1_plan *p = new (std::nothrow) z1_plan();
@@ -297,38 +353,10 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
 
     // chunk table: pieces cut at multiples of `chunk` inside each tensor
     std::vector<Chunk> chunks;
-    for (int32_t i = 0; i < n; ++i) {
-        const int64_t s0 = p->start[i], s1 = p->start[i] + p->len[i];
+    for (int32_t i = 0; i < n; ++i)
         p->L += p->len[i];
-        int64_t s = s0;
-        while (s < s1) {
-            const int64_t cut = (s / chunk + 1) * chunk;
-            const int64_t e = cut < s1 ? cut : s1;
-            Chunk c;
-            c.src = s;
-            c.dst = p->arena_off[i] + (s - s0);
-            c.tensor = i;
-            c.count = (int32_t)(e - s);
-            c.pad = 0;
-            chunks.push_back(c);
-            s = e;
-        }
-    }
-    // Issue order: consecutive workgroups alternate between kInterleave
-    // distant parts of the shard (chunk j of the table is piece
-    // (j % P) * m + j / P).  Measured on the 7B shard, P = 8 takes the
-    // accumulation pass from 1.44 to 1.38 ms; the result does not depend on
-    // the order (elements are independent, the norm is exactly rounded).
-    if (chunks.size() > (size_t)z1::kInterleave) {
-        const size_t P = z1::kInterleave, N = chunks.size(), m = (N + P - 1) / P;
-        std::vector<Chunk> re;
-        re.reserve(N);
-        for (size_t i = 0; i < m; ++i)
-            for (size_t j = 0; j < P; ++j)
-                if (j * m + i < N)
-                    re.push_back(chunks[j * m + i]);
-        chunks.swap(re);
-    }
+    append_chunks(chunks, n, p->start.data(), p->len.data(), p->arena_off.data(), 0, chunk);
+    interleave_chunks(chunks);
     p->n_chunks = (int64_t)chunks.size();
     if (p->n_chunks > INT32_MAX) {
         delete p;
@@ -489,6 +517,162 @@ z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_glo
     p->acc_complete = false;
     p->norm_done = false;
     return e == hipSuccess ? Z1_OK : Z1_EHIP;
+}
+
+z1_status z1_grad_norm_sq_acc(z1_plan *p, double *d_S, z1_stream stream)
+{
+    if (!p || !d_S)
+        return Z1_EINVAL;
+    if (!aligned(d_S, 8))
+        return Z1_EALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (z1::launch_norm_acc(geom(p), p->acc, p->d_partials, s) != hipSuccess ||
+        z1::launch_norm_fin(p->d_partials, p->n_chunks, p->d_stage, p->d_counter, d_S, s) !=
+            hipSuccess) {
+        p->next_k = 0;
+        p->acc_complete = false;
+        p->norm_done = false;
+        return Z1_EHIP;
+    }
+    p->next_k = 0;
+    p->acc_complete = true;
+    p->norm_done = true;
+    return Z1_OK;
+}
+
+z1_status z1_pack_layout(int32_t kind, int32_t n, const int64_t *numel, const int64_t *rows,
+                         int32_t dp_size, int64_t *seg_elems)
+{
+    if (!seg_elems || n < 0 || dp_size < 1)
+        return Z1_EINVAL;
+    std::vector<int64_t> st(n > 0 ? n : 1), ln(n > 0 ? n : 1), off(n > 0 ? n : 1);
+    int64_t seg = 0;
+    for (int32_t r = 0; r < dp_size; ++r) {
+        int64_t ae = 0;
+        const z1_status e =
+            z1_shard_plan_kind(kind, n, numel, rows, dp_size, r, st.data(), ln.data(), off.data(), &ae);
+        if (e != Z1_OK)
+            return e;
+        if (ae > seg)
+            seg = ae;
+    }
+    *seg_elems = (seg + 7) / 8 * 8;
+    return Z1_OK;
+}
+
+z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
+{
+    if (!out)
+        return Z1_EINVAL;
+    *out = nullptr;
+    if (!b || b->n_tensors < 0 || b->dp_size < 1 || b->n_micro < 1 || b->reserved != 0 ||
+        !b->send)
+        return Z1_EINVAL;
+    const int32_t n = b->n_tensors, K = b->n_micro, D = b->dp_size;
+    if (n > 0 && (!b->numel || !b->grads))
+        return Z1_EINVAL;
+    const int64_t chunk = chunk_or_default(b->chunk_elems);
+    if (!chunk_ok(chunk))
+        return Z1_EINVAL;
+    int64_t seg = 0;
+    z1_status st = z1_pack_layout(b->plan_kind, n, b->numel, b->rows, D, &seg);
+    if (st != Z1_OK)
+        return st;
+    if (seg > 0 && b->send_elems / seg < D)
+        return Z1_EINVAL;
+    if (!aligned(b->send, 16))
+        return Z1_EALIGN;
+    std::vector<const uint16_t *> gptr((size_t)K * n);
+    for (size_t j = 0; j < gptr.size(); ++j) {
+        gptr[j] = static_cast<const uint16_t *>(b->grads[j]);
+        if (b->numel[j % n] == 0)
+            continue;
+        if (!gptr[j])
+            return Z1_EINVAL;
+        if (!aligned(gptr[j], 16))
+            return Z1_EALIGN;
+    }
+    z1_pack *p = new (std::nothrow) z1_pack();
+    if (!p)
+        return Z1_ENOMEM;
+    p->n = n;
+    p->K = K;
+    p->dp = D;
+    p->seg = seg;
+    p->divide = b->divide != 0;
+    p->send = b->send;
+    std::vector<Chunk> chunks;
+    std::vector<int64_t> sv(n > 0 ? n : 1), lv(n > 0 ? n : 1), ov(n > 0 ? n : 1);
+    for (int32_t r = 0; r < D; ++r) {
+        int64_t ae = 0;
+        z1_shard_plan_kind(b->plan_kind, n, b->numel, b->rows, D, r, sv.data(), lv.data(),
+                           ov.data(), &ae);
+        append_chunks(chunks, n, sv.data(), lv.data(), ov.data(), (int64_t)r * seg, chunk);
+    }
+    interleave_chunks(chunks);
+    p->n_chunks = (int64_t)chunks.size();
+    if (p->n_chunks > INT32_MAX) {
+        delete p;
+        return Z1_EINVAL;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void *dc = nullptr, *dg = nullptr;
+    if (hipMalloc(&dc, (chunks.empty() ? 1 : chunks.size()) * sizeof(Chunk)) != hipSuccess ||
+        hipMalloc(&dg, (gptr.empty() ? 1 : gptr.size()) * sizeof(void *)) != hipSuccess) {
+        (void)hipGetLastError();
+        if (dc)
+            (void)hipFree(dc);
+        delete p;
+        return Z1_ENOMEM;
+    }
+    p->d_chunks = static_cast<Chunk *>(dc);
+    p->d_grads = static_cast<const uint16_t **>(dg);
+    hipError_t e = hipSuccess;
+    if (!chunks.empty())
+        e = hipMemcpyAsync(p->d_chunks, chunks.data(), chunks.size() * sizeof(Chunk),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !gptr.empty())
+        e = hipMemcpyAsync(p->d_grads, gptr.data(), gptr.size() * sizeof(void *),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        z1_pack_destroy(p);
+        return Z1_EHIP;
+    }
+    *out = p;
+    return Z1_OK;
+}
+
+z1_status z1_pack_destroy(z1_pack *p)
+{
+    if (!p)
+        return Z1_OK;
+    (void)hipDeviceSynchronize();
+    if (p->d_chunks)
+        (void)hipFree(p->d_chunks);
+    if (p->d_grads)
+        (void)hipFree(p->d_grads);
+    delete p;
+    return Z1_OK;
+}
+
+z1_status z1_pack_accum(z1_pack *p, int32_t k, z1_stream stream)
+{
+    if (!p || k < 0 || k >= p->K)
+        return Z1_EINVAL;
+    if (k != 0 && k != p->next_k)
+        return Z1_ESTATE;
+    const bool last = k == p->K - 1;
+    const z1::LaunchGeom g{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    if (z1::launch_pack(g, p->d_grads + (size_t)k * p->n, p->send, k == 0, last && p->divide,
+                        (float)p->dp, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
+        p->next_k = 0;
+        return Z1_EHIP;
+    }
+    p->next_k = last ? 0 : k + 1;
+    return Z1_OK;
 }
 
 z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream)

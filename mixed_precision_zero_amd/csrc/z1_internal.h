@@ -59,6 +59,11 @@ struct LaunchGeom {
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,
                         DD *partials, bool first, bool last, hipStream_t s);
+// accumulation into the send buffer: no norm; the last pass may divide by dp
+hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *send,
+                       bool first, bool divide, float dp, hipStream_t s);
+// norm partials of an acc arena filled by the caller
+hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials, hipStream_t s);
 hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
                            unsigned int *counter, double *S, hipStream_t s);
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,

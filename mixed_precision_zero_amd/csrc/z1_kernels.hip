@@ -203,13 +203,26 @@ __device__ __forceinline__ f32x4 accum_vec(u32x2 gr, f32x4 ar)
     return s;
 }
 
-// acc = (FIRST ? 0 : acc) + float(g); LAST also sums acc^2 per chunk.
-template <bool FIRST, bool LAST, int U>
+template <bool DIV>
+__device__ __forceinline__ f32x4 divide_vec(f32x4 s, float dp)
+{
+    if (DIV) {
+        s.x = s.x / dp;
+        s.y = s.y / dp;
+        s.z = s.z / dp;
+        s.w = s.w / dp;
+    }
+    return s;
+}
+
+// acc = (FIRST ? 0 : acc) + float(g); LAST also sums acc^2 per chunk; DIV
+// divides the sum by dp (binary32, correctly rounded) before it is stored.
+template <bool FIRST, bool LAST, bool DIV, int U>
 __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chunks,
                                                   int64_t n_chunks,
                                                   const uint16_t *const *__restrict__ gtab,
                                                   float *__restrict__ acc,
-                                                  DD *__restrict__ partials)
+                                                  DD *__restrict__ partials, float dp)
 {
     __shared__ DD lds[kBlock / 64];
     const int t = (int)threadIdx.x;
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const f32x4 s = accum_vec<FIRST, LAST>(gr[u], ar[u]);
+                const f32x4 s = divide_vec<DIV>(accum_vec<FIRST, LAST>(gr[u], ar[u]), dp);
                 st_stream(av + q0 + u * kBlock + t, s);
                 if (LAST) {
                     dd_add_sq(hi, lo, s.x);
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
             const u32x2 gr = ld_stream(gv + q);
             if (!FIRST)
                 ar = ld_stream(av + q);
-            const f32x4 s = accum_vec<FIRST, LAST>(gr, ar);
+            const f32x4 s = divide_vec<DIV>(accum_vec<FIRST, LAST>(gr, ar), dp);
             st_stream(av + q, s);
             if (LAST) {
                 dd_add_sq(hi, lo, s.x);
@@ -262,6 +275,8 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
             float s = __uint_as_float((uint32_t)g[e] << 16);
             if (!FIRST)
                 s = a[e] + s;
+            if (DIV)
+                s = s / dp;
             a[e] = s;
             if (LAST)
                 dd_add_sq(hi, lo, s);
@@ -271,6 +286,51 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
             if (t == 0)
                 partials[c] = DD{hi, lo};
         }
+    }
+}
+
+// ------------------------------------------------- norm of a given acc ----
+// Same per-chunk double-double partials as the last accumulation pass, from
+// an acc arena the caller filled (for example by a reduce-scatter).
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ chunks,
+                                                     int64_t n_chunks,
+                                                     const float *__restrict__ acc,
+                                                     DD *__restrict__ partials)
+{
+    __shared__ DD lds[kBlock / 64];
+    const int t = (int)threadIdx.x;
+    for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const Chunk ch = chunks[c];
+        const Span sp = span_of(ch);
+        const float *a = acc + (ch.dst - sp.lead);
+        const f32x4 *av = reinterpret_cast<const f32x4 *>(a);
+        double hi = 0.0, lo = 0.0;
+        int q0 = sp.qb;
+        for (; q0 + U * kBlock <= sp.qe; q0 += U * kBlock) {
+            f32x4 ar[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                ar[u] = ld_stream(av + q0 + u * kBlock + t);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                dd_add_sq(hi, lo, ar[u].x);
+                dd_add_sq(hi, lo, ar[u].y);
+                dd_add_sq(hi, lo, ar[u].z);
+                dd_add_sq(hi, lo, ar[u].w);
+            }
+        }
+        for (int q = q0 + t; q < sp.qe; q += kBlock) {
+            const f32x4 x = ld_stream(av + q);
+            dd_add_sq(hi, lo, x.x);
+            dd_add_sq(hi, lo, x.y);
+            dd_add_sq(hi, lo, x.z);
+            dd_add_sq(hi, lo, x.w);
+        }
+        for_partial_elems(sp, [&](int e) { dd_add_sq(hi, lo, a[e]); });
+        block_reduce_dd<kBlock>(hi, lo, lds);
+        if (t == 0)
+            partials[c] = DD{hi, lo};
     }
 }
 
@@ -479,18 +539,50 @@ hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, 
     if (geo.n_chunks == 0)
         return hipSuccess;
     const dim3 grid(geo.grid), block(kBlock);
+    constexpr int U = Z1_UNROLL_ACC;
     if (first && last)
-        k_accum<true, true, Z1_UNROLL_ACC><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
-                                                            acc, partials);
+        k_accum<true, true, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                             acc, partials, 1.0f);
     else if (first)
-        k_accum<true, false, Z1_UNROLL_ACC><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
-                                                             acc, partials);
+        k_accum<true, false, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                              acc, partials, 1.0f);
     else if (last)
-        k_accum<false, true, Z1_UNROLL_ACC><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
-                                                             acc, partials);
+        k_accum<false, true, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                              acc, partials, 1.0f);
     else
-        k_accum<false, false, Z1_UNROLL_ACC><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks,
-                                                              grad_tab, acc, partials);
+        k_accum<false, false, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks,
+                                                               grad_tab, acc, partials, 1.0f);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *send,
+                       bool first, bool divide, float dp, hipStream_t s)
+{
+    if (geo.n_chunks == 0)
+        return hipSuccess;
+    const dim3 grid(geo.grid), block(kBlock);
+    constexpr int U = Z1_UNROLL_ACC;
+    if (first && divide)
+        k_accum<true, false, true, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                             send, nullptr, dp);
+    else if (first)
+        k_accum<true, false, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                              send, nullptr, dp);
+    else if (divide)
+        k_accum<false, false, true, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks, grad_tab,
+                                                              send, nullptr, dp);
+    else
+        k_accum<false, false, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks,
+                                                               grad_tab, send, nullptr, dp);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials, hipStream_t s)
+{
+    if (geo.n_chunks == 0)
+        return hipSuccess;
+    k_norm_acc<Z1_UNROLL_ACC><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(geo.chunks, geo.n_chunks,
+                                                                      acc, partials);
     return hipGetLastError();
 }
 

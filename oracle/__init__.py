@@ -19,7 +19,9 @@ Parity status of each function (what pins it, see ``tests/pins.py``):
   norm_sq      closed form for constant input + math.fsum error bound
   clip_coef    torch.nn.utils.clip_grad_norm_ (binary64)
   adamw        step-1 and constant-gradient closed forms, zero-gradient decay,
-               torch.optim.AdamW (binary64)
+               torch.optim.AdamW (binary64), per-group lr / wd
+  lr_at        boundary closed forms, torch CosineAnnealingLR
+  pack_send    numpy.array_split gather per rank; numpy binary32 division
 """
 from __future__ import annotations
 
@@ -107,6 +109,8 @@ class Oracle:
         L.z1o_lr_at.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int64,
                                 ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
         L.z1o_lr_at.restype = ctypes.c_double
+        L.z1o_pack_send.argtypes = [ctypes.c_int32, P, ctypes.c_int32, P, P, P, ctypes.c_int32, P]
+        L.z1o_pack_send.restype = None
         L.z1o_num_threads.argtypes = []
         L.z1o_num_threads.restype = ctypes.c_int
         self.lib = L
@@ -218,6 +222,25 @@ class Oracle:
                                   ctypes.byref(hp), ctypes.byref(c), n_seg, _ptr(sl), _ptr(ls),
                                   _ptr(ws))
         return float(S), float(c.value), acc
+
+    def pack_send(self, numel, rows, kind: str, dp_size: int, acc_full: np.ndarray,
+                  divide: bool) -> np.ndarray:
+        """Reduce-scatter send buffer: every rank's slices of the full fp32
+        accumulated gradient (concatenation order), rank-major, packed."""
+        n = np.ascontiguousarray(np.asarray(numel, np.int64))
+        starts, lens = [], []
+        for r in range(dp_size):
+            s_, l_ = self.plan(kind, n, rows, dp_size, r)
+            starts.append(s_)
+            lens.append(l_)
+        st = np.ascontiguousarray(np.stack(starts)) if dp_size else np.zeros((0, n.size), np.int64)
+        ln = np.ascontiguousarray(np.stack(lens)) if dp_size else np.zeros((0, n.size), np.int64)
+        acc_full = np.ascontiguousarray(acc_full, dtype=np.float32)
+        assert acc_full.size == int(n.sum())
+        out = np.empty(int(ln.sum()), np.float32)
+        self.lib.z1o_pack_send(n.size, _ptr(n), dp_size, _ptr(st), _ptr(ln), _ptr(acc_full),
+                               int(bool(divide)), _ptr(out))
+        return out
 
     def lr_at(self, lr_max, lr_min, warmup, decay, style, t) -> float:
         """Learning rate at step t (style 0 none, 1 linear, 2 cosine decay)."""

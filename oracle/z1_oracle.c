@@ -213,6 +213,38 @@ Z1O_EXPORT double z1o_norm_sq(int64_t L, const float *acc)
 }
 
 /* ------------------------------------------------------------------ */
+/* The step before the shard path: the reduce-scatter send buffer      */
+/* ------------------------------------------------------------------ */
+/* [T6] §6.7: nanotron adds every micro-batch's gradient into the full
+ * .grad tensors and reduces over DP only after the last one; under ZeRO-1
+ * that reduction is a reduce-scatter ([NG] ZeRO-1 section; [T6] §6.3).  Its
+ * send buffer holds, for every rank r in order, rank r's slice of every
+ * tensor (the rank's packed shard order).  acc_full is the in-order fp32 sum
+ * of the full tensors (z1o_accumulate over the concatenation of all
+ * tensors); start/len are [dp_size][n_tensors] slices (any plan kind).  With
+ * divide != 0 every value is divided by dp_size in binary32 ("TorchTitan
+ * 生产级预训练方案", appendix B.1: a single division of the fp32 gradients by
+ * the world size).  out receives sum_r sum_i len[r][i] values. */
+Z1O_EXPORT void z1o_pack_send(int32_t n_tensors, const int64_t *numel, int32_t dp_size,
+                              const int64_t *start, const int64_t *len,
+                              const float *acc_full, int32_t divide, float *out)
+{
+    int64_t o = 0;
+    for (int32_t r = 0; r < dp_size; ++r) {
+        int64_t base = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            const int64_t s0 = start[(int64_t)r * n_tensors + i];
+            const int64_t ln = len[(int64_t)r * n_tensors + i];
+            for (int64_t e = 0; e < ln; ++e) {
+                float x = acc_full[base + s0 + e];
+                out[o++] = divide ? x / (float)dp_size : x;
+            }
+            base += numel[i];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* O2c  clip coefficient                                               */
 /* ------------------------------------------------------------------ */
 /* READING: c = min(1, clip / (sqrt(S) + 1e-6)) as torch's clip_grad_norm_;

@@ -451,6 +451,29 @@ def check_lr_schedule(o):
         assert abs(got - ref) <= 1e-12 * lmax, (k, got, ref)
 
 
+def check_pack_send(o):
+    """The send buffer is, rank after rank, numpy.array_split of every tensor
+    (per-tensor plan); divided values are numpy's binary32 quotient."""
+    rng = np.random.default_rng(13)
+    numel = np.array([17, 0, 1, 64, 1000, 5], np.int64)
+    acc = (rng.standard_normal(int(numel.sum())) * 1e-2).astype(np.float32)
+    tensors = np.split(acc, np.cumsum(numel)[:-1])
+    for D in (1, 2, 3, 7, 8):
+        want = np.concatenate([np.array_split(t, D)[r] for r in range(D) for t in tensors])
+        got = o.pack_send(numel, None, "per_tensor", D, acc, divide=False)
+        assert np.array_equal(got, want), D
+        gotd = o.pack_send(numel, None, "per_tensor", D, acc, divide=True)
+        assert np.array_equal(gotd, want / np.float32(D)), D
+        if D in (1, 2, 8):   # power-of-two divisors are exact
+            assert np.array_equal(gotd * np.float32(D), want)
+    # any plan kind covers every element exactly once
+    rows = np.array([17, 0, 1, 8, 100, 5], np.int64)
+    for kind in ("flat", "dim0"):
+        for D in (3, 8):
+            got = o.pack_send(numel, rows, kind, D, acc, divide=False)
+            assert np.array_equal(np.sort(got), np.sort(acc)), (kind, D)
+
+
 def check_step_vs_torch_tiny(o):
     """The whole composition on the Tiny workload: in-order fp32 sum of the
     bf16 micro-gradients (torch), clip_grad_norm_ + AdamW in binary64."""
@@ -495,4 +518,4 @@ ALL = [check_plan_bruteforce, check_plan_large, check_plan_flat_bruteforce,
        check_accumulate_exact_small, check_norm_constant, check_norm_fsum,
        check_clip_vs_torch, check_adamw_step1_closed_form, check_adamw_constant_gradient,
        check_adamw_zero_gradient, check_adamw_vs_torch, check_adamw_segments_vs_torch,
-       check_lr_schedule, check_step_vs_torch_tiny]
+       check_lr_schedule, check_pack_send, check_step_vs_torch_tiny]

@@ -203,3 +203,40 @@ def test_lr_schedule_errors():
         B.z1_lr_at(-1, lr_max=1.0, lr_min=0.0, warmup_steps=1, decay_steps=1)
     with pytest.raises(B.Z1Error):
         B.z1_lr_at(1, lr_max=1.0, lr_min=0.0, warmup_steps=-1, decay_steps=1)
+
+
+@pytest.mark.parametrize("kind", ["per_tensor", "flat", "dim0"])
+def test_pack_layout_is_largest_rank_arena(kind):
+    for name in ("tiny", "ragged", "llama7b"):
+        w = W.WORKLOADS[name]
+        rows = [s[0] for s in w.shapes]
+        for D in (1, 3, 8):
+            seg = B.z1_pack_layout(w.numel, D, kind, rows if kind == "dim0" else None)
+            arenas = [B.z1_shard_plan(w.numel, D, r, kind=kind,
+                                      rows=rows if kind == "dim0" else None)[3] for r in range(D)]
+            assert seg % 8 == 0 and seg - 8 < max(arenas) <= seg
+
+
+def test_pack_create_rejects_before_device_work():
+    numel = (ctypes.c_int64 * 1)(1024)
+    g = (ctypes.c_void_p * 2)(0x20000, 0x30000)
+    def bind(**over):
+        b = B.PackBind(n_tensors=1, dp_size=2, n_micro=2, plan_kind=0,
+                       numel=ctypes.cast(numel, ctypes.POINTER(ctypes.c_int64)), rows=None,
+                       grads=ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)), send=0x40000,
+                       send_elems=1024, chunk_elems=0, divide=1, reserved=0)
+        for k, v in over.items():
+            setattr(b, k, v)
+        return b
+    h = ctypes.c_void_p(1)
+    for over, status in ((dict(send_elems=1023), B.Z1_EINVAL), (dict(send=0x40004), B.Z1_EALIGN),
+                         (dict(n_micro=0), B.Z1_EINVAL), (dict(reserved=2), B.Z1_EINVAL),
+                         (dict(plan_kind=2), B.Z1_EINVAL), (dict(send=0), B.Z1_EINVAL)):
+        b = bind(**over)
+        assert B.lib.z1_pack_create(ctypes.byref(h), ctypes.byref(b), None) == status, over
+    g[1] = 0x30002
+    b = bind()
+    assert B.lib.z1_pack_create(ctypes.byref(h), ctypes.byref(b), None) == B.Z1_EALIGN
+    assert B.lib.z1_pack_accum(None, 0, None) == B.Z1_EINVAL
+    assert B.lib.z1_pack_destroy(None) == B.Z1_OK
+    assert B.lib.z1_grad_norm_sq_acc(None, None, None) == B.Z1_EINVAL

@@ -14,7 +14,8 @@ import pins
 MUTANTS = {
     "plan_extra_to_rank_eq_rho": [("len[i] = q + (rank < rho ? 1 : 0);",
                                    "len[i] = q + (rank <= rho ? 1 : 0);")],
-    "plan_start_max": [("(rank < rho ? rank : rho)", "(rank < rho ? rho : rank)")],
+    "plan_start_max": [("start[i] = (int64_t)rank * q + (rank < rho ? rank : rho);",
+                        "start[i] = (int64_t)rank * q + (rank < rho ? rho : rank);")],
     "plan_extra_to_last_ranks": [
         ("len[i] = q + (rank < rho ? 1 : 0);",
          "len[i] = q + (dp_size - 1 - rank < rho ? 1 : 0);"),
@@ -36,6 +37,12 @@ MUTANTS = {
                               "return lr_max * (double)(t - 1) / (double)warmup;")],
     "lr_cosine_sign": [("(1.0 + cos(M_PI * tau))", "(1.0 - cos(M_PI * tau))")],
     "lr_linear_wrong_end": [("return lr_max + (lr_min - lr_max) * tau;", "return lr_max - lr_max * tau;")],
+    "pack_divide_by_dp_minus_1": [("out[o++] = divide ? x / (float)dp_size : x;",
+                                   "out[o++] = divide ? x / (float)(dp_size > 1 ? dp_size - 1 : 1) : x;")],
+    "pack_multiply_reciprocal": [("out[o++] = divide ? x / (float)dp_size : x;",
+                                  "out[o++] = divide ? x * (1.0f / (float)dp_size) : x;")],
+    "pack_wrong_base": [("                out[o++] = divide ? x / (float)dp_size : x;\n            }\n            base += numel[i];",
+                         "                out[o++] = divide ? x / (float)dp_size : x;\n            }\n            base += ln;")],
     "rne_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
     "rne_truncate": [("kept += 1u;", "kept += 0u;")],
     "rne_nan_not_quieted": [("| 0x0040u", "| 0x0000u"),
@@ -46,9 +53,9 @@ MUTANTS = {
     "norm_no_square": [("double x = a * a;", "double x = a;")],
     "norm_in_float": [("double t = s + x;", "double t = (float)(s + x);")],
     "norm_uncompensated": [("return s + err;", "return s;")],
-    "clip_no_eps": [("(sqrt(S) + 1e-6)", "(sqrt(S))")],
+    "clip_no_eps": [("double c = clip / (sqrt(S) + 1e-6);", "double c = clip / sqrt(S);")],
     "clip_no_min": [("return c < 1.0 ? c : 1.0;", "return c;")],
-    "clip_uses_S": [("(sqrt(S) + 1e-6)", "(S + 1e-6)")],
+    "clip_uses_S": [("double c = clip / (sqrt(S) + 1e-6);", "double c = clip / (S + 1e-6);")],
     "adamw_decay_without_lr": [("(1.0 - lr * wd)", "(1.0 - wd)")],
     "adamw_decay_after_update": [
         ("pe = pe * (1.0 - lr * wd);", ""),
@@ -74,7 +81,7 @@ MUTANTS = {
 def test_mutant_is_caught(name, tmp_path):
     src = open(oracle.SOURCE).read()
     for old, new in MUTANTS[name]:
-        assert old in src, f"mutation anchor not found: {old!r}"
+        assert src.count(old) == 1, f"mutation anchor must occur exactly once: {old!r}"
         src = src.replace(old, new)
     path = tmp_path / f"{name}.c"
     path.write_text(src)
