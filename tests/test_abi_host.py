@@ -240,3 +240,23 @@ def test_pack_create_rejects_before_device_work():
     assert B.lib.z1_pack_accum(None, 0, None) == B.Z1_EINVAL
     assert B.lib.z1_pack_destroy(None) == B.Z1_OK
     assert B.lib.z1_grad_norm_sq_acc(None, None, None) == B.Z1_EINVAL
+
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=150, deadline=None)
+@given(shapes=st.lists(st.tuples(st.integers(0, 40), st.integers(1, 6)), min_size=0, max_size=12),
+       D=st.integers(1, 12), kind=st.sampled_from(["per_tensor", "flat", "dim0"]))
+def test_plan_kinds_cover_every_element_once(shapes, D, kind):
+    """Across all ranks every element of every tensor is owned exactly once,
+    and every rank's arena layout is valid."""
+    rows = [r for r, _ in shapes]
+    numel = [r * c for r, c in shapes]
+    owned = [np.zeros(n, np.int64) for n in numel]
+    for r in range(D):
+        s, l, off, arena = B.z1_shard_plan(numel, D, r, kind=kind, rows=rows)
+        _check_arena(s, l, off, arena)
+        for i in range(len(numel)):
+            owned[i][s[i]:s[i] + l[i]] += 1
+    assert all((o == 1).all() for o in owned)

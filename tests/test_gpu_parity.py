@@ -4,7 +4,9 @@ Bars (per step): shard plan and fp32 accumulation bit-exact; S within 1e-5
 relative; master, m and v within 1e-6 by max_e |x-y| / max(|y_e|, rms(y));
 bf16 weights within 1 ulp of the oracle's and equal to the RNE cast of the
 GPU's own master; canaries around every arena slice and the bf16 elements
-outside the rank's slices untouched.
+outside the rank's slices untouched.  On top of these tolerances every
+buffer and S must match bit for bit: the kernels evaluate the oracle's IEEE
+operation sequence and both sides round S once (harness.assert_report).
 """
 import dataclasses
 
