@@ -130,7 +130,7 @@ typedef enum z1_plan_kind {
  * z1_shard_plan_kind -- z1_shard_plan for any z1_plan_kind.
  *
  * rows: host [n_tensors] dimension-0 sizes, read only for Z1_PLAN_DIM0
- * (numel[i] must be a multiple of rows[i]; rows[i] == 0 only with
+ * (numel[i] must be a multiple of rows[i]; rows[i] == 0 requires
  * numel[i] == 0); may be NULL otherwise.  Empty slices report start 0.
  * Arena offsets follow the same rule as z1_shard_plan.
  * Errors: as z1_shard_plan, plus Z1_EINVAL for an unknown kind or bad rows.

@@ -177,7 +177,7 @@ z1_status z1_shard_plan_kind(int32_t kind, int32_t n_tensors, const int64_t *num
             return Z1_EINVAL;
         total += numel[i];
         if (kind == Z1_PLAN_DIM0 &&
-            (rows[i] < 0 || (rows[i] == 0) != (numel[i] == 0) ||
+            (rows[i] < 0 || (rows[i] == 0 && numel[i] != 0) ||
              (rows[i] > 0 && numel[i] % rows[i] != 0)))
             return Z1_EINVAL;
     }

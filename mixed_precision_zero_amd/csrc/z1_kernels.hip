@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
         int q0 = sp.qb;
         for (; q0 + U * kBlock <= sp.qe; q0 += U * kBlock) {
             u32x2 gr[U];
-            f32x4 ar[U];
+            f32x4 ar[U] = {};
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 gr[u] = ld_stream(gv + q0 + u * kBlock + t);

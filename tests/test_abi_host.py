@@ -182,7 +182,9 @@ def test_plan_kind_errors():
     with pytest.raises(B.Z1Error):
         B.z1_shard_plan([6, 4], 2, 0, kind="dim0", rows=[4, 2])    # 6 not a multiple of 4
     with pytest.raises(B.Z1Error):
-        B.z1_shard_plan([6, 0], 2, 0, kind="dim0", rows=[3, 2])    # rows without elements
+        B.z1_shard_plan([6, 4], 2, 0, kind="dim0", rows=[3, 0])    # elements without rows
+    s, l, _, _ = B.z1_shard_plan([6, 0], 2, 1, kind="dim0", rows=[3, 5])   # a (5, 0) tensor
+    assert list(l) == [2, 0]
     with pytest.raises(B.Z1Error):
         B.z1_shard_plan([6, 4], 2, 0, kind="dim0")                 # rows missing
 
