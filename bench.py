@@ -184,23 +184,41 @@ def main():
     traffic = traffic_from_profiles(w.name, "adamw")
     h3_bytes = (BYTES_ACC_FIRST + BYTES_ACC_NEXT * (w.n_micro - 1) + BYTES_ADAMW) * L
 
-    # probe copy: the achievable streaming ceiling on this machine
-    copy_gbps = None
+    # ceilings: traffic-only streaming kernels (z1_probe*) on this machine, after the
+    # timed steps (they overwrite the step's buffers)
+    ceilings = None
     if args.copy_gb > 0:
+        def timed_gbps(fn, nbytes, reps=6):
+            for _ in range(2):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
         nbytes = int(args.copy_gb * 1e9) // 16 * 16
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            B.z1_probe_copy(src, dst, nbytes)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        reps = 10
-        for _ in range(reps):
-            B.z1_probe_copy(src, dst, nbytes)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        copy_gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        sink = torch.zeros(4, dtype=torch.float32, device=dev)
+        nv = nbytes // 16
+        ceilings = {
+            "read": timed_gbps(lambda: B.z1_probe("read", [src, sink], nv), nbytes),
+            "write": timed_gbps(lambda: B.z1_probe("write", [dst], nv), nbytes),
+            "copy": timed_gbps(lambda: B.z1_probe_copy(src, dst, nbytes), 2 * nbytes),
+        }
         del src, dst
+        nvL = L // 4
+        half = torch.empty(nvL * 4, dtype=torch.bfloat16, device=dev)
+        ceilings["adamw_traffic"] = timed_gbps(
+            lambda: B.z1_probe("adamw_traffic", [st.acc, st.master, st.exp_avg, st.exp_avg_sq,
+                                                 half], nvL), 30 * 4 * nvL)
+        ceilings["accum_traffic"] = timed_gbps(
+            lambda: B.z1_probe("accum_traffic", [half, st.acc], nvL), 10 * 4 * nvL)
+        del half
+    copy_gbps = ceilings["copy"] if ceilings else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -251,7 +269,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
-                     "launch_ms": adam_avg},
+                     "launch_ms": adam_avg,
+                     "vs_same_traffic_ceiling": (achieved / ceilings["adamw_traffic"])
+                     if ceilings else None},
         "kernels_ms": {"accum_first": acc_first, "accum_next": acc_next,
                        "norm_fin": float(norm_ms.mean()), "adamw": adam_avg,
                        "adamw_median": float(np.median(adam_ms))},
@@ -260,6 +280,7 @@ def main():
         "optimizer_step_params_per_s": L / ((adam_avg + float(norm_ms.mean())) / 1e3),
         "adamw_34B_equivalent_GBps": 34 * L / (adam_avg / 1e3) / 1e9,
         "copy_probe_GBps": copy_gbps,
+        "ceilings_GBps": ceilings,
         "wall_s": wall,
         "cpu_baseline": cpu,
     }

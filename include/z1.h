@@ -394,6 +394,30 @@ z1_status z1_pack_accum(z1_pack *pack, int32_t k, z1_stream stream);
  * ------------------------------------------------------------------------ */
 z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the step): streaming kernels with a step
+ * kernel's traffic and no arithmetic, for the bandwidth this machine reaches
+ * with each traffic mix.  n_vec counts 16-byte vectors per fp32 stream;
+ * half-width (bf16) streams hold n_vec 8-byte vectors.  Every buffer is
+ * device memory, 16-byte aligned, large enough for its stream.
+ *   Z1_PROBE_READ           bufs[0] read (n_vec x 16 B); bufs[1] >= 4 bytes
+ *                           (never written in practice)
+ *   Z1_PROBE_WRITE          bufs[0] written
+ *   Z1_PROBE_ADAMW_TRAFFIC  read bufs[0..3] (acc, p, m, v), write bufs[1..3]
+ *                           and the half-width bufs[4]: 30 B per element
+ *   Z1_PROBE_ACCUM_TRAFFIC  read the half-width bufs[0] and bufs[1], write
+ *                           bufs[1]: 10 B per element
+ * The contents written are meaningless.  Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
+ * ------------------------------------------------------------------------ */
+enum {
+    Z1_PROBE_READ = 0,
+    Z1_PROBE_WRITE = 1,
+    Z1_PROBE_ADAMW_TRAFFIC = 2,
+    Z1_PROBE_ACCUM_TRAFFIC = 3
+};
+z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, int64_t n_vec,
+                   z1_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

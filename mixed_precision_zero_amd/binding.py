@@ -29,7 +29,9 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_plan_create", "z1_plan_destroy", "z1_plan_query", "z1_plan_layout",
            "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy",
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
-           "z1_pack_accum")
+           "z1_pack_accum", "z1_probe")
+
+PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
 DECAY_STYLES = {"none": 0, "linear": 1, "cosine": 2}
@@ -111,6 +113,7 @@ def _load():
         "z1_pack_create": ([ctypes.POINTER(P), ctypes.POINTER(PackBind), P], ctypes.c_int),
         "z1_pack_destroy": ([P], ctypes.c_int),
         "z1_pack_accum": ([P, I32, P], ctypes.c_int),
+        "z1_probe": ([I32, ctypes.POINTER(P), I32, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -337,6 +340,12 @@ def z1_pack_create(numel: Sequence[int], dp_size: int, grads: Sequence[Sequence]
 
 def z1_pack_accum(pack: Pack, k: int, stream=None) -> None:
     _check(lib.z1_pack_accum(pack.handle, k, _stream(stream)), "z1_pack_accum")
+
+
+def z1_probe(kind: str, bufs: Sequence, n_vec: int, stream=None) -> None:
+    """Traffic-only streaming kernel (see z1.h); bufs are tensors or addresses."""
+    arr = (ctypes.c_void_p * max(len(bufs), 1))(*[_dptr(b) for b in bufs])
+    _check(lib.z1_probe(PROBES[kind], arr, len(bufs), int(n_vec), _stream(stream)), "z1_probe")
 
 
 def z1_probe_copy(src, dst, n_bytes: int, stream=None) -> None:

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libz1.so")
-SOURCES = [os.path.join(CSRC, "z1_api.hip"), os.path.join(CSRC, "z1_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "z1_api.hip"), os.path.join(CSRC, "z1_kernels.hip"),
+           os.path.join(CSRC, "z1_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

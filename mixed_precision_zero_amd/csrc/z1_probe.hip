@@ -1,0 +1,158 @@
+// z1_probe.hip -- measurement aids (not part of the step): streaming kernels
+// with the traffic of the step's kernels and no arithmetic, so a benchmark can
+// report the HBM bandwidth this machine reaches for each traffic mix next to
+// what the step's kernels reach.  Same shape as the step's kernels: 256-thread
+// workgroups, 4 x 16-byte vectors per lane, non-temporal loads and stores,
+// one 1024-vector tile per workgroup.
+#include "z1.h"
+#include "z1_internal.h"
+
+namespace z1 {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kTileVec = 4 * kBlock;
+
+template <typename T>
+__device__ __forceinline__ T ld(const T *p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st(T *p, T x) { __builtin_nontemporal_store(x, p); }
+
+// Reads every vector; the sum feeds a store that only happens for an
+// impossible value, so the loads stay live.
+__global__ __launch_bounds__(kBlock) void k_probe_read(const f32x4 *__restrict__ src, int64_t n,
+                                                       float *__restrict__ sink)
+{
+    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            const f32x4 x = ld(src + i);
+            acc += x.x + x.y + x.z + x.w;
+        }
+    }
+    if (acc == -1234.5f)
+        sink[0] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void k_probe_write(f32x4 *__restrict__ dst, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    const f32x4 z = {1.f, 2.f, 3.f, 4.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n)
+            st(dst + i, z);
+    }
+}
+
+// k_adamw's traffic: read a, p, m, v; write p, m, v and a half-width w.
+__global__ __launch_bounds__(kBlock) void k_probe_adamw(const f32x4 *__restrict__ a,
+                                                        f32x4 *__restrict__ p,
+                                                        f32x4 *__restrict__ m,
+                                                        f32x4 *__restrict__ v,
+                                                        u32x2 *__restrict__ w, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    f32x4 ar[4], pr[4], mr[4], vr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            ar[u] = ld(a + i);
+            pr[u] = ld(p + i);
+            mr[u] = ld(m + i);
+            vr[u] = ld(v + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            st(p + i, pr[u] + ar[u]);
+            st(m + i, mr[u] + ar[u]);
+            st(v + i, vr[u] + ar[u]);
+            u32x2 wb;
+            wb.x = __float_as_uint(pr[u].x);
+            wb.y = __float_as_uint(pr[u].y);
+            st(w + i, wb);
+        }
+    }
+}
+
+// k_accum's traffic (k >= 1): read a half-width g and acc, write acc.
+__global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict__ g,
+                                                        f32x4 *__restrict__ acc, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    u32x2 gr[4];
+    f32x4 ar[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            gr[u] = ld(g + i);
+            ar[u] = ld(acc + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            f32x4 s = ar[u];
+            s.x += __uint_as_float(gr[u].x << 16);
+            s.y += __uint_as_float(gr[u].y << 16);
+            st(acc + i, s);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace z1
+
+extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, int64_t n_vec,
+                              z1_stream stream)
+{
+    using namespace z1;
+    static const int32_t need[] = {2, 1, 5, 2};
+    if (kind < Z1_PROBE_READ || kind > Z1_PROBE_ACCUM_TRAFFIC || !bufs || n_vec < 0 ||
+        n_bufs < need[kind])
+        return Z1_EINVAL;
+    for (int32_t i = 0; i < need[kind]; ++i) {
+        if (!bufs[i])
+            return Z1_EINVAL;
+        if (reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0)
+            return Z1_EALIGN;
+    }
+    if (n_vec == 0)
+        return Z1_OK;
+    const int64_t blocks = (n_vec + kTileVec - 1) / kTileVec;
+    if (blocks > INT32_MAX)
+        return Z1_EINVAL;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(kBlock);
+    switch (kind) {
+    case Z1_PROBE_READ:
+        k_probe_read<<<grid, block, 0, s>>>(static_cast<const f32x4 *>(bufs[0]), n_vec,
+                                            static_cast<float *>(bufs[1]));
+        break;
+    case Z1_PROBE_WRITE:
+        k_probe_write<<<grid, block, 0, s>>>(static_cast<f32x4 *>(bufs[0]), n_vec);
+        break;
+    case Z1_PROBE_ADAMW_TRAFFIC:
+        k_probe_adamw<<<grid, block, 0, s>>>(
+            static_cast<const f32x4 *>(bufs[0]), static_cast<f32x4 *>(bufs[1]),
+            static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
+            static_cast<u32x2 *>(bufs[4]), n_vec);
+        break;
+    default:
+        k_probe_accum<<<grid, block, 0, s>>>(static_cast<const u32x2 *>(bufs[0]),
+                                             static_cast<f32x4 *>(bufs[1]), n_vec);
+        break;
+    }
+    return hipGetLastError() == hipSuccess ? Z1_OK : Z1_EHIP;
+}

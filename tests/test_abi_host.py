@@ -146,6 +146,15 @@ def test_null_plan_calls():
     assert L.z1_probe_copy(None, None, 16, None) == B.Z1_EINVAL
     assert L.z1_probe_copy(0x1000, 0x2000, 15, None) == B.Z1_EINVAL
     assert L.z1_probe_copy(0x1008, 0x2000, 16, None) == B.Z1_EALIGN
+    bufs = (ctypes.c_void_p * 5)(0x1000, 0x2000, 0x3000, 0x4000, 0x5000)
+    assert L.z1_probe(7, bufs, 5, 16, None) == B.Z1_EINVAL        # unknown kind
+    assert L.z1_probe(-1, bufs, 5, 16, None) == B.Z1_EINVAL
+    assert L.z1_probe(2, bufs, 4, 16, None) == B.Z1_EINVAL        # adamw traffic needs 5
+    assert L.z1_probe(0, bufs, 2, -1, None) == B.Z1_EINVAL
+    assert L.z1_probe(0, None, 2, 16, None) == B.Z1_EINVAL
+    odd = (ctypes.c_void_p * 2)(0x1008, 0x2000)
+    assert L.z1_probe(0, odd, 2, 16, None) == B.Z1_EALIGN
+    assert L.z1_probe(1, bufs, 1, 0, None) == B.Z1_OK              # nothing to do
 
 
 @pytest.mark.parametrize("kind", ["flat", "dim0"])

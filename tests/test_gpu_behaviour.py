@@ -160,3 +160,20 @@ def test_probe_copy():
     B.z1_probe_copy(src, dst, n)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_traffic_probes_run():
+    """The measurement kernels run on odd sizes (tails) and leave the
+    buffers they should not touch alone."""
+    n = 1024 * 7 + 13
+    bufs = [torch.ones(n * 4, device="cuda") for _ in range(4)]
+    half = torch.zeros(n * 4, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(4, device="cuda")
+    B.z1_probe("read", [bufs[0], sink], n)
+    B.z1_probe("write", [bufs[1]], n)
+    B.z1_probe("adamw_traffic", [bufs[0], bufs[1], bufs[2], bufs[3], half], n)
+    B.z1_probe("accum_traffic", [half, bufs[2]], n)
+    torch.cuda.synchronize()
+    assert float(sink.sum()) == 0.0 and bool((bufs[0] == 1).all())
+    with pytest.raises(B.Z1Error):
+        B.z1_probe("adamw_traffic", [bufs[0]], n)
