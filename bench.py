@@ -1,12 +1,18 @@
 #!/usr/bin/env python3
 """Throughput of the ZeRO-1 shard optimizer step on one MI355X.
 
-One step = the whole path over one batch of synthetic input: K accumulation
-passes (z1_accum_grads), the norm (z1_grad_norm_sq) and the clipped AdamW
-with the bf16 cast (z1_adamw_step), all through the C ABI.  The default
-workload is the 7B Llama-shaped list at dp_size 8, rank 3 (842,301,952 shard
-elements, K = 4).  Inputs are generated on the device before timing and stay
-resident in HBM; every timed step does all of the work.
+One step = the whole path over one batch of synthetic input: the fp32
+accumulation of the K micro-batch gradients, the norm (z1_grad_norm_sq) and
+the clipped AdamW with the bf16 cast (z1_adamw_step), all through the C ABI.
+The default workload is the 7B Llama-shaped list at dp_size 8, rank 3
+(842,301,952 shard elements, K = 4).  Inputs are generated on the device
+before timing and stay resident in HBM; every timed step does all of the work.
+
+The K gradients are resident, so by default one z1_accum_grads_range(0, K)
+call reads all of them in one pass (12 bytes per element for K = 4); the
+same step with one z1_accum_grads call per micro-batch (36 bytes per element)
+is timed after it and reported under accum_variants.  Both store the same
+bits.  --accum slot makes the per-micro-batch form the headline.
 
 Prints ONE JSON line (rank 0).  Besides the driver's fields it carries
   roofline      the dominant kernel (AdamW) against the 8 TB/s HBM peak, with
@@ -30,8 +36,23 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, vendor figure
 BYTES_ADAMW = 30                 # read acc, p, m, v (16); write p, m, v (12) + bf16 (2)
 BYTES_ACC_FIRST = 6              # read bf16 g (2); write acc (4)
 BYTES_ACC_NEXT = 10              # read bf16 g (2) + acc (4); write acc (4)
+MAX_SLOTS = 8                    # micro-batch slots per multi-slot pass
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "z1_kernels.hip")
+
+
+def accum_bytes(K: int, resident: bool) -> int:
+    """Algorithmic bytes per shard element of the K accumulation passes."""
+    if not resident:
+        return BYTES_ACC_FIRST + BYTES_ACC_NEXT * (K - 1)
+    total, k = 0, 0
+    while k < K:   # the library's split: passes of at most 8 slots, as even as possible
+        left = K - k
+        passes = (left + MAX_SLOTS - 1) // MAX_SLOTS
+        g = (left + passes - 1) // passes
+        total += 2 * g + (4 if k == 0 else 8)
+        k += g
+    return total
 
 
 def parse():
@@ -49,6 +70,11 @@ def parse():
                     help="shard plan kind")
     ap.add_argument("--mup", action="store_true",
                     help="per-tensor muP lr multipliers and no decay on norms")
+    ap.add_argument("--accum", default="resident", choices=["resident", "slot"],
+                    help="resident (default): the K resident micro-batch gradients in one "
+                         "z1_accum_grads_range call (up to 8 slots per pass); slot: one "
+                         "z1_accum_grads call per micro-batch; the other form is timed too "
+                         "and reported beside")
     ap.add_argument("--mode", default="step", choices=["step", "pack"],
                     help="step: the shard step (default); pack: full-tensor accumulation into "
                          "the reduce-scatter send buffer, every element of the model")
@@ -131,58 +157,77 @@ def main():
     hp = w.hp()
     stream = torch.cuda.current_stream()
 
-    def one_step(t, ev=None):
-        for k in range(w.n_micro):
-            if ev is not None:
-                ev[k].record(stream)
-            st.accumulate(k)
+    def one_step(t, resident, ev=None):
+        # events: before the accumulation, after it, after the norm, after AdamW
         if ev is not None:
-            ev[w.n_micro].record(stream)
+            ev[0].record(stream)
+        if resident:
+            st.accumulate_range(0, w.n_micro)
+        else:
+            for k in range(w.n_micro):
+                st.accumulate(k)
+        if ev is not None:
+            ev[1].record(stream)
         st.norm()
         if ev is not None:
-            ev[w.n_micro + 1].record(stream)
+            ev[2].record(stream)
         st.adamw(hp, step=t)
         if ev is not None:
-            ev[w.n_micro + 2].record(stream)
+            ev[3].record(stream)
 
-    for t in range(1, args.warmup + 1):
-        one_step(t)
-    torch.cuda.synchronize()
+    def timed(resident, warmup, steps, t0):
+        for t in range(t0, t0 + warmup):
+            one_step(t, resident)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for s_ in range(steps):
+            one_step(t0 + warmup + s_, resident, evs[s_])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - wall0
+        span = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs])  # noqa: E731
+        return {"ms_step": start.elapsed_time(stop) / steps, "wall": wall_,
+                "accum": span(0, 1), "norm": span(1, 2), "adamw": span(2, 3),
+                "step": span(0, 3), "t_next": t0 + warmup + steps}
 
-    n_ev = w.n_micro + 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for s in range(args.steps):
-        one_step(args.warmup + 1 + s, evs[s])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-
-    acc_ms = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(w.n_micro)]
-                       for s in range(args.steps)])
-    norm_ms = np.array([evs[s][w.n_micro].elapsed_time(evs[s][w.n_micro + 1])
-                        for s in range(args.steps)])
-    adam_ms = np.array([evs[s][w.n_micro + 1].elapsed_time(evs[s][w.n_micro + 2])
-                        for s in range(args.steps)])
+    head_resident = args.accum == "resident"
+    r = timed(head_resident, args.warmup, args.steps, 1)
+    alt_steps = min(args.steps, 10)
+    alt = timed(not head_resident, min(args.warmup, 3), alt_steps, r["t_next"]) \
+        if alt_steps > 0 else None
+    ms_step, wall = r["ms_step"], r["wall"]
+    norm_ms, adam_ms = r["norm"], r["adamw"]
     adam_avg = float(adam_ms.mean())
-    step_ms = [evs[s][0].elapsed_time(evs[s][n_ev - 1]) for s in range(args.steps)]
-    log("[bench] per-step ms: " + " ".join(f"{x:.3f}" for x in step_ms))
+    log("[bench] per-step ms: " + " ".join(f"{x:.3f}" for x in r["step"]))
     log(f"[bench] k_adamw ms: mean {adam_avg:.4f} median {float(np.median(adam_ms)):.4f} "
         f"min {float(adam_ms.min()):.4f} max {float(adam_ms.max()):.4f}")
-    acc_first = float(acc_ms[:, 0].mean())
-    acc_next = float(acc_ms[:, 1:].mean()) if w.n_micro > 1 else None
+    accum_ms = float(r["accum"].mean())
+
+    def variant(x, resident):
+        b = (accum_bytes(w.n_micro, resident) + BYTES_ADAMW) * L
+        return {"calls": "one z1_accum_grads_range(0, K)" if resident
+                else "one z1_accum_grads per micro-batch",
+                "steps": len(x["step"]), "ms_per_step": x["ms_step"],
+                "params_per_s": L / (x["ms_step"] / 1e3),
+                "accum_ms": float(x["accum"].mean()), "adamw_ms": float(x["adamw"].mean()),
+                "bytes_per_param": b // L if L else None,
+                "step_hbm_GBps": b / (x["ms_step"] / 1e3) / 1e9,
+                "accum_hbm_GBps": accum_bytes(w.n_micro, resident) * L /
+                (float(x["accum"].mean()) / 1e3) / 1e9}
+    variants = {("resident" if head_resident else "slot"): variant(r, head_resident)}
+    if alt is not None:
+        variants["slot" if head_resident else "resident"] = variant(alt, not head_resident)
 
     value = L / (ms_step / 1e3)
     adam_bytes = BYTES_ADAMW * L
     achieved = adam_bytes / (adam_avg / 1e3) / 1e9
     traffic = traffic_from_profiles(w.name, "adamw")
-    h3_bytes = (BYTES_ACC_FIRST + BYTES_ACC_NEXT * (w.n_micro - 1) + BYTES_ADAMW) * L
+    h3_bytes = (accum_bytes(w.n_micro, head_resident) + BYTES_ADAMW) * L
 
     # ceilings: traffic-only streaming kernels (z1_probe*) on this machine, after the
     # timed steps (they overwrite the step's buffers)
@@ -265,16 +310,16 @@ def main():
                    "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
                    "chunk_elems": int(st.plan.info.chunk_elems),
                    "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
-                   "mup": bool(args.mup)},
+                   "mup": bool(args.mup), "accum": args.accum},
         "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
                      "launch_ms": adam_avg,
                      "vs_same_traffic_ceiling": (achieved / ceilings["adamw_traffic"])
                      if ceilings else None},
-        "kernels_ms": {"accum_first": acc_first, "accum_next": acc_next,
-                       "norm_fin": float(norm_ms.mean()), "adamw": adam_avg,
-                       "adamw_median": float(np.median(adam_ms))},
+        "kernels_ms": {"accum_all_K": accum_ms, "norm_fin": float(norm_ms.mean()),
+                       "adamw": adam_avg, "adamw_median": float(np.median(adam_ms))},
+        "accum_variants": variants,
         "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
         "step_bytes_per_param": h3_bytes // L if L else None,
         "optimizer_step_params_per_s": L / ((adam_avg + float(norm_ms.mean())) / 1e3),
@@ -310,7 +355,16 @@ def bench_pack(args, w, dev, log):
     stream = torch.cuda.current_stream()
     K = w.n_micro
 
+    resident = args.accum == "resident"
+
     def one(ev=None):
+        if resident:
+            if ev is not None:
+                ev[0].record(stream)
+            B.z1_pack_accum_range(pack, 0, K)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         for k in range(K):
             if ev is not None:
                 ev[k].record(stream)
@@ -321,17 +375,27 @@ def bench_pack(args, w, dev, log):
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in range(args.steps)]
+    n_ev = 2 if resident else K + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+           for _ in range(args.steps)]
     for s in range(args.steps):
         one(evs[s])
     torch.cuda.synchronize()
-    per = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(K)]
+    per = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(n_ev - 1)]
                     for s in range(args.steps)])
     step_ms = float(per.sum(1).mean())
     psi = w.total_params
-    first_ms = float(per[:, 0].mean())
-    next_ms = float(per[:, 1:].mean()) if K > 1 else None
-    byts = (6 + 10 * (K - 1)) * psi
+    byts = accum_bytes(K, resident) * psi
+    if resident:
+        kernels = {"pack_all_K": step_ms}
+        kname, achieved = "k_accum_slots (pack)", byts / (step_ms / 1e3) / 1e9
+    else:
+        first_ms = float(per[:, 0].mean())
+        next_ms = float(per[:, 1:].mean()) if K > 1 else None
+        kernels = {"pack_first": first_ms, "pack_next": next_ms}
+        kname = "k_accum (pack, k>=1)"
+        achieved = (10 * psi / (next_ms / 1e3) / 1e9) if next_ms else \
+            (6 * psi / (first_ms / 1e3) / 1e9)
     out = {"metric": "pack params/s (full-tensor fp32 accumulation into the reduce-scatter "
                      "send buffer, last pass / dp_size)",
            "value": psi / (step_ms / 1e3), "unit": "params/s", "n_gpus": 1,
@@ -339,12 +403,12 @@ def bench_pack(args, w, dev, log):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32 accumulate of bf16 grads", "data": "synthetic",
            "config": {"workload": w.name, "params": psi, "dp_size": w.dp_size,
-                      "micro_batches": K, "plan": args.plan, "seg_elems": seg},
-           "kernels_ms": {"pack_first": first_ms, "pack_next": next_ms},
-           "roofline": {"bound": "hbm", "kernel": "k_accum (pack, k>=1)",
-                        "achieved": (10 * psi / (next_ms / 1e3) / 1e9) if next_ms else
-                        (6 * psi / (first_ms / 1e3) / 1e9),
+                      "micro_batches": K, "plan": args.plan, "seg_elems": seg,
+                      "accum": args.accum},
+           "kernels_ms": kernels,
+           "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "traffic": None},
+           "bytes_per_param": byts // psi,
            "step_hbm_GBps": byts / (step_ms / 1e3) / 1e9}
     out["roofline"]["frac"] = out["roofline"]["achieved"] / HBM_PEAK_GBPS
     print(json.dumps(out), flush=True)

@@ -33,7 +33,8 @@
  *     frees or reallocates caller memory.
  *   - The library owns only what z1_plan_create allocates (the chunk table,
  *     pointer tables and norm partials) and frees it in z1_plan_destroy.
- *     z1_accum_grads, z1_grad_norm_sq and z1_adamw_step allocate nothing.
+ *     z1_accum_grads(_range), z1_grad_norm_sq and z1_adamw_step allocate
+ *     nothing.
  *   - Work is enqueued on the given stream and the calls return without
  *     waiting for it; none of the step calls synchronises with the host.
  *     A kernel fault surfaces at the caller's next synchronisation.
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 2
+#define Z1_ABI_VERSION 3
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -240,6 +241,28 @@ z1_status z1_plan_layout(const z1_plan *plan, int64_t *start, int64_t *len,
 z1_status z1_accum_grads(z1_plan *plan, int32_t k, z1_stream stream);
 
 /* ------------------------------------------------------------------------
+ * z1_accum_grads_range -- micro-batches k_begin .. k_end-1 in one call.
+ *
+ * Stores exactly what z1_accum_grads(plan, k) for k = k_begin, ..., k_end-1
+ * stores, in that order, bit for bit: the same binary32 additions in the
+ * same order ("Distributed Training", §2: the gradients of the K micro-batches
+ * are summed, one optimizer step after them).  It is for callers that hold
+ * several micro-batch gradients in device memory at once (K full-size bf16
+ * gradient sets, 2 bytes per parameter each): up to 8 slots are read in one
+ * pass, so the fp32 acc arena is read and written once per 8 slots instead of
+ * once per slot.  For K = 4 that is 12 bytes per shard element instead of 36.
+ * A range that ends at K also writes the norm partials, as the k == K-1 pass
+ * of z1_accum_grads does.  A range may follow single-slot calls and be
+ * followed by them.
+ *
+ * Order: k_begin must be 0 or one more than the last micro-batch already
+ * accumulated in this step, else Z1_ESTATE.  Z1_EINVAL for a NULL plan or
+ * unless 0 <= k_begin < k_end <= K.
+ * ------------------------------------------------------------------------ */
+z1_status z1_accum_grads_range(z1_plan *plan, int32_t k_begin, int32_t k_end,
+                               z1_stream stream);
+
+/* ------------------------------------------------------------------------
  * z1_grad_norm_sq -- S = sum over the shard of acc^2.
  *
  * Writes S, the exact sum rounded to binary64 (double-double partials per
@@ -384,6 +407,12 @@ z1_status z1_pack_destroy(z1_pack *pack);
  * Order as z1_accum_grads (k == 0 restarts; otherwise k must follow the
  * previous call), else Z1_ESTATE.  No norm is computed here. */
 z1_status z1_pack_accum(z1_pack *pack, int32_t k, z1_stream stream);
+
+/* Micro-batches k_begin .. k_end-1 in one call: bit for bit what
+ * z1_pack_accum(pack, k) for each k in order stores, reading up to 8 slots
+ * per pass (see z1_accum_grads_range).  Order and errors as
+ * z1_accum_grads_range. */
+z1_status z1_pack_accum_range(z1_pack *pack, int32_t k_begin, int32_t k_end, z1_stream stream);
 
 /* ------------------------------------------------------------------------
  * Measurement aid (not part of the step): a streaming copy of n_bytes

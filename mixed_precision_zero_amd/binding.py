@@ -29,7 +29,7 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_plan_create", "z1_plan_destroy", "z1_plan_query", "z1_plan_layout",
            "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy",
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
-           "z1_pack_accum", "z1_probe")
+           "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range")
 
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
@@ -105,6 +105,7 @@ def _load():
         "z1_plan_query": ([P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
         "z1_plan_layout": ([P, PI64, PI64, PI64], ctypes.c_int),
         "z1_accum_grads": ([P, I32, P], ctypes.c_int),
+        "z1_accum_grads_range": ([P, I32, I32, P], ctypes.c_int),
         "z1_grad_norm_sq": ([P, P, P], ctypes.c_int),
         "z1_adamw_step": ([P, ctypes.POINTER(AdamWHP), P, P], ctypes.c_int),
         "z1_probe_copy": ([P, P, I64, P], ctypes.c_int),
@@ -113,6 +114,7 @@ def _load():
         "z1_pack_create": ([ctypes.POINTER(P), ctypes.POINTER(PackBind), P], ctypes.c_int),
         "z1_pack_destroy": ([P], ctypes.c_int),
         "z1_pack_accum": ([P, I32, P], ctypes.c_int),
+        "z1_pack_accum_range": ([P, I32, I32, P], ctypes.c_int),
         "z1_probe": ([I32, ctypes.POINTER(P), I32, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -267,6 +269,11 @@ def z1_accum_grads(plan: Plan, k: int, stream=None) -> None:
     _check(lib.z1_accum_grads(plan.handle, k, _stream(stream)), "z1_accum_grads")
 
 
+def z1_accum_grads_range(plan: Plan, k_begin: int, k_end: int, stream=None) -> None:
+    _check(lib.z1_accum_grads_range(plan.handle, k_begin, k_end, _stream(stream)),
+           "z1_accum_grads_range")
+
+
 def z1_grad_norm_sq(plan: Plan, d_S, stream=None) -> None:
     """Writes S into the device float64 tensor d_S (first element)."""
     _check(lib.z1_grad_norm_sq(plan.handle, _dptr(d_S), _stream(stream)), "z1_grad_norm_sq")
@@ -340,6 +347,11 @@ def z1_pack_create(numel: Sequence[int], dp_size: int, grads: Sequence[Sequence]
 
 def z1_pack_accum(pack: Pack, k: int, stream=None) -> None:
     _check(lib.z1_pack_accum(pack.handle, k, _stream(stream)), "z1_pack_accum")
+
+
+def z1_pack_accum_range(pack: Pack, k_begin: int, k_end: int, stream=None) -> None:
+    _check(lib.z1_pack_accum_range(pack.handle, k_begin, k_end, _stream(stream)),
+           "z1_pack_accum_range")
 
 
 def z1_probe(kind: str, bufs: Sequence, n_vec: int, stream=None) -> None:

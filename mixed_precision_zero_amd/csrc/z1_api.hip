@@ -465,6 +465,38 @@ z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
     return Z1_OK;
 }
 
+z1_status z1_accum_grads_range(z1_plan *p, int32_t k_begin, int32_t k_end, z1_stream stream)
+{
+    if (!p || k_begin < 0 || k_end > p->K || k_begin >= k_end)
+        return Z1_EINVAL;
+    if (k_begin != 0 && k_begin != p->next_k)
+        return Z1_ESTATE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t k = k_begin; k < k_end;) {
+        // passes of at most kMaxSlots slots, as even as possible
+        const int32_t left = k_end - k;
+        const int32_t passes = (left + z1::kMaxSlots - 1) / z1::kMaxSlots;
+        const int32_t g = (left + passes - 1) / passes;
+        const bool first = k == 0, last = k + g == p->K;
+        const uint16_t *const *tab = p->d_grads + (size_t)k * p->n;
+        const hipError_t e =
+            g == 1 ? z1::launch_accum(geom(p), tab, p->acc, p->d_partials, first, last, s)
+                   : z1::launch_accum_slots(geom(p), tab, p->n, g, p->acc, p->d_partials, first,
+                                            last, false, 1.0f, s);
+        if (e != hipSuccess) {
+            p->next_k = 0;
+            p->acc_complete = false;
+            p->norm_done = false;
+            return Z1_EHIP;
+        }
+        k += g;
+    }
+    p->next_k = k_end;
+    p->acc_complete = k_end == p->K;
+    p->norm_done = false;
+    return Z1_OK;
+}
+
 z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
 {
     if (!p || !d_S)
@@ -672,6 +704,34 @@ z1_status z1_pack_accum(z1_pack *p, int32_t k, z1_stream stream)
         return Z1_EHIP;
     }
     p->next_k = last ? 0 : k + 1;
+    return Z1_OK;
+}
+
+z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_stream stream)
+{
+    if (!p || k_begin < 0 || k_end > p->K || k_begin >= k_end)
+        return Z1_EINVAL;
+    if (k_begin != 0 && k_begin != p->next_k)
+        return Z1_ESTATE;
+    const z1::LaunchGeom geo{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t k = k_begin; k < k_end;) {
+        const int32_t left = k_end - k;
+        const int32_t passes = (left + z1::kMaxSlots - 1) / z1::kMaxSlots;
+        const int32_t g = (left + passes - 1) / passes;
+        const bool first = k == 0, divide = p->divide && k + g == p->K;
+        const uint16_t *const *tab = p->d_grads + (size_t)k * p->n;
+        const hipError_t e =
+            g == 1 ? z1::launch_pack(geo, tab, p->send, first, divide, (float)p->dp, s)
+                   : z1::launch_accum_slots(geo, tab, p->n, g, p->send, nullptr, first, false,
+                                            divide, (float)p->dp, s);
+        if (e != hipSuccess) {
+            p->next_k = 0;
+            return Z1_EHIP;
+        }
+        k += g;
+    }
+    p->next_k = k_end == p->K ? 0 : k_end;
     return Z1_OK;
 }
 

@@ -15,6 +15,7 @@ constexpr int kVec = 4;
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxChunk = 1 << 20;
 constexpr int kInterleave = 8;  // chunk issue order: 8 interleaved regions
+constexpr int kMaxSlots = 8;     // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
 
@@ -62,6 +63,12 @@ hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, 
 // accumulation into the send buffer: no norm; the last pass may divide by dp
 hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *send,
                        bool first, bool divide, float dp, hipStream_t s);
+// slots 0..n_slots-1 of grad_tab (slot j's pointers at grad_tab + j * slot_stride)
+// in one pass, 2 <= n_slots <= kMaxSlots; first overwrites, last writes the
+// norm partials, divide divides the final sum by dp
+hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad_tab,
+                              int32_t slot_stride, int n_slots, float *acc, DD *partials,
+                              bool first, bool last, bool divide, float dp, hipStream_t s);
 // norm partials of an acc arena filled by the caller
 hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials, hipStream_t s);
 hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,

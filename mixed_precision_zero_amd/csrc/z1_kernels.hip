@@ -292,6 +292,103 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
 // ------------------------------------------------- norm of a given acc ----
 // Same per-chunk double-double partials as the last accumulation pass, from
 // an acc arena the caller filled (for example by a reduce-scatter).
+// G micro-batch slots in one pass: acc = (FIRST ? 0 : acc) + g_0 + ... +
+// g_{G-1}, every addition rounded to binary32 in slot order, which is the
+// value G single-slot passes store (each of them rounds the same sum to
+// binary32).  The acc arena is read and written once per pass instead of once
+// per slot.  LAST and DIV as in k_accum.
+template <bool FIRST, bool LAST, bool DIV, int G, int U>
+__global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict__ chunks,
+                                                        int64_t n_chunks,
+                                                        const uint16_t *const *__restrict__ gtab,
+                                                        int32_t slot_stride,
+                                                        float *__restrict__ acc,
+                                                        DD *__restrict__ partials, float dp)
+{
+    __shared__ DD lds[kBlock / 64];
+    const int t = (int)threadIdx.x;
+    for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const Chunk ch = chunks[c];
+        const Span sp = span_of(ch);
+        const uint16_t *g[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            g[j] = gtab[(int64_t)j * slot_stride + ch.tensor] + (ch.src - sp.lead);
+        float *a = acc + (ch.dst - sp.lead);
+        f32x4 *av = reinterpret_cast<f32x4 *>(a);
+        double hi = 0.0, lo = 0.0;
+
+        int q0 = sp.qb;
+        for (; q0 + U * kBlock <= sp.qe; q0 += U * kBlock) {
+            u32x2 gr[G][U];
+            f32x4 ar[U] = {};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = q0 + u * kBlock + t;
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    gr[j][u] = ld_stream(reinterpret_cast<const u32x2 *>(g[j]) + q);
+                if (!FIRST)
+                    ar[u] = ld_stream(av + q);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                f32x4 s = accum_vec<FIRST, false>(gr[0][u], ar[u]);
+#pragma unroll
+                for (int j = 1; j < G; ++j)
+                    s = accum_vec<false, false>(gr[j][u], s);
+                s = divide_vec<DIV>(s, dp);
+                st_stream(av + q0 + u * kBlock + t, s);
+                if (LAST) {
+                    dd_add_sq(hi, lo, s.x);
+                    dd_add_sq(hi, lo, s.y);
+                    dd_add_sq(hi, lo, s.z);
+                    dd_add_sq(hi, lo, s.w);
+                }
+            }
+        }
+        for (int q = q0 + t; q < sp.qe; q += kBlock) {
+            u32x2 gr[G];
+            f32x4 ar = {};
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                gr[j] = ld_stream(reinterpret_cast<const u32x2 *>(g[j]) + q);
+            if (!FIRST)
+                ar = ld_stream(av + q);
+            f32x4 s = accum_vec<FIRST, false>(gr[0], ar);
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                s = accum_vec<false, false>(gr[j], s);
+            s = divide_vec<DIV>(s, dp);
+            st_stream(av + q, s);
+            if (LAST) {
+                dd_add_sq(hi, lo, s.x);
+                dd_add_sq(hi, lo, s.y);
+                dd_add_sq(hi, lo, s.z);
+                dd_add_sq(hi, lo, s.w);
+            }
+        }
+        for_partial_elems(sp, [&](int e) {
+            float s = __uint_as_float((uint32_t)g[0][e] << 16);
+            if (!FIRST)
+                s = a[e] + s;
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                s = s + __uint_as_float((uint32_t)g[j][e] << 16);
+            if (DIV)
+                s = s / dp;
+            a[e] = s;
+            if (LAST)
+                dd_add_sq(hi, lo, s);
+        });
+        if (LAST) {
+            block_reduce_dd<kBlock>(hi, lo, lds);
+            if (t == 0)
+                partials[c] = DD{hi, lo};
+        }
+    }
+}
+
 template <int U>
 __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ chunks,
                                                      int64_t n_chunks,
@@ -555,6 +652,34 @@ hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, 
     return hipGetLastError();
 }
 
+template <int G>
+void launch_slots_g(const LaunchGeom &geo, const uint16_t *const *grad_tab, int32_t stride,
+                    float *acc, DD *partials, bool first, bool last, bool divide, float dp,
+                    hipStream_t s)
+{
+    const dim3 grid(geo.grid), block(kBlock);
+    constexpr int U = Z1_UNROLL_ACC;
+    // the norm (last) and the division (divide) are never asked for together
+    if (first && last)
+        k_accum_slots<true, true, false, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+    else if (last)
+        k_accum_slots<false, true, false, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+    else if (first && divide)
+        k_accum_slots<true, false, true, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+    else if (divide)
+        k_accum_slots<false, false, true, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+    else if (first)
+        k_accum_slots<true, false, false, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+    else
+        k_accum_slots<false, false, false, G, U><<<grid, block, 0, s>>>(
+            geo.chunks, geo.n_chunks, grad_tab, stride, acc, partials, dp);
+}
+
 hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *send,
                        bool first, bool divide, float dp, hipStream_t s)
 {
@@ -574,6 +699,28 @@ hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, f
     else
         k_accum<false, false, false, U><<<grid, block, 0, s>>>(geo.chunks, geo.n_chunks,
                                                                grad_tab, send, nullptr, dp);
+    return hipGetLastError();
+}
+
+hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad_tab,
+                              int32_t slot_stride, int n_slots, float *acc, DD *partials,
+                              bool first, bool last, bool divide, float dp, hipStream_t s)
+{
+    if (geo.n_chunks == 0)
+        return hipSuccess;
+    if (last && divide)
+        return hipErrorInvalidValue;
+    static_assert(kMaxSlots == 8, "one case per slot count 2..kMaxSlots");
+    switch (n_slots) {
+    case 2: launch_slots_g<2>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 3: launch_slots_g<3>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 4: launch_slots_g<4>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 5: launch_slots_g<5>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 6: launch_slots_g<6>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 7: launch_slots_g<7>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 8: launch_slots_g<8>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -76,6 +76,9 @@ class ShardStep:
     def accumulate(self, k: int, stream=None) -> None:
         B.z1_accum_grads(self.plan, k, stream)
 
+    def accumulate_range(self, k_begin: int, k_end: int, stream=None) -> None:
+        B.z1_accum_grads_range(self.plan, k_begin, k_end, stream)
+
     def norm(self, stream=None) -> None:
         B.z1_grad_norm_sq(self.plan, self.d_S, stream)
 
@@ -84,9 +87,16 @@ class ShardStep:
         B.z1_adamw_step(self.plan, d_S=self.d_S, step=t, stream=stream, **hp)
         self.t = t
 
-    def step(self, hp: dict, stream=None) -> None:
-        for k in range(self.n_micro):
-            self.accumulate(k, stream)
+    def step(self, hp: dict, stream=None, ranges=None) -> None:
+        """One optimizer step.  ranges=None accumulates one micro-batch per
+        call; otherwise a list of (k_begin, k_end) covering 0..K in order, one
+        z1_accum_grads_range call each."""
+        if ranges is None:
+            for k in range(self.n_micro):
+                self.accumulate(k, stream)
+        else:
+            for a, b in ranges:
+                self.accumulate_range(a, b, stream)
         self.norm(stream)
         self.adamw(hp, stream=stream)
 

@@ -1,6 +1,6 @@
 /*
- * z1_c_abi_test.c -- drives libz1 from plain C (no Python, no torch): one
- * tiny optimizer step through the C ABI, compared bit for bit with the CPU
+ * z1_c_abi_test.c -- drives libz1 from plain C (no Python, no torch): two
+ * tiny optimizer steps through the C ABI, compared bit for bit with the CPU
  * oracle (test infrastructure, linked only here).  Exit status 0 = pass.
  */
 #include <hip/hip_runtime_api.h>
@@ -133,43 +133,54 @@ int main(void)
     b.arena_elems = arena;
     z1_plan *plan = NULL;
     CHECK_Z1(z1_plan_create(&plan, &b, NULL));
-    z1_adamw_hp hp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1};
-    for (int k = 0; k < K; ++k)
-        CHECK_Z1(z1_accum_grads(plan, k, NULL));
-    CHECK_Z1(z1_grad_norm_sq(plan, d_S, NULL));
-    CHECK_Z1(z1_adamw_step(plan, &hp, d_S, NULL));
-    CHECK_HIP(hipDeviceSynchronize());
-
-    z1o_hp ohp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1};
-    double c = 0.0;
-    double S = z1o_step(L, K, hg, hacc, hp_, hm, hv, hw, &ohp, &c);
-    double S_gpu = 0.0;
-    CHECK_HIP(hipMemcpy(&S_gpu, d_S, 8, hipMemcpyDeviceToHost));
-    int bad = S_gpu != S;
+    /* step 1: one accumulation call per micro-batch; step 2: all K resident
+     * slots in one z1_accum_grads_range call.  Both must match the oracle. */
+    int bad = 0;
+    double S = 0.0, S_gpu = 0.0, c = 0.0;
     float *back = malloc(arena * 4);
-    const float *refs[3] = {hp_, hm, hv};
-    float *devs[3] = {d_master, d_m, d_v};
-    for (int a = 0; a < 3; ++a) {
-        CHECK_HIP(hipMemcpy(back, devs[a], arena * 4, hipMemcpyDeviceToHost));
+    for (int t = 1; t <= 2; ++t) {
+        z1_adamw_hp hp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
+        if (t == 1) {
+            for (int k = 0; k < K; ++k)
+                CHECK_Z1(z1_accum_grads(plan, k, NULL));
+        } else {
+            CHECK_Z1(z1_accum_grads_range(plan, 0, K, NULL));
+        }
+        CHECK_Z1(z1_grad_norm_sq(plan, d_S, NULL));
+        CHECK_Z1(z1_adamw_step(plan, &hp, d_S, NULL));
+        CHECK_HIP(hipDeviceSynchronize());
+
+        z1o_hp ohp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
+        S = z1o_step(L, K, hg, hacc, hp_, hm, hv, hw, &ohp, &c);
+        CHECK_HIP(hipMemcpy(&S_gpu, d_S, 8, hipMemcpyDeviceToHost));
+        bad += S_gpu != S;
+        const float *refs[4] = {hp_, hm, hv, hacc};
+        float *devs[4] = {d_master, d_m, d_v, d_acc};
+        for (int a = 0; a < 4; ++a) {
+            CHECK_HIP(hipMemcpy(back, devs[a], arena * 4, hipMemcpyDeviceToHost));
+            pos = 0;
+            for (int i = 0; i < NT; ++i) {
+                bad += memcmp(back + off[i], refs[a] + pos, len[i] * 4) != 0;
+                pos += len[i];
+            }
+        }
         pos = 0;
         for (int i = 0; i < NT; ++i) {
-            bad += memcmp(back + off[i], refs[a] + pos, len[i] * 4) != 0;
+            uint16_t *full = malloc(numel[i] * 2 + 2);
+            CHECK_HIP(hipMemcpy(full, w[i], numel[i] * 2, hipMemcpyDeviceToHost));
+            bad += memcmp(full + start[i], hw + pos, len[i] * 2) != 0;
+            for (int64_t e = 0; e < numel[i]; ++e)
+                if ((e < start[i] || e >= start[i] + len[i]) && full[e] != 0)
+                    ++bad; /* outside the slice: untouched */
             pos += len[i];
+            free(full);
         }
+        printf("C ABI step %d (%s): L=%lld S=%.17g (oracle %.17g) c=%.6g\n", t,
+               t == 1 ? "z1_accum_grads per micro-batch" : "z1_accum_grads_range", (long long)L,
+               S_gpu, S, c);
     }
-    pos = 0;
-    for (int i = 0; i < NT; ++i) {
-        uint16_t *full = malloc(numel[i] * 2 + 2);
-        CHECK_HIP(hipMemcpy(full, w[i], numel[i] * 2, hipMemcpyDeviceToHost));
-        bad += memcmp(full + start[i], hw + pos, len[i] * 2) != 0;
-        for (int64_t e = 0; e < numel[i]; ++e)
-            if ((e < start[i] || e >= start[i] + len[i]) && full[e] != 0)
-                ++bad; /* outside the slice: untouched */
-        pos += len[i];
-        free(full);
-    }
+    free(back);
     CHECK_Z1(z1_plan_destroy(plan));
-    printf("C ABI step: L=%lld S=%.17g (oracle %.17g) c=%.6g -> %s\n", (long long)L, S_gpu, S, c,
-           bad ? "MISMATCH" : "bit-exact");
+    printf("C ABI: %s\n", bad ? "MISMATCH" : "bit-exact");
     return bad ? 1 : 0;
 }

@@ -67,8 +67,10 @@ class Parity:
     """Runs a workload on the GPU and the oracle side by side."""
 
     def __init__(self, w: W.Workload, device="cuda", chunk_elems=0, max_blocks=0,
-                 seed=0, canaries=True, kind="per_tensor", lr_scale=None, wd_scale=None):
+                 seed=0, canaries=True, kind="per_tensor", lr_scale=None, wd_scale=None,
+                 ranges=None):
         self.w = w
+        self.ranges = ranges     # None: one accumulation call per micro-batch
         self.dev = torch.device(device)
         self.o = oracle.get()
         self.seed = seed
@@ -141,7 +143,7 @@ class Parity:
             W.make_micro_grads(w, t, k, seed=self.seed, device=self.dev, out=st.grads[k])
             g[k] = self._packed_host_bf16(st.grads[k])
         t1 = time.time()
-        st.step(w.hp())
+        st.step(w.hp(), ranges=self.ranges)
         torch.cuda.synchronize()
         t2 = time.time()
         S, c, _ = self.o.step(g, self.p, self.m, self.v, step=t, acc=self.acc, w=self.wbits,

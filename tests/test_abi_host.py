@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 2
+    assert B.z1_abi_version() == 3
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -138,6 +138,8 @@ def test_null_plan_calls():
     L = B.lib
     assert L.z1_plan_create(None, None, None) == B.Z1_EINVAL
     assert L.z1_accum_grads(None, 0, None) == B.Z1_EINVAL
+    assert L.z1_accum_grads_range(None, 0, 1, None) == B.Z1_EINVAL
+    assert L.z1_pack_accum_range(None, 0, 1, None) == B.Z1_EINVAL
     assert L.z1_grad_norm_sq(None, None, None) == B.Z1_EINVAL
     hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
     assert L.z1_adamw_step(None, ctypes.byref(hp), None, None) == B.Z1_EINVAL

@@ -1,5 +1,7 @@
 """The C ABI driven from plain C (tests/c/z1_c_abi_test.c, built by
-__graft_entry__.build()): one step, bit-exact against the oracle."""
+__graft_entry__.build()): two steps, one with an accumulation call per
+micro-batch and one with all slots in one z1_accum_grads_range call, each
+bit-exact against the oracle."""
 import os
 import subprocess
 
