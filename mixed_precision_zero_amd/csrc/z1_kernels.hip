@@ -41,6 +41,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef Z1_UNROLL_ACC
 #define Z1_UNROLL_ACC 4
 #endif
+// Multi-slot passes keep G x U gradient vectors per lane in flight; above 6
+// slots U = 2 (7B shard, 8 slots: 5.1 -> 5.95 TB/s; at 6 slots U = 4 and 2
+// are within 1%).
+#ifndef Z1_UNROLL_SLOTS_WIDE
+#define Z1_UNROLL_SLOTS_WIDE 2
+#endif
 #ifndef Z1_UNROLL_ADAM
 #define Z1_UNROLL_ADAM 4
 #endif
@@ -658,7 +664,7 @@ void launch_slots_g(const LaunchGeom &geo, const uint16_t *const *grad_tab, int3
                     hipStream_t s)
 {
     const dim3 grid(geo.grid), block(kBlock);
-    constexpr int U = Z1_UNROLL_ACC;
+    constexpr int U = G <= 6 ? Z1_UNROLL_ACC : Z1_UNROLL_SLOTS_WIDE;
     // the norm (last) and the division (divide) are never asked for together
     if (first && last)
         k_accum_slots<true, true, false, G, U><<<grid, block, 0, s>>>(

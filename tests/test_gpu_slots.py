@@ -49,6 +49,13 @@ def test_tiny_eleven_slots_two_passes_small_chunks():
     _run(w, 2, [(0, 11)], chunk_elems=1024, max_blocks=3)
 
 
+def test_tiny_fifteen_slots_wide_passes():
+    """K = 15: passes of 8 and 7 slots (the two-vectors-per-lane form), on
+    1024-element chunks so every workgroup loops and takes partial vectors."""
+    w = dataclasses.replace(W.TINY, name="tiny_k15", n_micro=15, shapes=((257, 63), (61,), (1030,)))
+    _run(w, 2, [(0, 15)], chunk_elems=1024)
+
+
 def test_ragged_small_three_slots():
     shapes = W.ragged_shapes(300, 12, seed=3)
     w = dataclasses.replace(W.RAGGED, name="ragged_small", shapes=shapes, n_micro=3,
