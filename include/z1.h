@@ -39,7 +39,8 @@
  *     waiting for it; none of the step calls synchronises with the host.
  *     A kernel fault surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before anything is enqueued: a
- *     call that returns an error has enqueued no work.
+ *     call that returns Z1_EINVAL, Z1_EALIGN or Z1_ESTATE has enqueued no
+ *     work.  Z1_EHIP means a launch failed (see each call).
  *   - A plan is used from one host thread and one stream at a time.
  *   - No C++ exception crosses this interface.
  */
@@ -257,7 +258,9 @@ z1_status z1_accum_grads(z1_plan *plan, int32_t k, z1_stream stream);
  *
  * Order: k_begin must be 0 or one more than the last micro-batch already
  * accumulated in this step, else Z1_ESTATE.  Z1_EINVAL for a NULL plan or
- * unless 0 <= k_begin < k_end <= K.
+ * unless 0 <= k_begin < k_end <= K (nothing enqueued).  Z1_EHIP if a launch
+ * fails; the passes before it may already be enqueued, and the plan then
+ * expects the step to restart at k = 0.
  * ------------------------------------------------------------------------ */
 z1_status z1_accum_grads_range(z1_plan *plan, int32_t k_begin, int32_t k_end,
                                z1_stream stream);
@@ -446,6 +449,21 @@ enum {
 };
 z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, int64_t n_vec,
                    z1_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the step): Z1_PROBE_PLAN_ADAMW runs the AdamW
+ * kernel's chunk walk over the plan's own buffers -- the same loads of acc,
+ * master, exp_avg and exp_avg_sq and the same stores of master, exp_avg,
+ * exp_avg_sq and the bf16 weight slices -- with the update replaced by an
+ * add.  Its duration next to z1_adamw_step's, in the same process, is the
+ * cost of the arithmetic on exactly the step's memory.  It OVERWRITES the
+ * master, exp_avg, exp_avg_sq arenas and the weight slices with meaningless
+ * values; call it only on buffers whose contents are no longer needed.
+ * Call order is not checked and not changed.
+ * Errors: Z1_EINVAL (NULL plan, unknown kind), Z1_EHIP.
+ * ------------------------------------------------------------------------ */
+enum { Z1_PROBE_PLAN_ADAMW = 0 };
+z1_status z1_probe_plan(z1_plan *plan, int32_t kind, z1_stream stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,8 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_plan_create", "z1_plan_destroy", "z1_plan_query", "z1_plan_layout",
            "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy",
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
-           "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range")
+           "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range",
+           "z1_probe_plan")
 
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
@@ -116,6 +117,7 @@ def _load():
         "z1_pack_accum": ([P, I32, P], ctypes.c_int),
         "z1_pack_accum_range": ([P, I32, I32, P], ctypes.c_int),
         "z1_probe": ([I32, ctypes.POINTER(P), I32, I64, P], ctypes.c_int),
+        "z1_probe_plan": ([P, I32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -352,6 +354,11 @@ def z1_pack_accum(pack: Pack, k: int, stream=None) -> None:
 def z1_pack_accum_range(pack: Pack, k_begin: int, k_end: int, stream=None) -> None:
     _check(lib.z1_pack_accum_range(pack.handle, k_begin, k_end, _stream(stream)),
            "z1_pack_accum_range")
+
+
+def z1_probe_plan(plan: Plan, kind: str = "adamw", stream=None) -> None:
+    """Overwrites the plan's master / m / v arenas and weight slices."""
+    _check(lib.z1_probe_plan(plan.handle, {"adamw": 0}[kind], _stream(stream)), "z1_probe_plan")
 
 
 def z1_probe(kind: str, bufs: Sequence, n_vec: int, stream=None) -> None:

@@ -735,6 +735,17 @@ z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_str
     return Z1_OK;
 }
 
+z1_status z1_probe_plan(z1_plan *p, int32_t kind, z1_stream stream)
+{
+    if (!p || kind != Z1_PROBE_PLAN_ADAMW)
+        return Z1_EINVAL;
+    if (z1::launch_adamw_traffic(geom(p), p->d_weights, p->acc, p->master, p->exp_avg,
+                                 p->exp_avg_sq, reinterpret_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return Z1_EHIP;
+    return Z1_OK;
+}
+
 z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream)
 {
     if (!src || !dst || n_bytes < 0 || n_bytes % 16 != 0)

@@ -76,6 +76,10 @@ hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                         const float *acc, float *master, float *m, float *v,
                         const AdamConsts &k, const double *S, hipStream_t s);
+// k_adamw's loads and stores over the same plan with no arithmetic (measurement)
+hipError_t launch_adamw_traffic(const LaunchGeom &geo, uint16_t *const *weight_tab,
+                                const float *acc, float *master, float *m, float *v,
+                                hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
 
 }  // namespace z1

@@ -535,7 +535,21 @@ __device__ __forceinline__ void adamw_vec(f32x4 a, f32x4 &p, f32x4 &m, f32x4 &v,
     w.y = bf16_rne(p.z) | (bf16_rne(p.w) << 16);
 }
 
-template <int U>
+// Element-wise traffic stand-in for adamw_vec (measurement only): the same
+// inputs and outputs, an add instead of the update, a truncating cast.
+__device__ __forceinline__ void traffic_vec(f32x4 a, f32x4 &p, f32x4 &m, f32x4 &v, u32x2 &w)
+{
+    p = p + a;
+    m = m + a;
+    v = v + a;
+    w.x = (__float_as_uint(p.x) >> 16) | (__float_as_uint(p.y) & 0xFFFF0000u);
+    w.y = (__float_as_uint(p.z) >> 16) | (__float_as_uint(p.w) & 0xFFFF0000u);
+}
+
+// MATH = false is a measurement twin: the same chunk walk, loads and stores
+// over the same buffers, with the arithmetic replaced by traffic_vec, so the
+// cost of the update itself can be read off on the step's own buffers.
+template <int U, bool MATH>
 __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chunks,
                                                   int64_t n_chunks,
                                                   uint16_t *const *__restrict__ wtab,
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
                                                   const double *__restrict__ S)
 {
     double c = 1.0;
-    if (k.clip > 0.0) {
+    if (MATH && k.clip > 0.0) {
         const double cc = k.clip / (sqrt(S[0]) + 1e-6);
         c = cc < 1.0 ? cc : 1.0;
     }
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
     for (int64_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
         const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
-        const TensorRate tr = tensor_rate(k, scales[ch.tensor]);
+        const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
         uint16_t *w = wtab[ch.tensor] + (ch.src - sp.lead);
         const int64_t off = ch.dst - sp.lead;
         const float *a = acc + off;
@@ -584,7 +598,10 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
             for (int u = 0; u < U; ++u) {
                 const int q = q0 + u * kBlock + t;
                 u32x2 wb;
-                adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
+                if constexpr (MATH)
+                    adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
+                else
+                    traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
                 st_stream(pv + q, pr[u]);
                 st_stream(mv + q, mr[u]);
                 st_stream(vv + q, vr[u]);
@@ -594,18 +611,29 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
         for (int q = q0 + t; q < sp.qe; q += kBlock) {
             f32x4 pr = ld_stream(pv + q), mr = ld_stream(mv + q), vr = ld_stream(vv + q);
             u32x2 wb;
-            adamw_vec(ld_stream(av + q), pr, mr, vr, wb, k, tr, c);
+            if constexpr (MATH)
+                adamw_vec(ld_stream(av + q), pr, mr, vr, wb, k, tr, c);
+            else
+                traffic_vec(ld_stream(av + q), pr, mr, vr, wb);
             st_stream(pv + q, pr);
             st_stream(mv + q, mr);
             st_stream(vv + q, vr);
             st_stream(wv + q, wb);
         }
         for_partial_elems(sp, [&](int e) {
-            const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
-            p[e] = r.p;
-            m[e] = r.m;
-            v[e] = r.v;
-            w[e] = (uint16_t)bf16_rne(r.p);
+            if constexpr (MATH) {
+                const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
+                p[e] = r.p;
+                m[e] = r.m;
+                v[e] = r.v;
+                w[e] = (uint16_t)bf16_rne(r.p);
+            } else {
+                const float x = p[e] + a[e];
+                p[e] = x;
+                m[e] = m[e] + a[e];
+                v[e] = v[e] + a[e];
+                w[e] = (uint16_t)(__float_as_uint(x) >> 16);
+            }
         });
     }
 }
@@ -759,9 +787,19 @@ hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, cons
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
-    k_adamw<Z1_UNROLL_ADAM><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(geo.chunks, geo.n_chunks,
-                                                             weight_tab, scales, acc, master, m, v,
-                                                             k, S);
+    k_adamw<Z1_UNROLL_ADAM, true><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
+        geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, k, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw_traffic(const LaunchGeom &geo, uint16_t *const *weight_tab,
+                                const float *acc, float *master, float *m, float *v,
+                                hipStream_t s)
+{
+    if (geo.n_chunks == 0)
+        return hipSuccess;
+    k_adamw<Z1_UNROLL_ADAM, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
+        geo.chunks, geo.n_chunks, weight_tab, nullptr, acc, master, m, v, AdamConsts{}, nullptr);
     return hipGetLastError();
 }
 

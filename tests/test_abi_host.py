@@ -140,6 +140,7 @@ def test_null_plan_calls():
     assert L.z1_accum_grads(None, 0, None) == B.Z1_EINVAL
     assert L.z1_accum_grads_range(None, 0, 1, None) == B.Z1_EINVAL
     assert L.z1_pack_accum_range(None, 0, 1, None) == B.Z1_EINVAL
+    assert L.z1_probe_plan(None, 0, None) == B.Z1_EINVAL
     assert L.z1_grad_norm_sq(None, None, None) == B.Z1_EINVAL
     hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
     assert L.z1_adamw_step(None, ctypes.byref(hp), None, None) == B.Z1_EINVAL

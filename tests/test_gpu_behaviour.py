@@ -177,3 +177,39 @@ def test_traffic_probes_run():
     assert float(sink.sum()) == 0.0 and bool((bufs[0] == 1).all())
     with pytest.raises(B.Z1Error):
         B.z1_probe("adamw_traffic", [bufs[0]], n)
+
+
+def test_plan_probe_covers_exactly_the_slices():
+    """z1_probe_plan walks the AdamW kernel's chunks over the plan's buffers:
+    every slice element gets p + acc (an exact fp32 add here), nothing outside
+    the slices is touched."""
+    w = dataclasses.replace(W.TINY, shapes=((7, 33), (5,), (3, 1000), (1,)), dp_size=3, rank=1)
+    st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device="cuda", arena_pad=64)
+    try:
+        canary = float.fromhex("0x1.5a5a5ap+77")
+        for a in (st.master, st.exp_avg, st.exp_avg_sq, st.acc):
+            a.fill_(canary)
+        used = torch.zeros(st.master.numel(), dtype=torch.bool, device="cuda")
+        for _, _, ln, off in st.slices():
+            used[off:off + ln] = True
+        n = int(used.sum())
+        st.master[used] = torch.arange(n, device="cuda", dtype=torch.float32)
+        st.acc[used] = 0.5
+        for a in (st.exp_avg, st.exp_avg_sq):
+            a[used] = 1.0
+        for wt in st.weights:
+            wt.fill_(3.0)
+        B.z1_probe_plan(st.plan)
+        torch.cuda.synchronize()
+        assert torch.equal(st.master[used], torch.arange(n, device="cuda", dtype=torch.float32) + 0.5)
+        assert bool((st.exp_avg[used] == 1.5).all()) and bool((st.exp_avg_sq[used] == 1.5).all())
+        for a in (st.master, st.exp_avg, st.exp_avg_sq, st.acc):
+            assert bool((a[~used] == canary).all())
+        for i, s, ln, _ in st.slices():
+            flat = st.weights[i].reshape(-1)
+            assert bool((flat[:s] == 3.0).all()) and bool((flat[s + ln:] == 3.0).all())
+            if ln:
+                assert not bool((flat[s:s + ln] == 3.0).any())
+        assert B.lib.z1_probe_plan(st.plan.handle, 1, None) == B.Z1_EINVAL   # unknown kind
+    finally:
+        st.close()
