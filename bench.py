@@ -75,6 +75,9 @@ def parse():
                          "z1_accum_grads_range call (up to 8 slots per pass); slot: one "
                          "z1_accum_grads call per micro-batch; the other form is timed too "
                          "and reported beside")
+    ap.add_argument("--layout", default="full", choices=["full", "packed"],
+                    help="bf16 weights and gradients as full-size tensors (default) or as "
+                         "packed shards in arena order")
     ap.add_argument("--mode", default="step", choices=["step", "pack"],
                     help="step: the shard step (default); pack: full-tensor accumulation into "
                          "the reduce-scatter send buffer, every element of the model")
@@ -132,12 +135,11 @@ def main():
         lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
     st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev,
                    chunk_elems=args.chunk, max_blocks=args.max_blocks, kind=args.plan,
-                   lr_scale=lr_s, wd_scale=wd_s)
+                   lr_scale=lr_s, wd_scale=wd_s, layout=args.layout)
     L = int(st.plan.info.shard_elems)
     master_full = W.make_master(w, seed=0, device=dev)
     st.scatter_to_arena(st.master, master_full)
-    for wt, mt in zip(st.weights, master_full):
-        wt.copy_(mt)
+    st.load_weights(master_full)
     # a bounded sample for the CPU oracle: the first slices, in packed order
     sample_target = 1 << 23
     sample_idx = []
@@ -151,6 +153,7 @@ def main():
     del master_full
     for k in range(w.n_micro):
         W.make_micro_grads(w, 1, k, seed=0, device=dev, out=st.grads[k])
+        st.stage_grads(k)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: L={L} chunks={st.plan.info.n_chunks} setup {time.time() - t0:.1f}s")
 
@@ -315,7 +318,7 @@ def main():
                    "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
                    "chunk_elems": int(st.plan.info.chunk_elems),
                    "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
-                   "mup": bool(args.mup), "accum": args.accum},
+                   "mup": bool(args.mup), "accum": args.accum, "layout": args.layout},
         "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,

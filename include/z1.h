@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 3
+#define Z1_ABI_VERSION 4
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -150,14 +150,20 @@ typedef struct z1_bind {
     int32_t rank;           /* in [0, dp_size)                              */
     int32_t n_micro;        /* K, bf16 micro-batch gradients per step, >= 1 */
     const int64_t *numel;   /* host [n_tensors]                             */
-    /* bf16 working weights: host array [n_tensors] of device pointers, each
-     * to element 0 of the FULL tensor (numel[i] bf16 values).  The step
-     * writes only elements [start[i], start[i]+len[i]).                  */
+    /* bf16 working weights.  layout Z1_LAYOUT_FULL: host array [n_tensors]
+     * of device pointers, each to element 0 of the FULL tensor (numel[i]
+     * bf16 values); the step writes only elements [start[i],
+     * start[i]+len[i]).  Z1_LAYOUT_PACKED: host array [1] holding one device
+     * pointer to a packed bf16 shard of arena_elems values in arena order
+     * (element e of slice i at arena_off[i] + e, as in the fp32 arenas);
+     * padding elements are never written.                                  */
     void *const *weights;
-    /* bf16 micro-batch gradients: host array [n_micro * n_tensors] of
-     * device pointers; grads[k*n_tensors + i] points to element 0 of the
-     * FULL gradient of tensor i for micro-batch k.  Only this rank's slice
-     * is read.                                                             */
+    /* bf16 micro-batch gradients.  Z1_LAYOUT_FULL: host array
+     * [n_micro * n_tensors] of device pointers; grads[k*n_tensors + i]
+     * points to element 0 of the FULL gradient of tensor i for micro-batch
+     * k, of which only this rank's slice is read.  Z1_LAYOUT_PACKED: host
+     * array [n_micro], grads[k] one packed bf16 shard in arena order (for
+     * example the output of an equal-count reduce-scatter).               */
     const void *const *grads;
     /* fp32 arenas, device, arena_elems floats each (see z1_shard_plan).
      * master holds the fp32 master weights, exp_avg / exp_avg_sq the Adam
@@ -185,7 +191,19 @@ typedef struct z1_bind {
      * must be finite, wd_scale >= 0.                                       */
     const double *lr_scale;
     const double *wd_scale;
+    int32_t layout;         /* z1_layout of weights and grads (0 = full)    */
+    int32_t reserved;       /* must be 0                                    */
 } z1_bind;
+
+/* Where the bf16 weights and gradients live (z1_bind.layout).  The packed
+ * form is the shard as the collectives around the step exchange it: with the
+ * arena offsets residue-matched to the slice starts, a packed bf16 shard has
+ * the same 16-byte alignment per element as the full tensor, so the kernels
+ * are the same for both. */
+typedef enum z1_layout {
+    Z1_LAYOUT_FULL = 0,
+    Z1_LAYOUT_PACKED = 1
+} z1_layout;
 
 /* Geometry of a created plan. */
 typedef struct z1_plan_info {
@@ -207,8 +225,9 @@ typedef struct z1_plan_info {
  * the call.  The upload is enqueued on `stream` and the call waits for it
  * (plan creation is not part of the step), so the plan is ready on return.
  * Errors: Z1_EINVAL (bad geometry, null pointers, arena too small,
- * bad chunk_elems, bad plan_kind / rows / multipliers), Z1_EALIGN (a weight, gradient or arena
- * pointer not 16-byte aligned), Z1_ENOMEM, Z1_EHIP.  *out is NULL on error.
+ * bad chunk_elems, bad plan_kind / rows / multipliers / layout, reserved not 0), Z1_EALIGN
+ * (a weight, gradient or arena pointer not 16-byte aligned), Z1_ENOMEM, Z1_EHIP.  *out is
+ * NULL on error.
  * ------------------------------------------------------------------------ */
 z1_status z1_plan_create(z1_plan **out, const z1_bind *bind, z1_stream stream);
 

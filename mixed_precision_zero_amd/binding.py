@@ -35,6 +35,7 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
+LAYOUTS = {"full": 0, "packed": 1}
 DECAY_STYLES = {"none": 0, "linear": 1, "cosine": 2}
 
 
@@ -56,7 +57,8 @@ class Bind(ctypes.Structure):
                 ("max_blocks", ctypes.c_int32), ("plan_kind", ctypes.c_int32),
                 ("rows", ctypes.POINTER(ctypes.c_int64)),
                 ("lr_scale", ctypes.POINTER(ctypes.c_double)),
-                ("wd_scale", ctypes.POINTER(ctypes.c_double))]
+                ("wd_scale", ctypes.POINTER(ctypes.c_double)),
+                ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class LRSchedule(ctypes.Structure):
@@ -220,18 +222,25 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
                    chunk_elems: int = 0, max_blocks: int = 0, stream=None,
                    kind: str = "per_tensor", rows: Optional[Sequence[int]] = None,
                    lr_scale: Optional[Sequence[float]] = None,
-                   wd_scale: Optional[Sequence[float]] = None) -> Plan:
-    """Bind device buffers: weights[i] and grads[k][i] are full-size bf16
-    tensors (or raw device addresses), the four arenas fp32 of arena_elems."""
+                   wd_scale: Optional[Sequence[float]] = None,
+                   layout: str = "full") -> Plan:
+    """Bind device buffers, the four arenas fp32 of arena_elems.
+    layout "full": weights[i] and grads[k][i] are full-size bf16 tensors (or
+    raw device addresses).  layout "packed": weights is one packed bf16
+    shard and grads[k] one packed bf16 shard per micro-batch, in arena order."""
     n = _i64(numel)
     K = len(grads)
-    for gk in grads:
-        if len(gk) != n.size:
-            raise ValueError("grads[k] must list one tensor per parameter")
-    if len(weights) != n.size:
-        raise ValueError("weights must list one tensor per parameter")
-    wp = (ctypes.c_void_p * max(n.size, 1))(*[_dptr(w) for w in weights])
-    gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
+    if layout == "packed":
+        wp = (ctypes.c_void_p * 1)(_dptr(weights))
+        gp = (ctypes.c_void_p * max(K, 1))(*[_dptr(g) for g in grads])
+    else:
+        for gk in grads:
+            if len(gk) != n.size:
+                raise ValueError("grads[k] must list one tensor per parameter")
+        if len(weights) != n.size:
+            raise ValueError("weights must list one tensor per parameter")
+        wp = (ctypes.c_void_p * max(n.size, 1))(*[_dptr(w) for w in weights])
+        gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
     arena = [master, exp_avg, exp_avg_sq, acc]
     sizes = [a.numel() for a in arena if hasattr(a, "numel")]
     r = _i64(rows) if rows is not None else None
@@ -249,7 +258,8 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
              chunk_elems=chunk_elems, max_blocks=max_blocks, plan_kind=PLAN_KINDS[kind],
              rows=_p64(r) if r is not None else None,
              lr_scale=ls.ctypes.data_as(PD) if ls is not None else None,
-             wd_scale=ws.ctypes.data_as(PD) if ws is not None else None)
+             wd_scale=ws.ctypes.data_as(PD) if ws is not None else None,
+             layout=LAYOUTS[layout], reserved=0)
     h = ctypes.c_void_p()
     _check(lib.z1_plan_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)),
            "z1_plan_create")

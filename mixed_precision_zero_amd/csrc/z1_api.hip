@@ -266,7 +266,8 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
         return Z1_EINVAL;
     *out = nullptr;
     if (!b || b->n_tensors < 0 || b->n_micro < 1 || b->dp_size < 1 || b->rank < 0 ||
-        b->rank >= b->dp_size || b->max_blocks < 0)
+        b->rank >= b->dp_size || b->max_blocks < 0 || b->reserved != 0 ||
+        (b->layout != Z1_LAYOUT_FULL && b->layout != Z1_LAYOUT_PACKED))
         return Z1_EINVAL;
     const int32_t n = b->n_tensors, K = b->n_micro;
     if (n > 0 && (!b->numel || !b->weights || !b->grads))
@@ -315,7 +316,44 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     // pointers: non-null for tensors this rank touches, 16-byte aligned
     std::vector<uint16_t *> wptr(n);
     std::vector<const uint16_t *> gptr((size_t)K * n);
-    for (int32_t i = 0; i < n; ++i) {
+    const bool packed = b->layout == Z1_LAYOUT_PACKED;
+    int64_t shard_elems = 0;
+    for (int32_t i = 0; i < n; ++i)
+        shard_elems += p->len[i];
+    if (packed && shard_elems > 0) {
+        // one shard buffer per role; tensor i's pointer is placed so that
+        // element start[i] + e lands on arena element arena_off[i] + e
+        // (arena_off[i] - start[i] is a multiple of 8: 16-byte aligned)
+        const void *wbase = b->weights[0];
+        if (!wbase) {
+            delete p;
+            return Z1_EINVAL;
+        }
+        if (!aligned(wbase, 16)) {
+            delete p;
+            return Z1_EALIGN;
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            if (!b->grads[k]) {
+                delete p;
+                return Z1_EINVAL;
+            }
+            if (!aligned(b->grads[k], 16)) {
+                delete p;
+                return Z1_EALIGN;
+            }
+        }
+        auto at = [&](const void *base, int32_t i) {
+            return reinterpret_cast<uintptr_t>(base) +
+                   (uintptr_t)(2 * (p->arena_off[i] - p->start[i]));
+        };
+        for (int32_t i = 0; i < n; ++i) {
+            wptr[i] = reinterpret_cast<uint16_t *>(at(wbase, i));
+            for (int32_t k = 0; k < K; ++k)
+                gptr[(size_t)k * n + i] = reinterpret_cast<const uint16_t *>(at(b->grads[k], i));
+        }
+    }
+    for (int32_t i = 0; i < n && !packed; ++i) {
         wptr[i] = static_cast<uint16_t *>(b->weights[i]);
         for (int32_t k = 0; k < K; ++k)
             gptr[(size_t)k * n + i] = static_cast<const uint16_t *>(b->grads[(size_t)k * n + i]);

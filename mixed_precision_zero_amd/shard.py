@@ -4,6 +4,11 @@ This is memory plumbing: it allocates the fp32 arenas (master, m, v, acc),
 the full-size bf16 weights and micro-gradient slots and the device norm
 scalar with torch, creates the plan, and calls the four library entry points
 in step order.  No arithmetic of the step happens here.
+
+layout="packed" binds one packed bf16 weight shard and one packed bf16
+gradient shard per micro-batch (arena order) instead of the full tensors;
+the full-size tensors then serve only as staging for seeded inputs
+(stage_grads copies this rank's slices into the packed slot).
 """
 from __future__ import annotations
 
@@ -21,7 +26,7 @@ class ShardStep:
                  grads: Optional[List[List[torch.Tensor]]] = None,
                  arena_pad: int = 0, kind: str = "per_tensor",
                  lr_scale: Optional[Sequence[float]] = None,
-                 wd_scale: Optional[Sequence[float]] = None):
+                 wd_scale: Optional[Sequence[float]] = None, layout: str = "full"):
         self.shapes = [tuple(s) for s in shapes]
         self.numel = [int(torch.Size(s).numel()) for s in self.shapes]
         self.rows = [int(s[0]) if len(s) else 1 for s in self.shapes]
@@ -41,11 +46,18 @@ class ShardStep:
         self.grads = grads if grads is not None else [
             [torch.zeros(s, **bf) for s in self.shapes] for _ in range(n_micro)]
         self.d_S = torch.zeros(1, dtype=torch.float64, device=self.device)
-        self.plan = B.z1_plan_create(self.numel, dp_size, rank, self.weights, self.grads,
+        self.layout = layout
+        self.w_packed = self.g_packed = None
+        bind_w, bind_g = self.weights, self.grads
+        if layout == "packed":
+            self.w_packed = torch.zeros(n, **bf)
+            self.g_packed = [torch.zeros(n, **bf) for _ in range(n_micro)]
+            bind_w, bind_g = self.w_packed, self.g_packed
+        self.plan = B.z1_plan_create(self.numel, dp_size, rank, bind_w, bind_g,
                                      self.master, self.exp_avg, self.exp_avg_sq, self.acc,
                                      chunk_elems=chunk_elems, max_blocks=max_blocks, kind=kind,
                                      rows=self.rows if kind == "dim0" else None,
-                                     lr_scale=lr_scale, wd_scale=wd_scale)
+                                     lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
         self.t = 0
 
     # -- layout helpers (torch copies; initialisation and inspection only) --
@@ -66,7 +78,23 @@ class ShardStep:
             return arena[:0].clone()
         return torch.cat(parts)
 
+    def stage_grads(self, k: int) -> None:
+        """Packed layout: copy this rank's slices of the full staging
+        gradients of micro-batch k into its packed slot (no-op otherwise)."""
+        if self.layout == "packed":
+            self.scatter_to_arena(self.g_packed[k], self.grads[k])
+
+    def load_weights(self, full: Sequence[torch.Tensor]) -> None:
+        """The bf16 weights before a step, from full-size tensors."""
+        if self.layout == "packed":
+            self.scatter_to_arena(self.w_packed, full)
+        else:
+            for wt, x in zip(self.weights, full):
+                wt.copy_(x)
+
     def packed_weights(self) -> torch.Tensor:
+        if self.layout == "packed":
+            return self.packed(self.w_packed)
         parts = [self.weights[i].reshape(-1)[s:s + ln] for i, s, ln, _ in self.slices() if ln]
         if not parts:
             return torch.zeros(0, dtype=torch.bfloat16, device=self.device)

@@ -68,7 +68,7 @@ class Parity:
 
     def __init__(self, w: W.Workload, device="cuda", chunk_elems=0, max_blocks=0,
                  seed=0, canaries=True, kind="per_tensor", lr_scale=None, wd_scale=None,
-                 ranges=None):
+                 ranges=None, layout="full"):
         self.w = w
         self.ranges = ranges     # None: one accumulation call per micro-batch
         self.dev = torch.device(device)
@@ -78,7 +78,7 @@ class Parity:
         self.st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=self.dev,
                             chunk_elems=chunk_elems, max_blocks=max_blocks,
                             arena_pad=64 if canaries else 0, kind=kind,
-                            lr_scale=lr_scale, wd_scale=wd_scale)
+                            lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
         rows = [s[0] if len(s) else 1 for s in w.shapes]
         self.o_start, self.o_len = self.o.plan(kind, w.numel, rows, w.dp_size, w.rank)
         self.segments = None
@@ -97,10 +97,11 @@ class Parity:
             self.free_mask = ~used
             for a in (self.st.master, self.st.exp_avg, self.st.exp_avg_sq, self.st.acc):
                 a[self.free_mask] = CANARY
+            if self.st.w_packed is not None:
+                self.st.w_packed[self.free_mask] = CANARY
         master = W.make_master(w, seed=seed, device=self.dev)
         self.st.scatter_to_arena(self.st.master, master)
-        for wt, mt in zip(self.st.weights, master):
-            wt.copy_(mt)     # torch's own cast: the weights before any step
+        self.st.load_weights(master)     # torch's own cast: the weights before any step
         self.p = self._packed_host_f32(master)
         del master
         self.m = np.zeros(self.L, np.float32)
@@ -141,6 +142,7 @@ class Parity:
         g = np.empty((w.n_micro, self.L), np.uint16)
         for k in range(w.n_micro):
             W.make_micro_grads(w, t, k, seed=self.seed, device=self.dev, out=st.grads[k])
+            st.stage_grads(k)
             g[k] = self._packed_host_bf16(st.grads[k])
         t1 = time.time()
         st.step(w.hp(), ranges=self.ranges)
@@ -183,6 +185,9 @@ class Parity:
         ok = True
         for a in (self.st.master, self.st.exp_avg, self.st.exp_avg_sq, self.st.acc):
             ok &= bool((a[self.free_mask] == CANARY).all())
+        if self.st.w_packed is not None:
+            c = torch.tensor(CANARY, dtype=torch.bfloat16, device=self.dev)
+            ok &= bool((self.st.w_packed[self.free_mask] == c).all())
         return ok
 
     def weights_outside_slices_intact(self) -> bool:

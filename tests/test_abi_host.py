@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 3
+    assert B.z1_abi_version() == 4
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -125,6 +125,9 @@ def _bind(**over):
     (dict(master=0), B.Z1_EINVAL), (dict(w0=0), B.Z1_EINVAL), (dict(g1=0), B.Z1_EINVAL),
     (dict(w0=0x10008), B.Z1_EALIGN), (dict(g1=0x30002), B.Z1_EALIGN),
     (dict(acc=0x70004), B.Z1_EALIGN),
+    (dict(layout=2), B.Z1_EINVAL), (dict(reserved=1), B.Z1_EINVAL),
+    (dict(layout=1, w0=0), B.Z1_EINVAL), (dict(layout=1, g1=0), B.Z1_EINVAL),
+    (dict(layout=1, w0=0x10008), B.Z1_EALIGN), (dict(layout=1, g1=0x30002), B.Z1_EALIGN),
 ])
 def test_plan_create_rejects_before_device_work(over, status):
     """Validation happens on the host: fake addresses never reach the device."""
