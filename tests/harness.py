@@ -159,24 +159,45 @@ class Parity:
         return self.compare(S)
 
     def compare(self, S_ref: float) -> StepReport:
+        """Bit equality first (cheap); the tolerance metrics are computed only
+        for a buffer that is not bit-identical (for identical buffers they
+        are 0 by definition)."""
         st = self.st
         acc_g = st.packed(st.acc).cpu().numpy()
         S_g = float(st.d_S.item())
-        rep = StepReport(step=self.t, acc_mismatch=int((acc_g != self.acc).sum()),
-                         S_gpu=S_g, S_ref=S_ref,
+        acc_bad = 0 if np.array_equal(acc_g, self.acc) else int((acc_g != self.acc).sum())
+        del acc_g
+        rep = StepReport(step=self.t, acc_mismatch=acc_bad, S_gpu=S_g, S_ref=S_ref,
                          S_rel=abs(S_g - S_ref) / S_ref if S_ref else abs(S_g))
+        master_exact = True
+        x_master = None
         for name, gpu, ref in (("master", st.master, self.p), ("exp_avg", st.exp_avg, self.m),
                                ("exp_avg_sq", st.exp_avg_sq, self.v)):
             x = st.packed(gpu).cpu().numpy()
-            rep.rel[name] = rel_rms_err(x, ref)
-            rep.not_bitexact[name] = int((x.view(np.uint32) != ref.view(np.uint32)).sum())
+            if np.array_equal(x.view(np.uint32), ref.view(np.uint32)):
+                rep.rel[name] = 0.0
+                rep.not_bitexact[name] = 0
+            else:
+                rep.rel[name] = rel_rms_err(x, ref)
+                rep.not_bitexact[name] = int((x.view(np.uint32) != ref.view(np.uint32)).sum())
+                if name == "master":
+                    master_exact = False
             if name == "master":
-                # the GPU's bf16 must be torch's RNE cast of the GPU's own master
-                own = bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+                x_master = x
+            del x
         wb = bf16_bits(st.packed_weights())
-        rep.bf16_max_ulp = int(np.max(np.abs(bf16_ord(wb) - bf16_ord(self.wbits)))) if wb.size else 0
-        rep.bf16_self_mismatch = int((wb != own).sum()) if wb.size else 0
-        rep.not_bitexact["bf16"] = int((wb != self.wbits).sum())
+        if wb.size and not np.array_equal(wb, self.wbits):
+            rep.bf16_max_ulp = int(np.max(np.abs(bf16_ord(wb) - bf16_ord(self.wbits))))
+            rep.not_bitexact["bf16"] = int((wb != self.wbits).sum())
+        else:
+            rep.not_bitexact["bf16"] = 0
+        if wb.size:
+            # the GPU's bf16 must be torch's RNE cast of the GPU's own master:
+            # every element when anything differs, else a strided sample
+            # (exactness against the oracle already implies it)
+            sl = slice(None) if (not master_exact or rep.not_bitexact["bf16"]) else slice(None, None, 97)
+            own = bf16_bits(torch.from_numpy(np.ascontiguousarray(x_master[sl])).to(torch.bfloat16))
+            rep.bf16_self_mismatch = int((wb[sl] != own).sum())
         return rep
 
     def canaries_intact(self) -> bool:
