@@ -118,7 +118,9 @@ void append_chunks(std::vector<Chunk> &chunks, int32_t n, const int64_t *start, 
 }
 
 // Issue order: consecutive workgroups alternate between kInterleave distant
-// parts of the table (entry j is piece (j % P) * m + j / P).  Measured on the
+// parts of the table (entry j is piece (j % P) * m + j / P).  The hardware
+// hands workgroups to the 8 XCDs round-robin, so with P = 8 each XCD walks
+// one contiguous eighth of the shard through its own L2.  Measured on the
 // 7B shard, P = 8 takes the accumulation pass from 1.44 to 1.38 ms; results
 // do not depend on the order (elements are independent, the norm is exactly
 // rounded).
