@@ -105,10 +105,10 @@ def traffic_from_profiles(workload: str, kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
-        print("bench.py: the ZeRO-1 shard step here runs on one GPU; multi-GPU runs "
-              "(reduce-scatter / all-gather over RCCL) are not part of this build",
+        print(json.dumps({"error": "the shard step is measured on one GPU only; "
+                                   "--gpus must be 1", "n_gpus": args.gpus}), flush=True)
+        print("bench.py: one rank's ZeRO-1 shard step runs on one GPU; the collectives "
+              "around it (reduce-scatter / all-gather over RCCL) are not implemented",
               file=sys.stderr)
         sys.exit(2)
 
