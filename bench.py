@@ -312,7 +312,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state, f64 update math, bf16 weights/grads",
+        "dtype": "f64",
+        "dtype_detail": "binary64 AdamW update (the dominant kernel) on fp32 master/m/v; "
+                        "binary32 accumulation of bf16 gradients; bf16 weights out",
         "data": "synthetic",
         "config": {"workload": w.name, "params": w.total_params, "shard_elems": L,
                    "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
@@ -409,7 +411,8 @@ def bench_pack(args, w, dev, log):
            "value": psi / (step_ms / 1e3), "unit": "params/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32 accumulate of bf16 grads", "data": "synthetic",
+           "dtype": "f32", "dtype_detail": "binary32 accumulation of bf16 gradients",
+           "data": "synthetic",
            "config": {"workload": w.name, "params": psi, "dp_size": w.dp_size,
                       "micro_batches": K, "plan": args.plan, "seg_elems": seg,
                       "accum": args.accum},
