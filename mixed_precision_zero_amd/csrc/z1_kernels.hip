@@ -96,10 +96,19 @@ __device__ __forceinline__ void two_sum(double a, double b, double &s, double &e
     e = (a - (s - bb)) + (b - bb);
 }
 
+// A non-finite plain sum (an Inf or NaN square somewhere) makes the error
+// terms meaningless (Inf - Inf); the sum is then the plain one, +Inf or NaN,
+// and the low part is dropped so it cannot turn an Inf into NaN.  Finite
+// sums take the double-double path unchanged.
 __device__ __forceinline__ void dd_add(double &hi, double &lo, double bhi, double blo)
 {
     double s, e;
     two_sum(hi, bhi, s, e);
+    if (!__builtin_isfinite(s)) {
+        hi = s;
+        lo = 0.0;
+        return;
+    }
     e = e + (lo + blo);
     two_sum(s, e, hi, lo);
 }
@@ -564,7 +573,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
     double c = 1.0;
     if (MATH && k.clip > 0.0) {
         const double cc = k.clip / (sqrt(S[0]) + 1e-6);
-        c = cc < 1.0 ? cc : 1.0;
+        c = cc >= 1.0 ? 1.0 : cc;  // clamp at 1; a NaN norm gives a NaN coefficient
     }
     const int t = (int)threadIdx.x;
     for (int64_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {

@@ -209,7 +209,9 @@ Z1O_EXPORT double z1o_norm_sq(int64_t L, const float *acc)
             err += (x - t) + s;
         s = t;
     }
-    return s + err;
+    /* a non-finite term leaves the error sum meaningless (Inf - Inf): the
+     * exact sum is then the plain one, +Inf or NaN */
+    return isfinite(s) ? s + err : s;
 }
 
 /* ------------------------------------------------------------------ */
@@ -254,7 +256,7 @@ Z1O_EXPORT double z1o_clip_coef(double S, double clip)
     if (!(clip > 0.0))
         return 1.0;
     double c = clip / (sqrt(S) + 1e-6);
-    return c < 1.0 ? c : 1.0;
+    return c >= 1.0 ? 1.0 : c; /* a clamp at 1: a NaN norm gives a NaN coefficient */
 }
 
 /* ------------------------------------------------------------------ */

@@ -259,6 +259,16 @@ def check_norm_fsum(o):
         S = o.norm_sq(acc)
         exact = math.fsum((acc.astype(np.float64) ** 2).tolist())
         assert S == exact, f"n={n}: S={S!r} correctly rounded={exact!r}"
+    # non-finite squares: the exact sum is +Inf with an Inf term, NaN with a
+    # NaN term (math.fsum agrees)
+    acc = (rng.standard_normal(5000) * 1e-2).astype(np.float32)
+    for bad, want in ((np.inf, math.inf), (-np.inf, math.inf)):
+        a = acc.copy()
+        a[1234] = bad
+        assert o.norm_sq(a) == want == math.fsum((a.astype(np.float64) ** 2).tolist())
+    a = acc.copy()
+    a[7] = np.nan
+    assert math.isnan(o.norm_sq(a))
 
 
 def check_clip_vs_torch(o):
@@ -280,6 +290,23 @@ def check_clip_vs_torch(o):
         else:
             assert c == 1.0
     assert o.clip_coef(1e6, 0.0) == 1.0 and o.clip_coef(1e6, -1.0) == 1.0
+    # non-finite gradients propagate as they do through torch's clip_grad_norm_
+    # (its clamp at 1 keeps a NaN coefficient): an Inf gradient makes S = Inf
+    # and c = 0 (Inf * 0 = NaN at that element); a NaN gradient makes every
+    # clipped gradient NaN
+    for bad in (math.inf, math.nan):
+        acc = (rng.standard_normal(1000) * 1e-2).astype(np.float32)
+        acc[17] = bad
+        c = o.clip_coef(o.norm_sq(acc), 1.0)
+        t = torch.from_numpy(acc.astype(np.float64))
+        t.grad = t.clone()
+        torch.nn.utils.clip_grad_norm_([t], max_norm=1.0)
+        with np.errstate(invalid="ignore"):       # Inf * 0 and NaN products are the point
+            ours = c * acc.astype(np.float64)
+        ref = t.grad.numpy()
+        assert np.array_equal(np.isnan(ours), np.isnan(ref)), f"NaN positions differ ({bad})"
+        fin = ~np.isnan(ref)
+        assert np.array_equal(ours[fin], ref[fin]), f"finite values differ ({bad})"
 
 
 # ---------------------------------------------------------------------------

@@ -1,5 +1,6 @@
 """GPU behaviour beyond parity: determinism, call order, resume."""
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -211,5 +212,61 @@ def test_plan_probe_covers_exactly_the_slices():
             if ln:
                 assert not bool((flat[s:s + ln] == 3.0).any())
         assert B.lib.z1_probe_plan(st.plan.handle, 1, None) == B.Z1_EINVAL   # unknown kind
+    finally:
+        st.close()
+
+
+def _nan_aware_equal_f32(x: np.ndarray, y: np.ndarray) -> bool:
+    nx, ny = np.isnan(x), np.isnan(y)
+    return bool(np.array_equal(nx, ny) and
+                np.array_equal(x[~nx].view(np.uint32), y[~ny].view(np.uint32)))
+
+
+def _bf16_nan(h: np.ndarray) -> np.ndarray:
+    return ((h & 0x7F80) == 0x7F80) & ((h & 0x7F) != 0)
+
+
+@pytest.mark.parametrize("resident", [False, True], ids=["per_call", "resident"])
+@pytest.mark.parametrize("bad", ["inf", "nan"])
+def test_nonfinite_gradient_matches_oracle(bad, resident):
+    """A non-finite gradient element propagates exactly as in the oracle:
+    Inf gives S = Inf and c = 0 (only that element turns NaN, 0 * Inf); NaN
+    gives S = NaN and c = NaN (every element turns NaN).  NaN positions must
+    agree and every other element must match bit for bit (NaN payloads are
+    not compared)."""
+    import oracle
+    o = oracle.get()
+    w = W.TINY
+    st = _fresh(w)
+    try:
+        for k in range(w.n_micro):
+            W.make_micro_grads(w, 1, k, seed=0, device="cuda", out=st.grads[k])
+        i, s0, ln, _ = next(x for x in st.slices() if x[2] > 8)
+        st.grads[1][i].view(-1)[s0 + ln // 2] = float(bad)
+        p = st.packed(st.master).cpu().numpy().copy()
+        m = np.zeros_like(p)
+        v = np.zeros_like(p)
+        wb = np.zeros(p.size, np.uint16)
+        acc = np.zeros_like(p)
+        g = np.stack([torch.cat([st.grads[k][j].reshape(-1)[s:s + n] for j, s, n, _ in st.slices()
+                                 if n]).view(torch.int16).cpu().numpy().view(np.uint16)
+                      for k in range(w.n_micro)])
+        st.step(w.hp(), ranges=[(0, w.n_micro)] if resident else None)
+        torch.cuda.synchronize()
+        with np.errstate(invalid="ignore", over="ignore"):
+            S, c, _ = o.step(g, p, m, v, step=1, acc=acc, w=wb, **w.hp())
+        S_gpu = float(st.d_S.item())
+        if bad == "inf":
+            assert S == math.inf and S_gpu == math.inf and c == 0.0
+        else:
+            assert math.isnan(S) and math.isnan(S_gpu) and math.isnan(c)
+        for name, gpu, ref in (("acc", st.acc, acc), ("master", st.master, p),
+                               ("exp_avg", st.exp_avg, m), ("exp_avg_sq", st.exp_avg_sq, v)):
+            assert _nan_aware_equal_f32(st.packed(gpu).cpu().numpy(), ref), name
+        wg = st.packed_weights().view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(_bf16_nan(wg), _bf16_nan(wb))
+        assert np.array_equal(wg[~_bf16_nan(wg)], wb[~_bf16_nan(wb)])
+        n_nan = int(np.isnan(p).sum())
+        assert (n_nan == 1) if bad == "inf" else (n_nan == p.size)
     finally:
         st.close()

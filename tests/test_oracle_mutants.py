@@ -52,9 +52,11 @@ MUTANTS = {
     "acc_drops_last": [("for (int32_t k = 1; k < K; ++k)", "for (int32_t k = 1; k < K - 1; ++k)")],
     "norm_no_square": [("double x = a * a;", "double x = a;")],
     "norm_in_float": [("double t = s + x;", "double t = (float)(s + x);")],
-    "norm_uncompensated": [("return s + err;", "return s;")],
+    "norm_uncompensated": [("return isfinite(s) ? s + err : s;", "return s;")],
     "clip_no_eps": [("double c = clip / (sqrt(S) + 1e-6);", "double c = clip / sqrt(S);")],
-    "clip_no_min": [("return c < 1.0 ? c : 1.0;", "return c;")],
+    "clip_no_min": [("return c >= 1.0 ? 1.0 : c;", "return c;")],
+    "norm_inf_becomes_nan": [("return isfinite(s) ? s + err : s;", "return s + err;")],
+    "clip_nan_means_no_clip": [("return c >= 1.0 ? 1.0 : c;", "return c < 1.0 ? c : 1.0;")],
     "clip_uses_S": [("double c = clip / (sqrt(S) + 1e-6);", "double c = clip / (S + 1e-6);")],
     "adamw_decay_without_lr": [("(1.0 - lr * wd)", "(1.0 - wd)")],
     "adamw_decay_after_update": [
