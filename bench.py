@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -85,8 +86,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with comments and whitespace removed,
+    so that counters taken on a kernel stay attached to it through comment
+    edits and are dropped after any change to the code."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"\s+", "", src)
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str, kernel: str):

@@ -12,8 +12,12 @@
 //
 // Arithmetic follows the definition exactly (this file is built with
 // -ffp-contract=off and without fast-math):
-//   * accumulation is one binary32 add per micro-batch, in order;
-//   * the squared norm is an exact-square, double-double sum;
+//   * accumulation is one binary32 add per micro-batch, in order, whether
+//     one pass reads one micro-batch slot or several;
+//   * the squared norm is an exact-square, double-double sum (+Inf or NaN
+//     when a square is);
+//   * the clip coefficient is clip / (sqrt(S) + 1e-6) clamped at 1, a NaN
+//     norm giving a NaN coefficient;
 //   * AdamW is evaluated in binary64 with the same operation sequence as the
 //     definition (separate multiply and add, IEEE division and square root),
 //     then rounded once to binary32 and, for the weight, to bf16 (nearest
