@@ -133,21 +133,47 @@ int main(void)
     b.arena_elems = arena;
     z1_plan *plan = NULL;
     CHECK_Z1(z1_plan_create(&plan, &b, NULL));
+    /* the same gradients as packed bf16 shards in arena order, and a packed
+     * weight shard whose padding holds a canary, bound to a second plan over
+     * the same fp32 arenas (Z1_LAYOUT_PACKED) */
+    void *gp[K], *wp = NULL;
+    uint16_t *packed_host = malloc(arena * 2 + 16);
+    for (int k = 0; k < K; ++k) {
+        memset(packed_host, 0, arena * 2);
+        pos = 0;
+        for (int i = 0; i < NT; ++i) {
+            memcpy(packed_host + off[i], hg + (int64_t)k * L + pos, len[i] * 2);
+            pos += len[i];
+        }
+        CHECK_HIP(hipMalloc(&gp[k], arena * 2 + 16));
+        CHECK_HIP(hipMemcpy(gp[k], packed_host, arena * 2, hipMemcpyHostToDevice));
+    }
+    CHECK_HIP(hipMalloc(&wp, arena * 2 + 16));
+    CHECK_HIP(hipMemset(wp, 0x5A, arena * 2 + 16));
+    z1_bind bp = b;
+    bp.weights = (void *const *)&wp;
+    bp.grads = (const void *const *)gp;
+    bp.layout = Z1_LAYOUT_PACKED;
+    z1_plan *plan_packed = NULL;
+    CHECK_Z1(z1_plan_create(&plan_packed, &bp, NULL));
+
     /* step 1: one accumulation call per micro-batch; step 2: all K resident
-     * slots in one z1_accum_grads_range call.  Both must match the oracle. */
+     * slots in one z1_accum_grads_range call; step 3: the packed layout.
+     * Each must match the oracle. */
     int bad = 0;
     double S = 0.0, S_gpu = 0.0, c = 0.0;
     float *back = malloc(arena * 4);
-    for (int t = 1; t <= 2; ++t) {
+    for (int t = 1; t <= 3; ++t) {
         z1_adamw_hp hp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
+        z1_plan *pl = t == 3 ? plan_packed : plan;
         if (t == 1) {
             for (int k = 0; k < K; ++k)
-                CHECK_Z1(z1_accum_grads(plan, k, NULL));
+                CHECK_Z1(z1_accum_grads(pl, k, NULL));
         } else {
-            CHECK_Z1(z1_accum_grads_range(plan, 0, K, NULL));
+            CHECK_Z1(z1_accum_grads_range(pl, 0, K, NULL));
         }
-        CHECK_Z1(z1_grad_norm_sq(plan, d_S, NULL));
-        CHECK_Z1(z1_adamw_step(plan, &hp, d_S, NULL));
+        CHECK_Z1(z1_grad_norm_sq(pl, d_S, NULL));
+        CHECK_Z1(z1_adamw_step(pl, &hp, d_S, NULL));
         CHECK_HIP(hipDeviceSynchronize());
 
         z1o_hp ohp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
@@ -165,7 +191,20 @@ int main(void)
             }
         }
         pos = 0;
-        for (int i = 0; i < NT; ++i) {
+        if (t == 3) {
+            CHECK_HIP(hipMemcpy(packed_host, wp, arena * 2, hipMemcpyDeviceToHost));
+            int64_t used = 0;
+            for (int i = 0; i < NT; ++i) {
+                bad += memcmp(packed_host + off[i], hw + pos, len[i] * 2) != 0;
+                pos += len[i];
+                used += len[i];
+            }
+            int64_t canaries = 0;
+            for (int64_t e = 0; e < arena; ++e)
+                canaries += packed_host[e] == 0x5A5A;
+            bad += canaries != arena - used; /* padding: untouched */
+        }
+        for (int i = 0; i < NT && t < 3; ++i) {
             uint16_t *full = malloc(numel[i] * 2 + 2);
             CHECK_HIP(hipMemcpy(full, w[i], numel[i] * 2, hipMemcpyDeviceToHost));
             bad += memcmp(full + start[i], hw + pos, len[i] * 2) != 0;
@@ -175,12 +214,14 @@ int main(void)
             pos += len[i];
             free(full);
         }
-        printf("C ABI step %d (%s): L=%lld S=%.17g (oracle %.17g) c=%.6g\n", t,
-               t == 1 ? "z1_accum_grads per micro-batch" : "z1_accum_grads_range", (long long)L,
-               S_gpu, S, c);
+        printf("C ABI step %d (%s): L=%lld S=%.17g (oracle %.17g) c=%.6g bad=%d\n", t,
+               t == 1 ? "z1_accum_grads per micro-batch"
+                      : (t == 2 ? "z1_accum_grads_range" : "packed layout, range"),
+               (long long)L, S_gpu, S, c, bad);
     }
     free(back);
     CHECK_Z1(z1_plan_destroy(plan));
+    CHECK_Z1(z1_plan_destroy(plan_packed));
     printf("C ABI: %s\n", bad ? "MISMATCH" : "bit-exact");
     return bad ? 1 : 0;
 }
