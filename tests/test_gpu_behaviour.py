@@ -270,3 +270,44 @@ def test_nonfinite_gradient_matches_oracle(bad, resident):
         assert (n_nan == 1) if bad == "inf" else (n_nan == p.size)
     finally:
         st.close()
+
+
+def test_two_plans_on_two_streams_are_independent():
+    """Two plans (their own chunk tables, norm partials and arrival counters)
+    stepping concurrently on two streams give the bits each gives alone."""
+    wa = RAGGED_SMALL
+    wb = dataclasses.replace(W.TINY, n_micro=3)
+
+    def run(concurrent):
+        sa, sb = _fresh(wa), _fresh(wb)
+        try:
+            for k in range(wa.n_micro):
+                W.make_micro_grads(wa, 1, k, seed=0, device="cuda", out=sa.grads[k])
+            for k in range(wb.n_micro):
+                W.make_micro_grads(wb, 1, k, seed=0, device="cuda", out=sb.grads[k])
+            torch.cuda.synchronize()
+            s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+            for t in range(1, 4):
+                if concurrent:
+                    with torch.cuda.stream(s1):
+                        sa.step(wa.hp(), ranges=[(0, wa.n_micro)])
+                    with torch.cuda.stream(s2):
+                        sb.step(wb.hp())
+                else:
+                    with torch.cuda.stream(s1):
+                        sa.step(wa.hp(), ranges=[(0, wa.n_micro)])
+                    s1.synchronize()
+                    with torch.cuda.stream(s1):
+                        sb.step(wb.hp())
+                    s1.synchronize()
+            torch.cuda.synchronize()
+            return _state(sa) + _state(sb)
+        finally:
+            sa.close()
+            sb.close()
+
+    ref = run(False)
+    for _ in range(2):
+        got = run(True)
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
