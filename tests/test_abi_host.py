@@ -10,8 +10,8 @@ import oracle
 from mixed_precision_zero_amd import binding as B
 from mixed_precision_zero_amd import workloads as W
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "z1.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "z1.h")
 
 
 def declared_functions():
@@ -277,3 +277,19 @@ def test_plan_kinds_cover_every_element_once(shapes, D, kind):
         for i in range(len(numel)):
             owned[i][s[i]:s[i] + l[i]] += 1
     assert all((o == 1).all() for o in owned)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the package without libz1.so cannot be
+    imported (ImportError naming the missing library)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "mixed_precision_zero_amd")
+    dst = tmp_path / "mixed_precision_zero_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "*.so.tmp", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import mixed_precision_zero_amd.binding"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libz1" in r.stderr
