@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 4
+#define Z1_ABI_VERSION 5
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -363,6 +363,48 @@ typedef struct z1_lr_schedule {
  * Errors: Z1_EINVAL for NULL, negative counts, unknown style, t < 0.
  * ------------------------------------------------------------------------ */
 z1_status z1_lr_at(const z1_lr_schedule *schedule, int64_t step, double *lr);
+
+/* ------------------------------------------------------------------------
+ * Per-step schedule for replayed steps.  z1_adamw_step bakes its step t and
+ * lr into the launch, so a captured graph would repeat one step.  A
+ * schedule holds, on the device, the binary64 constants z1_adamw_step would
+ * derive for each of n_steps consecutive steps t = hp->step, hp->step + 1,
+ * ... (lr from z1_lr_at(lr, t) when lr is not NULL, else hp->lr every step;
+ * beta1, beta2, eps, weight_decay and clip from hp), plus a device counter
+ * of the next row.  z1_adamw_step_scheduled applies the constants of that
+ * row and then advances the counter, both as kernels on the stream, so
+ * [accumulate, norm, z1_adamw_step_scheduled] captured once and replayed
+ * once per step trains with the schedule ("Nanotron Guide", config.yaml:
+ * warmup and decay of the learning rate).  Each replayed step stores the
+ * bits z1_adamw_step stores for the same t and lr.
+ *
+ * Ownership: the schedule owns its table (80 bytes per step) and counter;
+ * z1_schedule_destroy waits for the device and frees them.  A schedule
+ * steps one plan at a time (its counter is shared by every caller).
+ * z1_schedule_create errors: Z1_EINVAL (NULL, a hyperparameter z1_adamw_step
+ * would reject, n_steps outside [1, Z1_SCHEDULE_MAX_STEPS], a bad lr
+ * schedule), Z1_ENOMEM, Z1_EHIP; it waits for its upload on `stream`.
+ * ------------------------------------------------------------------------ */
+#define Z1_SCHEDULE_MAX_STEPS (1LL << 24)
+typedef struct z1_schedule z1_schedule;
+z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
+                             const z1_lr_schedule *lr, int64_t n_steps, z1_stream stream);
+z1_status z1_schedule_destroy(z1_schedule *schedule);
+
+/* The step the next scheduled launch applies (t of its row) and how many
+ * scheduled launches found the table exhausted (those changed nothing).
+ * A blocking copy of the device counter: synchronise the stream the
+ * scheduled steps were enqueued on first.  Either output may be NULL.
+ * Errors: Z1_EINVAL, Z1_EHIP. */
+z1_status z1_schedule_query(const z1_schedule *schedule, int64_t *next_step, int64_t *overrun);
+
+/* z1_adamw_step with the constants of the schedule's current row; then the
+ * row advances.  With the table exhausted nothing is updated and the
+ * overrun count grows.  d_S_global and call order as z1_adamw_step (the
+ * order is checked when the call is made, not when a graph is replayed).
+ * Errors: Z1_EINVAL, Z1_EALIGN, Z1_ESTATE, Z1_EHIP. */
+z1_status z1_adamw_step_scheduled(z1_plan *plan, z1_schedule *schedule,
+                                  const double *d_S_global, z1_stream stream);
 
 /* ------------------------------------------------------------------------
  * z1_grad_norm_sq_acc -- S from an acc arena the caller filled itself.

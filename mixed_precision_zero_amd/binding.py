@@ -30,7 +30,8 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_accum_grads", "z1_grad_norm_sq", "z1_adamw_step", "z1_lr_at", "z1_probe_copy",
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
            "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range",
-           "z1_probe_plan")
+           "z1_probe_plan", "z1_schedule_create", "z1_schedule_destroy", "z1_schedule_query",
+           "z1_adamw_step_scheduled")
 
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
@@ -120,6 +121,11 @@ def _load():
         "z1_pack_accum_range": ([P, I32, I32, P], ctypes.c_int),
         "z1_probe": ([I32, ctypes.POINTER(P), I32, I64, P], ctypes.c_int),
         "z1_probe_plan": ([P, I32, P], ctypes.c_int),
+        "z1_schedule_create": ([ctypes.POINTER(P), ctypes.POINTER(AdamWHP),
+                                ctypes.POINTER(LRSchedule), I64, P], ctypes.c_int),
+        "z1_schedule_destroy": ([P], ctypes.c_int),
+        "z1_schedule_query": ([P, PI64, PI64], ctypes.c_int),
+        "z1_adamw_step_scheduled": ([P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -296,6 +302,56 @@ def z1_adamw_step(plan: Plan, *, lr, beta1, beta2, eps, weight_decay, clip, step
     hp = AdamWHP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
     _check(lib.z1_adamw_step(plan.handle, ctypes.byref(hp), _dptr(d_S), _stream(stream)),
            "z1_adamw_step")
+
+
+class Schedule:
+    """Owner of a z1_schedule handle (destroyed with z1_schedule_destroy)."""
+
+    def __init__(self, handle: int, n_steps: int):
+        self.handle = handle
+        self.n_steps = n_steps
+
+    def close(self):
+        if self.handle:
+            _check(lib.z1_schedule_destroy(self.handle), "z1_schedule_destroy")
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def z1_schedule_create(*, lr, beta1, beta2, eps, weight_decay, clip, step, n_steps: int,
+                       lr_schedule: Optional[dict] = None, stream=None) -> Schedule:
+    """Per-step constants for steps step .. step + n_steps - 1; lr_schedule is
+    a dict of z1_lr_at's keywords (None: lr every step)."""
+    hp = AdamWHP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
+    sc = None
+    if lr_schedule is not None:
+        d = dict(lr_schedule)
+        sc = LRSchedule(d["lr_max"], d["lr_min"], d["warmup_steps"], d["decay_steps"],
+                        DECAY_STYLES[d.get("decay_style", "cosine")], 0)
+    h = ctypes.c_void_p()
+    _check(lib.z1_schedule_create(ctypes.byref(h), ctypes.byref(hp),
+                                  ctypes.byref(sc) if sc is not None else None, int(n_steps),
+                                  _stream(stream)), "z1_schedule_create")
+    return Schedule(h.value, int(n_steps))
+
+
+def z1_schedule_query(sched: Schedule):
+    """(next step, overrun count); synchronise the stream that ran the steps first."""
+    t = ctypes.c_int64()
+    o = ctypes.c_int64()
+    _check(lib.z1_schedule_query(sched.handle, ctypes.byref(t), ctypes.byref(o)),
+           "z1_schedule_query")
+    return t.value, o.value
+
+
+def z1_adamw_step_scheduled(plan: Plan, sched: Schedule, d_S=None, stream=None) -> None:
+    _check(lib.z1_adamw_step_scheduled(plan.handle, sched.handle, _dptr(d_S), _stream(stream)),
+           "z1_adamw_step_scheduled")
 
 
 def z1_grad_norm_sq_acc(plan: Plan, d_S, stream=None) -> None:

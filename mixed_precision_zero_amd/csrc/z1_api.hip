@@ -37,6 +37,13 @@ struct z1_plan {
     bool norm_done = false;
 };
 
+struct z1_schedule {
+    int64_t t_first = 1, n_steps = 0;
+    bool clipping = false;
+    AdamConsts *d_table = nullptr;  // [n_steps] constants of steps t_first ...
+    int64_t *d_state = nullptr;     // [0] next row, [1] scheduled steps asked for past the end
+};
+
 struct z1_pack {
     int32_t n = 0, K = 0, dp = 0;
     int64_t seg = 0, n_chunks = 0;
@@ -139,6 +146,32 @@ void interleave_chunks(std::vector<Chunk> &chunks)
 }
 
 int64_t chunk_or_default(int64_t c) { return c ? c : z1::kDefaultChunk; }
+
+bool hp_ok(const z1_adamw_hp *hp)
+{
+    return isfinite(hp->lr) && hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 &&
+           hp->beta2 < 1.0 && hp->eps > 0.0 && isfinite(hp->eps) && hp->weight_decay >= 0.0 &&
+           isfinite(hp->weight_decay) && !isnan(hp->clip) && hp->step >= 1;
+}
+
+// The binary64 constants of one step, derived on the host (bias corrections
+// from libm pow, as the oracle derives them).
+AdamConsts consts_of(const z1_adamw_hp *hp)
+{
+    AdamConsts k;
+    const double t = (double)hp->step;
+    k.lr = hp->lr;
+    k.beta1 = hp->beta1;
+    k.beta2 = hp->beta2;
+    k.omb1 = 1.0 - hp->beta1;
+    k.omb2 = 1.0 - hp->beta2;
+    k.eps = hp->eps;
+    k.weight_decay = hp->weight_decay;
+    k.bc1 = 1.0 - pow(hp->beta1, t);
+    k.bc2 = 1.0 - pow(hp->beta2, t);
+    k.clip = hp->clip > 0.0 ? hp->clip : 0.0;
+    return k;
+}
 bool chunk_ok(int64_t c) { return c >= 1024 && c <= z1::kMaxChunk && c % 1024 == 0; }
 
 }  // namespace
@@ -555,12 +588,7 @@ z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
 z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_global,
                         z1_stream stream)
 {
-    if (!p || !hp)
-        return Z1_EINVAL;
-    if (!isfinite(hp->lr) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
-        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) || !isfinite(hp->eps) ||
-        !(hp->weight_decay >= 0.0) || !isfinite(hp->weight_decay) || isnan(hp->clip) ||
-        hp->step < 1)
+    if (!p || !hp || !hp_ok(hp))
         return Z1_EINVAL;
     const bool clipping = hp->clip > 0.0;
     if (clipping && !d_S_global)
@@ -570,18 +598,7 @@ z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_glo
     if (!p->acc_complete || (clipping && !p->norm_done))
         return Z1_ESTATE;
 
-    AdamConsts k;
-    const double t = (double)hp->step;
-    k.lr = hp->lr;
-    k.beta1 = hp->beta1;
-    k.beta2 = hp->beta2;
-    k.omb1 = 1.0 - hp->beta1;
-    k.omb2 = 1.0 - hp->beta2;
-    k.eps = hp->eps;
-    k.weight_decay = hp->weight_decay;
-    k.bc1 = 1.0 - pow(hp->beta1, t);
-    k.bc2 = 1.0 - pow(hp->beta2, t);
-    k.clip = clipping ? hp->clip : 0.0;
+    const AdamConsts k = consts_of(hp);
     hipError_t e = z1::launch_adamw(geom(p), p->d_weights, p->d_scales, p->acc, p->master,
                                     p->exp_avg, p->exp_avg_sq, k, d_S_global,
                                     reinterpret_cast<hipStream_t>(stream));
@@ -773,6 +790,109 @@ z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_str
     }
     p->next_k = k_end == p->K ? 0 : k_end;
     return Z1_OK;
+}
+
+z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
+                             const z1_lr_schedule *lr, int64_t n_steps, z1_stream stream)
+{
+    if (!out)
+        return Z1_EINVAL;
+    *out = nullptr;
+    if (!hp || !hp_ok(hp) || n_steps < 1 || n_steps > Z1_SCHEDULE_MAX_STEPS ||
+        hp->step > INT64_MAX - n_steps)
+        return Z1_EINVAL;
+    std::vector<AdamConsts> table((size_t)n_steps);
+    for (int64_t j = 0; j < n_steps; ++j) {
+        z1_adamw_hp h = *hp;
+        h.step = hp->step + j;
+        if (lr) {
+            const z1_status st = z1_lr_at(lr, h.step, &h.lr);
+            if (st != Z1_OK)
+                return st;
+            if (!isfinite(h.lr))
+                return Z1_EINVAL;
+        }
+        table[(size_t)j] = consts_of(&h);
+    }
+    z1_schedule *sc = new (std::nothrow) z1_schedule();
+    if (!sc)
+        return Z1_ENOMEM;
+    sc->t_first = hp->step;
+    sc->n_steps = n_steps;
+    sc->clipping = hp->clip > 0.0;
+    auto fail = [&](z1_status st) {
+        if (sc->d_table)
+            (void)hipFree(sc->d_table);
+        if (sc->d_state)
+            (void)hipFree(sc->d_state);
+        delete sc;
+        return st;
+    };
+    z1_status st;
+    if ((st = device_alloc(&sc->d_table, table.size())) != Z1_OK ||
+        (st = device_alloc(&sc->d_state, 2)) != Z1_OK)
+        return fail(st);
+    const int64_t zero[2] = {0, 0};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(sc->d_table, table.data(), table.size() * sizeof(AdamConsts),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(sc->d_state, zero, sizeof zero, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);  // the host table dies with this call
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(Z1_EHIP);
+    }
+    *out = sc;
+    return Z1_OK;
+}
+
+z1_status z1_schedule_destroy(z1_schedule *sc)
+{
+    if (!sc)
+        return Z1_OK;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(sc->d_table);
+    (void)hipFree(sc->d_state);
+    delete sc;
+    return Z1_OK;
+}
+
+z1_status z1_schedule_query(const z1_schedule *sc, int64_t *next_step, int64_t *overrun)
+{
+    if (!sc)
+        return Z1_EINVAL;
+    int64_t st[2] = {0, 0};
+    if (hipMemcpy(st, sc->d_state, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return Z1_EHIP;
+    }
+    if (next_step)
+        *next_step = sc->t_first + st[0];
+    if (overrun)
+        *overrun = st[1];
+    return Z1_OK;
+}
+
+z1_status z1_adamw_step_scheduled(z1_plan *p, z1_schedule *sc, const double *d_S_global,
+                                  z1_stream stream)
+{
+    if (!p || !sc)
+        return Z1_EINVAL;
+    if (sc->clipping && !d_S_global)
+        return Z1_EINVAL;
+    if (d_S_global && !aligned(d_S_global, 8))
+        return Z1_EALIGN;
+    if (!p->acc_complete || (sc->clipping && !p->norm_done))
+        return Z1_ESTATE;
+    const hipError_t e = z1::launch_adamw_scheduled(
+        geom(p), p->d_weights, p->d_scales, p->acc, p->master, p->exp_avg, p->exp_avg_sq,
+        sc->d_table, sc->n_steps, sc->d_state, d_S_global, reinterpret_cast<hipStream_t>(stream));
+    p->next_k = 0;
+    p->acc_complete = false;
+    p->norm_done = false;
+    return e == hipSuccess ? Z1_OK : Z1_EHIP;
 }
 
 z1_status z1_probe_plan(z1_plan *p, int32_t kind, z1_stream stream)

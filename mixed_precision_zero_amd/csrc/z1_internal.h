@@ -76,6 +76,12 @@ hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                         const float *acc, float *master, float *m, float *v,
                         const AdamConsts &k, const double *S, hipStream_t s);
+// k_adamw with the constants of row state[0] of a per-step table (skipped when
+// the table is exhausted), then one thread advances state (row or overrun)
+hipError_t launch_adamw_scheduled(const LaunchGeom &geo, uint16_t *const *weight_tab,
+                                  const Scale *scales, const float *acc, float *master, float *m,
+                                  float *v, const AdamConsts *table, int64_t n_rows,
+                                  int64_t *state, const double *S, hipStream_t s);
 // k_adamw's loads and stores over the same plan with no arithmetic (measurement)
 hipError_t launch_adamw_traffic(const LaunchGeom &geo, uint16_t *const *weight_tab,
                                 const float *acc, float *master, float *m, float *v,

@@ -562,7 +562,10 @@ __device__ __forceinline__ void traffic_vec(f32x4 a, f32x4 &p, f32x4 &m, f32x4 &
 // MATH = false is a measurement twin: the same chunk walk, loads and stores
 // over the same buffers, with the arithmetic replaced by traffic_vec, so the
 // cost of the update itself can be read off on the step's own buffers.
-template <int U, bool MATH>
+// TABLE = true takes the step's constants from row state[0] of a per-step
+// table instead of the kernel argument (a replayed graph then advances from
+// step to step); when the table is exhausted the whole grid returns at once.
+template <int U, bool MATH, bool TABLE>
 __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chunks,
                                                   int64_t n_chunks,
                                                   uint16_t *const *__restrict__ wtab,
@@ -571,9 +574,19 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
                                                   float *__restrict__ master,
                                                   float *__restrict__ exp_avg,
                                                   float *__restrict__ exp_avg_sq,
-                                                  const AdamConsts k,
-                                                  const double *__restrict__ S)
+                                                  const AdamConsts k_arg,
+                                                  const double *__restrict__ S,
+                                                  const AdamConsts *__restrict__ table,
+                                                  int64_t n_rows,
+                                                  const int64_t *__restrict__ state)
 {
+    AdamConsts k = k_arg;
+    if constexpr (TABLE) {
+        const int64_t row = state[0];
+        if (row >= n_rows)
+            return;
+        k = table[row];
+    }
     double c = 1.0;
     if (MATH && k.clip > 0.0) {
         const double cc = k.clip / (sqrt(S[0]) + 1e-6);
@@ -648,6 +661,20 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chun
                 w[e] = (uint16_t)(__float_as_uint(x) >> 16);
             }
         });
+    }
+}
+
+// Runs after the scheduled AdamW launch on the same stream: the next replay
+// takes the next row; a step asked for past the last row is counted.
+__global__ __launch_bounds__(64) void k_schedule_advance(int64_t *__restrict__ state,
+                                                         int64_t n_rows)
+{
+    if (threadIdx.x == 0) {
+        const int64_t row = state[0];
+        if (row < n_rows)
+            state[0] = row + 1;
+        else
+            state[1] = state[1] + 1;
     }
 }
 
@@ -800,8 +827,22 @@ hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, cons
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
-    k_adamw<Z1_UNROLL_ADAM, true><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
-        geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, k, S);
+    k_adamw<Z1_UNROLL_ADAM, true, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
+        geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, k, S, nullptr, 0,
+        nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw_scheduled(const LaunchGeom &geo, uint16_t *const *weight_tab,
+                                  const Scale *scales, const float *acc, float *master, float *m,
+                                  float *v, const AdamConsts *table, int64_t n_rows,
+                                  int64_t *state, const double *S, hipStream_t s)
+{
+    if (geo.n_chunks > 0)
+        k_adamw<Z1_UNROLL_ADAM, true, true><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
+            geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, AdamConsts{}, S,
+            table, n_rows, state);
+    k_schedule_advance<<<dim3(1), dim3(64), 0, s>>>(state, n_rows);
     return hipGetLastError();
 }
 
@@ -811,8 +852,9 @@ hipError_t launch_adamw_traffic(const LaunchGeom &geo, uint16_t *const *weight_t
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
-    k_adamw<Z1_UNROLL_ADAM, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
-        geo.chunks, geo.n_chunks, weight_tab, nullptr, acc, master, m, v, AdamConsts{}, nullptr);
+    k_adamw<Z1_UNROLL_ADAM, false, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
+        geo.chunks, geo.n_chunks, weight_tab, nullptr, acc, master, m, v, AdamConsts{}, nullptr,
+        nullptr, 0, nullptr);
     return hipGetLastError();
 }
 

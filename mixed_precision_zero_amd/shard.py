@@ -115,6 +115,11 @@ class ShardStep:
         B.z1_adamw_step(self.plan, d_S=self.d_S, step=t, stream=stream, **hp)
         self.t = t
 
+    def adamw_scheduled(self, sched, stream=None) -> None:
+        """AdamW with the constants of the schedule's current row (the row
+        then advances on the device)."""
+        B.z1_adamw_step_scheduled(self.plan, sched, d_S=self.d_S, stream=stream)
+
     def step(self, hp: dict, stream=None, ranges=None) -> None:
         """One optimizer step.  ranges=None accumulates one micro-batch per
         call; otherwise a list of (k_begin, k_end) covering 0..K in order, one

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 4
+    assert B.z1_abi_version() == 5
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -144,6 +144,9 @@ def test_null_plan_calls():
     assert L.z1_accum_grads_range(None, 0, 1, None) == B.Z1_EINVAL
     assert L.z1_pack_accum_range(None, 0, 1, None) == B.Z1_EINVAL
     assert L.z1_probe_plan(None, 0, None) == B.Z1_EINVAL
+    assert L.z1_adamw_step_scheduled(None, None, None, None) == B.Z1_EINVAL
+    assert L.z1_schedule_query(None, None, None) == B.Z1_EINVAL
+    assert L.z1_schedule_destroy(None) == B.Z1_OK
     assert L.z1_grad_norm_sq(None, None, None) == B.Z1_EINVAL
     hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
     assert L.z1_adamw_step(None, ctypes.byref(hp), None, None) == B.Z1_EINVAL
@@ -161,6 +164,25 @@ def test_null_plan_calls():
     odd = (ctypes.c_void_p * 2)(0x1008, 0x2000)
     assert L.z1_probe(0, odd, 2, 16, None) == B.Z1_EALIGN
     assert L.z1_probe(1, bufs, 1, 0, None) == B.Z1_OK              # nothing to do
+
+
+@pytest.mark.parametrize("over,n_steps", [
+    (dict(), 0), (dict(), -3), (dict(), (1 << 24) + 1), (dict(step=0), 4),
+    (dict(beta1=1.0), 4), (dict(eps=0.0), 4), (dict(lr=float("nan")), 4),
+    (dict(weight_decay=-0.1), 4), (dict(clip=float("nan")), 4),
+])
+def test_schedule_create_rejects_before_device_work(over, n_steps):
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, clip=1.0, step=1)
+    hp.update(over)
+    h = ctypes.c_void_p(1)
+    a = B.AdamWHP(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["clip"],
+                  hp["step"])
+    assert B.lib.z1_schedule_create(ctypes.byref(h), ctypes.byref(a), None, n_steps,
+                                    None) == B.Z1_EINVAL
+    assert h.value is None
+    bad_lr = B.LRSchedule(1e-3, 1e-4, -1, 10, 2, 0)         # negative warmup
+    assert B.lib.z1_schedule_create(ctypes.byref(h), ctypes.byref(B.AdamWHP(
+        1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)), ctypes.byref(bad_lr), 4, None) == B.Z1_EINVAL
 
 
 @pytest.mark.parametrize("kind", ["flat", "dim0"])

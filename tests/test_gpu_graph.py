@@ -78,3 +78,70 @@ def test_step_graph_replays_bitexact(w, resident):
         del g
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("w", [W.TINY, RAGGED_SMALL], ids=lambda w: w.name)
+def test_scheduled_step_captured_once_trains_over_steps(w):
+    """[accumulate all slots, norm, z1_adamw_step_scheduled] captured once and
+    replayed for 6 steps of a warmup + cosine learning-rate schedule, with
+    fresh gradients written between replays: every replay stores the bits of
+    the eager step with that step's t and z1_lr_at(t).  A 7th replay finds
+    the table exhausted: master, m, v and the weights stay as they were."""
+    from mixed_precision_zero_amd import binding as B
+    from mixed_precision_zero_amd.shard import ShardStep
+    dev = torch.device("cuda")
+    T = 6
+    lr_sched = dict(lr_max=w.lr, lr_min=w.lr / 10, warmup_steps=2, decay_steps=3,
+                    decay_style="cosine")
+    hp = w.hp()
+    gs = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev)
+    es = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev)
+    sched = None
+    try:
+        master = W.make_master(w, seed=0, device=dev)
+        for st in (gs, es):
+            st.scatter_to_arena(st.master, master)
+            st.load_weights(master)
+        sched = B.z1_schedule_create(**hp, step=1, n_steps=T, lr_schedule=lr_sched)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gs.accumulate_range(0, w.n_micro)
+            gs.norm()
+            gs.adamw_scheduled(sched)
+        torch.cuda.synchronize()
+        assert B.z1_schedule_query(sched) == (1, 0)
+
+        def state(st):
+            return [st.master.view(torch.int32).clone(), st.exp_avg.view(torch.int32).clone(),
+                    st.exp_avg_sq.view(torch.int32).clone(), st.acc.view(torch.int32).clone(),
+                    st.packed_weights().view(torch.int16).clone(), st.d_S.clone()]
+
+        for t in range(1, T + 2):
+            for k in range(w.n_micro):
+                W.make_micro_grads(w, t, k, seed=0, device=dev, out=gs.grads[k])
+                for a, b in zip(es.grads[k], gs.grads[k]):
+                    a.copy_(b)
+            torch.cuda.synchronize()
+            before = state(gs)
+            g.replay()
+            torch.cuda.synchronize()
+            if t <= T:
+                es.accumulate_range(0, w.n_micro)
+                es.norm()
+                lr_t = B.z1_lr_at(t, **lr_sched)
+                B.z1_adamw_step(es.plan, **{**hp, "lr": lr_t}, step=t, d_S=es.d_S)
+                torch.cuda.synchronize()
+                for i, (a, b) in enumerate(zip(state(gs), state(es))):
+                    assert torch.equal(a, b), f"step {t}: buffer {i} differs from the eager step"
+                assert B.z1_schedule_query(sched) == (t + 1, 0)
+            else:
+                after = state(gs)
+                for i in (0, 1, 2, 4):          # master, m, v, weights untouched
+                    assert torch.equal(after[i], before[i]), f"exhausted table changed buffer {i}"
+                assert B.z1_schedule_query(sched) == (T + 1, 1)
+        del g
+    finally:
+        if sched is not None:
+            sched.close()
+        gs.close()
+        es.close()
