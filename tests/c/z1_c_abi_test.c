@@ -157,13 +157,20 @@ int main(void)
     z1_plan *plan_packed = NULL;
     CHECK_Z1(z1_plan_create(&plan_packed, &bp, NULL));
 
+    /* step 4 runs through a one-row schedule (device constants for t = 4) */
+    z1_schedule *sched = NULL;
+    {
+        z1_adamw_hp h4 = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 4};
+        CHECK_Z1(z1_schedule_create(&sched, &h4, NULL, 1, NULL));
+    }
+
     /* step 1: one accumulation call per micro-batch; step 2: all K resident
-     * slots in one z1_accum_grads_range call; step 3: the packed layout.
-     * Each must match the oracle. */
+     * slots in one z1_accum_grads_range call; step 3: the packed layout;
+     * step 4: the scheduled AdamW.  Each must match the oracle. */
     int bad = 0;
     double S = 0.0, S_gpu = 0.0, c = 0.0;
     float *back = malloc(arena * 4);
-    for (int t = 1; t <= 3; ++t) {
+    for (int t = 1; t <= 4; ++t) {
         z1_adamw_hp hp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
         z1_plan *pl = t == 3 ? plan_packed : plan;
         if (t == 1) {
@@ -173,7 +180,10 @@ int main(void)
             CHECK_Z1(z1_accum_grads_range(pl, 0, K, NULL));
         }
         CHECK_Z1(z1_grad_norm_sq(pl, d_S, NULL));
-        CHECK_Z1(z1_adamw_step(pl, &hp, d_S, NULL));
+        if (t == 4)
+            CHECK_Z1(z1_adamw_step_scheduled(pl, sched, d_S, NULL));
+        else
+            CHECK_Z1(z1_adamw_step(pl, &hp, d_S, NULL));
         CHECK_HIP(hipDeviceSynchronize());
 
         z1o_hp ohp = {1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, t};
@@ -204,7 +214,7 @@ int main(void)
                 canaries += packed_host[e] == 0x5A5A;
             bad += canaries != arena - used; /* padding: untouched */
         }
-        for (int i = 0; i < NT && t < 3; ++i) {
+        for (int i = 0; i < NT && t != 3; ++i) {
             uint16_t *full = malloc(numel[i] * 2 + 2);
             CHECK_HIP(hipMemcpy(full, w[i], numel[i] * 2, hipMemcpyDeviceToHost));
             bad += memcmp(full + start[i], hw + pos, len[i] * 2) != 0;
@@ -215,11 +225,19 @@ int main(void)
             free(full);
         }
         printf("C ABI step %d (%s): L=%lld S=%.17g (oracle %.17g) c=%.6g bad=%d\n", t,
-               t == 1 ? "z1_accum_grads per micro-batch"
-                      : (t == 2 ? "z1_accum_grads_range" : "packed layout, range"),
+               t == 1   ? "z1_accum_grads per micro-batch"
+               : t == 2 ? "z1_accum_grads_range"
+               : t == 3 ? "packed layout, range"
+                        : "scheduled AdamW",
                (long long)L, S_gpu, S, c, bad);
     }
     free(back);
+    int64_t next_step = 0, overrun = -1;
+    CHECK_Z1(z1_schedule_query(sched, &next_step, &overrun));
+    bad += next_step != 5 || overrun != 0;
+    printf("C ABI schedule: next step %lld, overrun %lld\n", (long long)next_step,
+           (long long)overrun);
+    CHECK_Z1(z1_schedule_destroy(sched));
     CHECK_Z1(z1_plan_destroy(plan));
     CHECK_Z1(z1_plan_destroy(plan_packed));
     printf("C ABI: %s\n", bad ? "MISMATCH" : "bit-exact");

@@ -1,7 +1,8 @@
 """The C ABI driven from plain C (tests/c/z1_c_abi_test.c, built by
-__graft_entry__.build()): two steps, one with an accumulation call per
-micro-batch and one with all slots in one z1_accum_grads_range call, each
-bit-exact against the oracle."""
+__graft_entry__.build()): four steps -- an accumulation call per
+micro-batch, all slots in one z1_accum_grads_range call, a packed-layout
+plan, and AdamW through a one-row schedule -- each bit-exact against the
+oracle."""
 import os
 import subprocess
 
