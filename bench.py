@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--layout", default="full", choices=["full", "packed"],
                     help="bf16 weights and gradients as full-size tensors (default) or as "
                          "packed shards in arena order")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps replayed from one captured HIP graph (z1_adamw_step_scheduled), "
+                         "reported beside the eager headline; 0 = skip")
     ap.add_argument("--mode", default="step", choices=["step", "pack"],
                     help="step: the shard step (default); pack: full-tensor accumulation into "
                          "the reduce-scatter send buffer, every element of the model")
@@ -234,6 +237,38 @@ def main():
     if alt is not None:
         variants["slot" if head_resident else "resident"] = variant(alt, not head_resident)
 
+    # the headline step captured once in a HIP graph (with a per-step schedule
+    # for t and lr) and replayed: same work, no host enqueue per step
+    graph = None
+    if args.graph_steps > 0:
+        t0 = (alt["t_next"] if alt is not None else r["t_next"])
+        warm = 2
+        sched = B.z1_schedule_create(**hp, step=t0, n_steps=warm + args.graph_steps)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            if head_resident:
+                st.accumulate_range(0, w.n_micro)
+            else:
+                for k in range(w.n_micro):
+                    st.accumulate(k)
+            st.norm()
+            st.adamw_scheduled(sched)
+        for _ in range(warm):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.graph_steps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        next_t, overrun = B.z1_schedule_query(sched)
+        gms = g0.elapsed_time(g1) / args.graph_steps
+        graph = {"steps": args.graph_steps, "ms_per_step": gms, "params_per_s": L / (gms / 1e3),
+                 "schedule_next_step": next_t, "schedule_overrun": overrun}
+        del gr
+        sched.close()
+
     value = L / (ms_step / 1e3)
     adam_bytes = BYTES_ADAMW * L
     achieved = adam_bytes / (adam_avg / 1e3) / 1e9
@@ -338,6 +373,7 @@ def main():
         "kernels_ms": {"accum_all_K": accum_ms, "norm_fin": float(norm_ms.mean()),
                        "adamw": adam_avg, "adamw_median": float(np.median(adam_ms))},
         "accum_variants": variants,
+        "graph_replay": graph,
         "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
         "step_bytes_per_param": h3_bytes // L if L else None,
         "optimizer_step_params_per_s": L / ((adam_avg + float(norm_ms.mean())) / 1e3),
