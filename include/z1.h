@@ -33,14 +33,18 @@
  *     frees or reallocates caller memory.
  *   - The library owns only what z1_plan_create allocates (the chunk table,
  *     pointer tables and norm partials) and frees it in z1_plan_destroy.
- *     z1_accum_grads(_range), z1_grad_norm_sq and z1_adamw_step allocate
- *     nothing.
+ *     z1_accum_grads(_range), z1_grad_norm_sq, z1_adamw_step and
+ *     z1_adamw_step_scheduled allocate nothing (z1_schedule_create owns its
+ *     table until z1_schedule_destroy).
  *   - Work is enqueued on the given stream and the calls return without
  *     waiting for it; none of the step calls synchronises with the host.
  *     A kernel fault surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before anything is enqueued: a
  *     call that returns Z1_EINVAL, Z1_EALIGN or Z1_ESTATE has enqueued no
  *     work.  Z1_EHIP means a launch failed (see each call).
+ *   - A plan (or schedule, or pack) belongs to the GPU that is current when
+ *     it is created; its calls take a stream of that GPU, with that GPU
+ *     current.
  *   - A plan is used from one host thread and one stream at a time.
  *   - No C++ exception crosses this interface.
  */
