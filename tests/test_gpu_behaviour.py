@@ -311,3 +311,36 @@ def test_two_plans_on_two_streams_are_independent():
         got = run(True)
         for a, b in zip(got, ref):
             assert np.array_equal(a, b)
+
+
+def test_adamw_runs_at_the_memory_limit_of_its_buffers():
+    """Performance guard that does not depend on where the buffers land:
+    k_adamw must take no more than 15% longer than its no-arithmetic twin
+    (z1_probe_plan: the same chunk walk, loads and stores) on the same
+    buffers.  Measured ratios are 0.99-1.01; an update that became
+    compute-bound or a broken access pattern would fail this."""
+    w = dataclasses.replace(W.LLAMA_1P7B, n_micro=1)
+    st = _fresh(w)
+    try:
+        W.make_micro_grads(w, 1, 0, seed=0, device="cuda", out=st.grads[0])
+        stream = torch.cuda.current_stream()
+
+        def timed(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        step_ms, twin_ms = [], []
+        for t in range(1, 9):
+            st.accumulate(0)
+            st.norm()
+            step_ms.append(timed(lambda: st.adamw(w.hp(), step=t)))
+            twin_ms.append(timed(lambda: B.z1_probe_plan(st.plan)))
+        ratio = float(np.median(step_ms[2:])) / float(np.median(twin_ms[2:]))
+        print(f"k_adamw / twin = {ratio:.3f}")
+        assert ratio <= 1.15, f"k_adamw takes {ratio:.2f}x its no-arithmetic twin"
+    finally:
+        st.close()
