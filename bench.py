@@ -316,6 +316,19 @@ def main():
         twin_gbps = timed_gbps(lambda: B.z1_probe_plan(st.plan), BYTES_ADAMW * L)
     copy_gbps = ceilings["copy"] if ceilings else None
 
+    # GB/s of each timed piece: algorithmic bytes / mean time, as a fraction of
+    # the 8 TB/s peak and of the copy probe measured in this process
+    def rate(nbytes, ms):
+        gbps = nbytes / (ms / 1e3) / 1e9
+        return {"GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                "frac_of_copy": (gbps / copy_gbps) if copy_gbps else None}
+    acc_b = accum_bytes(w.n_micro, head_resident) * L
+    norm_avg = float(norm_ms.mean())
+    rates = {"accum_all_K": rate(acc_b, accum_ms),
+             "adamw": rate(BYTES_ADAMW * L, adam_avg),
+             "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg),
+             "H3_step": rate(acc_b + BYTES_ADAMW * L, ms_step)}
+
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
@@ -372,6 +385,7 @@ def main():
                      "vs_same_traffic_ceiling": (achieved / twin_gbps) if twin_gbps else None},
         "kernels_ms": {"accum_all_K": accum_ms, "norm_fin": float(norm_ms.mean()),
                        "adamw": adam_avg, "adamw_median": float(np.median(adam_ms))},
+        "rates": rates,
         "accum_variants": variants,
         "graph_replay": graph,
         "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
