@@ -229,11 +229,13 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
                    kind: str = "per_tensor", rows: Optional[Sequence[int]] = None,
                    lr_scale: Optional[Sequence[float]] = None,
                    wd_scale: Optional[Sequence[float]] = None,
-                   layout: str = "full") -> Plan:
+                   layout: str = "full", arena_elems: Optional[int] = None) -> Plan:
     """Bind device buffers, the four arenas fp32 of arena_elems.
     layout "full": weights[i] and grads[k][i] are full-size bf16 tensors (or
     raw device addresses).  layout "packed": weights is one packed bf16
-    shard and grads[k] one packed bf16 shard per micro-batch, in arena order."""
+    shard and grads[k] one packed bf16 shard per micro-batch, in arena order.
+    arena_elems defaults to the smallest arena tensor's length; pass it when
+    the arenas are raw device addresses."""
     n = _i64(numel)
     K = len(grads)
     if layout == "packed":
@@ -249,6 +251,8 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
         gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
     arena = [master, exp_avg, exp_avg_sq, acc]
     sizes = [a.numel() for a in arena if hasattr(a, "numel")]
+    if arena_elems is not None:
+        sizes = [int(arena_elems)]
     r = _i64(rows) if rows is not None else None
     ls = np.ascontiguousarray(np.asarray(lr_scale, np.float64)) if lr_scale is not None else None
     ws = np.ascontiguousarray(np.asarray(wd_scale, np.float64)) if wd_scale is not None else None
