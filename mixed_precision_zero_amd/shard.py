@@ -92,6 +92,19 @@ class ShardStep:
             for wt, x in zip(self.weights, full):
                 wt.copy_(x)
 
+    def load_weights_packed_order(self, packed: torch.Tensor) -> None:
+        """Inverse of packed_weights(): write this rank's slices of the bf16
+        weights from their concatenation."""
+        pos = 0
+        for i, s, ln, off in self.slices():
+            if not ln:
+                continue
+            if self.layout == "packed":
+                self.w_packed[off:off + ln].copy_(packed[pos:pos + ln])
+            else:
+                self.weights[i].view(-1)[s:s + ln].copy_(packed[pos:pos + ln])
+            pos += ln
+
     def packed_weights(self) -> torch.Tensor:
         if self.layout == "packed":
             return self.packed(self.w_packed)

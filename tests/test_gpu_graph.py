@@ -145,3 +145,65 @@ def test_scheduled_step_captured_once_trains_over_steps(w):
             sched.close()
         gs.close()
         es.close()
+
+
+def test_scheduled_step_graph_7b_matches_eager():
+    """The benchmarked form at full size: [all 4 slots, norm, scheduled AdamW]
+    captured once on the 7B shard and replayed for steps 1 and 2; each replay
+    stores the bits of the eager step taken from the same state."""
+    from mixed_precision_zero_amd import binding as B
+    from mixed_precision_zero_amd.shard import ShardStep
+    w = W.LLAMA_7B
+    dev = torch.device("cuda")
+    st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev)
+    sched = None
+    try:
+        master = W.make_master(w, seed=0, device=dev)
+        st.scatter_to_arena(st.master, master)
+        st.load_weights(master)
+        del master
+        hp = w.hp()
+        sched = B.z1_schedule_create(**hp, step=1, n_steps=2)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.accumulate_range(0, w.n_micro)
+            st.norm()
+            st.adamw_scheduled(sched)
+        torch.cuda.synchronize()
+
+        def snap():
+            return [st.master.clone(), st.exp_avg.clone(), st.exp_avg_sq.clone(),
+                    st.packed_weights().clone()]
+
+        def restore(s):
+            st.master.copy_(s[0])
+            st.exp_avg.copy_(s[1])
+            st.exp_avg_sq.copy_(s[2])
+            st.load_weights_packed_order(s[3])
+
+        state = snap()
+        for t in (1, 2):
+            for k in range(w.n_micro):
+                W.make_micro_grads(w, t, k, seed=0, device=dev, out=st.grads[k])
+            restore(state)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = snap() + [st.acc.clone(), st.d_S.clone()]
+            restore(state)
+            st.accumulate_range(0, w.n_micro)
+            st.norm()
+            st.adamw(hp, step=t)
+            torch.cuda.synchronize()
+            ref = snap() + [st.acc.clone(), st.d_S.clone()]
+            for i, (a, b) in enumerate(zip(got, ref)):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                    f"step {t}: buffer {i} differs between replay and eager"
+            state = ref[:4]
+            del got
+        assert B.z1_schedule_query(sched) == (3, 0)
+        del g
+    finally:
+        if sched is not None:
+            sched.close()
+        st.close()
