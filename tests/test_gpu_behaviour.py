@@ -344,3 +344,40 @@ def test_adamw_runs_at_the_memory_limit_of_its_buffers():
         assert ratio <= 1.15, f"k_adamw takes {ratio:.2f}x its no-arithmetic twin"
     finally:
         st.close()
+
+
+def test_bf16_cast_in_the_kernel_exhaustive():
+    """With lr = 0, weight decay 0, zero gradients and no clipping the update
+    leaves every master value as it is (p * 1 - 0), so one step writes
+    bf16_RNE(p) of arbitrary bit patterns through k_adamw's own cast.  All
+    2^32 fp32 patterns, in four 2^30-element steps: equal to torch's cast for
+    every non-NaN pattern (master unchanged too), a quiet NaN of the same sign
+    for every NaN."""
+    n = 1 << 30
+    st = ShardStep([(n,)], 1, 0, 1, device="cuda")
+    try:
+        hp = dict(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, clip=0.0)
+        st.grads[0][0].zero_()
+        bad = bad_nan = 0
+        for c in range(4):
+            bits = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda").to(torch.int32)
+            st.master.copy_(bits.view(torch.float32))
+            st.exp_avg.zero_()
+            st.exp_avg_sq.zero_()
+            st.accumulate(0)
+            st.adamw(hp, step=1)
+            torch.cuda.synchronize()
+            f = bits.view(torch.float32)
+            nan = torch.isnan(f)
+            ref = f.to(torch.bfloat16).view(torch.int16)
+            got = st.weights[0].view(torch.int16)
+            bad += int(((got != ref) & ~nan).sum())
+            bad += int(((st.master.view(torch.int32) != bits) & ~nan).sum())
+            h = got[nan].to(torch.int32) & 0xFFFF
+            sign = (bits[nan] >> 31) & 1
+            bad_nan += int((((h & 0x7FC0) != 0x7FC0) | ((h >> 15) != sign)).sum())
+            del bits, f, nan, ref, h, sign
+        assert bad == 0, f"{bad} patterns differ from torch's cast (or the master changed)"
+        assert bad_nan == 0, f"{bad_nan} NaN patterns did not give a quiet NaN of the same sign"
+    finally:
+        st.close()
