@@ -381,3 +381,35 @@ def test_bf16_cast_in_the_kernel_exhaustive():
         assert bad_nan == 0, f"{bad_nan} NaN patterns did not give a quiet NaN of the same sign"
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("resident", [False, True], ids=["per_call", "resident"])
+def test_accumulation_exhaustive_over_all_bf16_pairs(resident):
+    """acc = f32(g0) + f32(g1) for every pair of bf16 bit patterns (2^32
+    pairs, four 2^30-element passes): equal to torch's binary32 addition of
+    the two widened values for every non-NaN sum, NaN exactly where it is
+    NaN."""
+    n = 1 << 30
+    st = ShardStep([(n,)], 1, 0, 2, device="cuda")
+    try:
+        g0, g1 = st.grads[0][0], st.grads[1][0]
+        bad = 0
+        for c in range(4):
+            bits = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda")
+            g0.view(torch.int16).copy_((bits >> 16).to(torch.int16))
+            g1.view(torch.int16).copy_((bits & 0xFFFF).to(torch.int16))
+            del bits
+            if resident:
+                st.accumulate_range(0, 2)
+            else:
+                st.accumulate(0)
+                st.accumulate(1)
+            torch.cuda.synchronize()
+            ref = g0.float() + g1.float()
+            nan = torch.isnan(ref)
+            bad += int((torch.isnan(st.acc[:n]) != nan).sum())
+            bad += int(((st.acc[:n].view(torch.int32) != ref.view(torch.int32)) & ~nan).sum())
+            del ref, nan
+        assert bad == 0, f"{bad} bf16 pairs sum differently from torch's binary32 addition"
+    finally:
+        st.close()
