@@ -413,3 +413,63 @@ def test_accumulation_exhaustive_over_all_bf16_pairs(resident):
         assert bad == 0, f"{bad} bf16 pairs sum differently from torch's binary32 addition"
     finally:
         st.close()
+
+
+def _finite_patterns(rng, n, bits, nonneg_frac=None):
+    """Random bit patterns with every finite exponent (subnormals and zero
+    included), as uint32 (fp32) or uint16 (bf16)."""
+    if bits == 32:
+        u = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+        e = rng.integers(0, 255, size=n, dtype=np.uint32)
+        u = (u & np.uint32(0x807FFFFF)) | (e << np.uint32(23))
+        if nonneg_frac is not None:
+            neg = rng.random(n) >= nonneg_frac
+            u = np.where(neg, u | np.uint32(0x80000000), u & np.uint32(0x7FFFFFFF))
+        return u
+    u = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+    e = rng.integers(0, 255, size=n, dtype=np.uint16)
+    return (u & np.uint16(0x807F)) | (e << np.uint16(7))
+
+
+@pytest.mark.parametrize("clip,step", [(0.0, 1), (1.0, 7)])
+def test_adamw_wide_range_matches_oracle(clip, step):
+    """p, m, v and the gradient drawn over every finite fp32 / bf16 exponent
+    (subnormals, zero, near-overflow; 1% of v negative, so its square root is
+    NaN): one step on the GPU stores the oracle's bits for every element that
+    is not NaN, and NaN exactly where the oracle has NaN."""
+    import oracle
+    o = oracle.get()
+    n = 1 << 22
+    rng = np.random.default_rng(77 + step)
+    p = _finite_patterns(rng, n, 32).view(np.float32)
+    m = _finite_patterns(rng, n, 32).view(np.float32)
+    v = _finite_patterns(rng, n, 32, nonneg_frac=0.99).view(np.float32)
+    g = _finite_patterns(rng, n, 16)
+    st = ShardStep([(n,)], 1, 0, 1, device="cuda")
+    try:
+        st.master[:n].copy_(torch.from_numpy(p.copy()))
+        st.exp_avg[:n].copy_(torch.from_numpy(m.copy()))
+        st.exp_avg_sq[:n].copy_(torch.from_numpy(v.copy()))
+        st.grads[0][0].view(torch.int16).copy_(torch.from_numpy(g.view(np.int16).copy()))
+        hp = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, clip=clip)
+        st.accumulate(0)
+        st.norm()
+        st.adamw(hp, step=step)
+        torch.cuda.synchronize()
+        wb = np.zeros(n, np.uint16)
+        with np.errstate(all="ignore"):
+            S, c, _ = o.step(g.reshape(1, n), p, m, v, step=step, w=wb, **hp)
+        assert float(st.d_S.item()) == S
+        for name, gpu, ref in (("master", st.master, p), ("exp_avg", st.exp_avg, m),
+                               ("exp_avg_sq", st.exp_avg_sq, v)):
+            x = gpu[:n].cpu().numpy()
+            assert np.array_equal(np.isnan(x), np.isnan(ref)), f"{name}: NaN positions differ"
+            keep = ~np.isnan(ref)
+            assert np.array_equal(x[keep].view(np.uint32), ref[keep].view(np.uint32)), name
+        wg = st.weights[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(_bf16_nan(wg), _bf16_nan(wb))
+        keep = ~_bf16_nan(wb)
+        assert np.array_equal(wg[keep], wb[keep])
+        assert np.isnan(p).any()          # the negative-v elements took the NaN path
+    finally:
+        st.close()
