@@ -189,3 +189,46 @@ def test_pack_llama7b_sampled():
             got = send[r * seg + int(off[i]) + e].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (r, i)
     pack.close()
+
+
+@pytest.mark.parametrize("resident", [False, True], ids=["per_call", "resident"])
+def test_pack_divide_exhaustive_over_all_bf16_pairs(resident):
+    """send = (f32(g0) + f32(g1)) / 7 for every pair of bf16 patterns (2^32
+    pairs, four 2^30-element tensors), against the correctly rounded binary32
+    quotient: the binary32 sum divided in binary64 and rounded once to
+    binary32 (double rounding is harmless for one division, since 53 >= 2*24+2).
+    NaN exactly where the reference is NaN."""
+    n, D = 1 << 30, 7
+    g0 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    g1 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    seg = B.z1_pack_layout([n], D)
+    send = torch.empty(D * seg, dtype=torch.float32, device="cuda")
+    pack = B.z1_pack_create([n], D, [[g0], [g1]], send, divide=True)
+    try:
+        slices = []
+        for r in range(D):
+            s, ln, off, _ = B.z1_shard_plan([n], D, r)
+            slices.append((int(s[0]), int(ln[0]), r * seg + int(off[0])))
+        bad = 0
+        for c in range(4):
+            bits = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda")
+            g0.view(torch.int16).copy_((bits >> 16).to(torch.int16))
+            g1.view(torch.int16).copy_((bits & 0xFFFF).to(torch.int16))
+            del bits
+            if resident:
+                B.z1_pack_accum_range(pack, 0, 2)
+            else:
+                B.z1_pack_accum(pack, 0)
+                B.z1_pack_accum(pack, 1)
+            torch.cuda.synchronize()
+            ref = ((g0.float() + g1.float()).double() / D).float()
+            for s, ln, o in slices:
+                got = send[o:o + ln]
+                want = ref[s:s + ln]
+                nan = torch.isnan(want)
+                bad += int((torch.isnan(got) != nan).sum())
+                bad += int(((got.view(torch.int32) != want.view(torch.int32)) & ~nan).sum())
+            del ref
+        assert bad == 0, f"{bad} quotients differ from the correctly rounded binary32 value"
+    finally:
+        pack.close()
