@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 5
+#define Z1_ABI_VERSION 6
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -300,6 +300,28 @@ z1_status z1_accum_grads_range(z1_plan *plan, int32_t k_begin, int32_t k_end,
  * enqueued; Z1_EINVAL for NULL; Z1_EALIGN if d_S is not 8-byte aligned.
  * ------------------------------------------------------------------------ */
 z1_status z1_grad_norm_sq(z1_plan *plan, double *d_S, z1_stream stream);
+
+/* ------------------------------------------------------------------------
+ * The norm exchanged between ranks without rounding.  On D ranks the clip
+ * coefficient needs the global S = sum over ranks of S_r; adding rounded
+ * S_r values makes S depend on how it was split.  Instead each rank takes
+ * its S_r as the unevaluated pair (hi, lo) the reduction ends with:
+ *
+ * z1_grad_norm_sq_pair writes d_pair[0] = hi, d_pair[1] = lo (DEVICE, 16-byte
+ * aligned), S_r = hi + lo to about 2^-106 relative.  Same call order and
+ * errors as z1_grad_norm_sq; afterwards z1_adamw_step may follow.
+ *
+ * The ranks all-gather the D pairs (16 bytes each, rank order) and each one
+ * calls z1_norm_combine on the gathered [D][2] array (DEVICE, 16-byte
+ * aligned): the pairs are added in index order in the same double-double
+ * arithmetic and the sum is rounded once into d_S (DEVICE double).  Every
+ * rank then holds the same S, equal to what one rank holding the whole
+ * model computes unless the exact sum lies within about D * 2^-106 of a
+ * binary64 rounding boundary.  With D = 1 it equals z1_grad_norm_sq.
+ * Errors: Z1_EINVAL (NULL, n < 1), Z1_EALIGN, Z1_EHIP.
+ * ------------------------------------------------------------------------ */
+z1_status z1_grad_norm_sq_pair(z1_plan *plan, double *d_pair, z1_stream stream);
+z1_status z1_norm_combine(const double *d_pairs, int32_t n, double *d_S, z1_stream stream);
 
 /* AdamW hyperparameters of one step (binary64, passed by value to the
  * kernel; the library derives 1 - lr*wd, 1 - beta1, 1 - beta2 and the bias

@@ -31,7 +31,7 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
            "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range",
            "z1_probe_plan", "z1_schedule_create", "z1_schedule_destroy", "z1_schedule_query",
-           "z1_adamw_step_scheduled")
+           "z1_adamw_step_scheduled", "z1_grad_norm_sq_pair", "z1_norm_combine")
 
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
 
@@ -121,6 +121,8 @@ def _load():
         "z1_pack_accum_range": ([P, I32, I32, P], ctypes.c_int),
         "z1_probe": ([I32, ctypes.POINTER(P), I32, I64, P], ctypes.c_int),
         "z1_probe_plan": ([P, I32, P], ctypes.c_int),
+        "z1_grad_norm_sq_pair": ([P, P, P], ctypes.c_int),
+        "z1_norm_combine": ([P, I32, P, P], ctypes.c_int),
         "z1_schedule_create": ([ctypes.POINTER(P), ctypes.POINTER(AdamWHP),
                                 ctypes.POINTER(LRSchedule), I64, P], ctypes.c_int),
         "z1_schedule_destroy": ([P], ctypes.c_int),
@@ -299,6 +301,18 @@ def z1_accum_grads_range(plan: Plan, k_begin: int, k_end: int, stream=None) -> N
 def z1_grad_norm_sq(plan: Plan, d_S, stream=None) -> None:
     """Writes S into the device float64 tensor d_S (first element)."""
     _check(lib.z1_grad_norm_sq(plan.handle, _dptr(d_S), _stream(stream)), "z1_grad_norm_sq")
+
+
+def z1_grad_norm_sq_pair(plan: Plan, d_pair, stream=None) -> None:
+    """S of this rank as the pair (hi, lo) in the device float64 tensor d_pair[:2]."""
+    _check(lib.z1_grad_norm_sq_pair(plan.handle, _dptr(d_pair), _stream(stream)),
+           "z1_grad_norm_sq_pair")
+
+
+def z1_norm_combine(d_pairs, n: int, d_S, stream=None) -> None:
+    """S from n gathered pairs (device float64 [n, 2]) added in order, into d_S."""
+    _check(lib.z1_norm_combine(_dptr(d_pairs), int(n), _dptr(d_S), _stream(stream)),
+           "z1_norm_combine")
 
 
 def z1_adamw_step(plan: Plan, *, lr, beta1, beta2, eps, weight_decay, clip, step,

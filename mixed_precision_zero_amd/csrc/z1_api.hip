@@ -585,6 +585,34 @@ z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
     return Z1_OK;
 }
 
+z1_status z1_grad_norm_sq_pair(z1_plan *p, double *d_pair, z1_stream stream)
+{
+    if (!p || !d_pair)
+        return Z1_EINVAL;
+    if (!aligned(d_pair, 16))
+        return Z1_EALIGN;
+    if (!p->acc_complete)
+        return Z1_ESTATE;
+    if (z1::launch_norm_fin(p->d_partials, p->n_chunks, p->d_stage, p->d_counter, nullptr,
+                            reinterpret_cast<hipStream_t>(stream),
+                            reinterpret_cast<DD *>(d_pair)) != hipSuccess)
+        return Z1_EHIP;
+    p->norm_done = true;
+    return Z1_OK;
+}
+
+z1_status z1_norm_combine(const double *d_pairs, int32_t n, double *d_S, z1_stream stream)
+{
+    if (!d_pairs || !d_S || n < 1)
+        return Z1_EINVAL;
+    if (!aligned(d_pairs, 16) || !aligned(d_S, 8))
+        return Z1_EALIGN;
+    return z1::launch_norm_combine(reinterpret_cast<const DD *>(d_pairs), n, d_S,
+                                   reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? Z1_OK
+               : Z1_EHIP;
+}
+
 z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_global,
                         z1_stream stream)
 {

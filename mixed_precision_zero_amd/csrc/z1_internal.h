@@ -71,8 +71,12 @@ hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad
                               bool first, bool last, bool divide, float dp, hipStream_t s);
 // norm partials of an acc arena filled by the caller
 hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials, hipStream_t s);
+// S (when S != nullptr) and/or the unrounded pair (when pair != nullptr)
 hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
-                           unsigned int *counter, double *S, hipStream_t s);
+                           unsigned int *counter, double *S, hipStream_t s,
+                           DD *pair = nullptr);
+// S from n pairs added in index order
+hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_t s);
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                         const float *acc, float *master, float *m, float *v,
                         const AdamConsts &k, const double *S, hipStream_t s);

@@ -459,7 +459,8 @@ __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ c
 __global__ __launch_bounds__(kFinBlock) void k_norm_fin(const DD *__restrict__ partials,
                                                         int64_t n, DD *__restrict__ stage,
                                                         unsigned int *__restrict__ counter,
-                                                        double *__restrict__ S)
+                                                        double *__restrict__ S,
+                                                        DD *__restrict__ pair)
 {
     __shared__ DD lds[kFinBlock / 64];
     __shared__ bool is_last;
@@ -491,8 +492,24 @@ __global__ __launch_bounds__(kFinBlock) void k_norm_fin(const DD *__restrict__ p
     }
     block_reduce_dd<kFinBlock>(hi, lo, lds);
     if (threadIdx.x == 0) {
+        if (S)
+            S[0] = hi + lo;
+        if (pair)
+            pair[0] = DD{hi, lo};  // the unrounded pair, for an exchange between ranks
+        counter[0] = 0u;           // ready for the next launch on this plan
+    }
+}
+
+// S from n double-double pairs (one per rank), added in index order with the
+// same pair arithmetic, rounded once.
+__global__ __launch_bounds__(64) void k_norm_combine(const DD *__restrict__ pairs, int32_t n,
+                                                     double *__restrict__ S)
+{
+    if (threadIdx.x == 0) {
+        double hi = 0.0, lo = 0.0;
+        for (int32_t i = 0; i < n; ++i)
+            dd_add(hi, lo, pairs[i].hi, pairs[i].lo);
         S[0] = hi + lo;
-        counter[0] = 0u;  // ready for the next launch on this plan
     }
 }
 
@@ -808,7 +825,7 @@ hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials
 }
 
 hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
-                           unsigned int *counter, double *S, hipStream_t s)
+                           unsigned int *counter, double *S, hipStream_t s, DD *pair)
 {
     // about 8 partials per thread per stage-1 workgroup, at most kFinStages
     int64_t g = (n_chunks + 8 * kFinBlock - 1) / (8 * kFinBlock);
@@ -817,7 +834,13 @@ hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
     if (g > kFinStages)
         g = kFinStages;
     k_norm_fin<<<dim3((unsigned)g), dim3(kFinBlock), 0, s>>>(partials, n_chunks, stage, counter,
-                                                             S);
+                                                             S, pair);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_t s)
+{
+    k_norm_combine<<<dim3(1), dim3(64), 0, s>>>(pairs, n, S);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 5
+    assert B.z1_abi_version() == 6
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -147,6 +147,10 @@ def test_null_plan_calls():
     assert L.z1_adamw_step_scheduled(None, None, None, None) == B.Z1_EINVAL
     assert L.z1_schedule_query(None, None, None) == B.Z1_EINVAL
     assert L.z1_schedule_destroy(None) == B.Z1_OK
+    assert L.z1_grad_norm_sq_pair(None, None, None) == B.Z1_EINVAL
+    assert L.z1_norm_combine(None, 1, None, None) == B.Z1_EINVAL
+    assert L.z1_norm_combine(0x1000, 0, 0x2000, None) == B.Z1_EINVAL
+    assert L.z1_norm_combine(0x1008, 1, 0x2000, None) == B.Z1_EALIGN
     assert L.z1_grad_norm_sq(None, None, None) == B.Z1_EINVAL
     hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
     assert L.z1_adamw_step(None, ctypes.byref(hp), None, None) == B.Z1_EINVAL

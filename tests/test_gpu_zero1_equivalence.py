@@ -1,11 +1,12 @@
 """The ZeRO-1 identity on one GPU: the D ranks' shard steps, each on its own
-plan over the same full tensors and given the global S (what an exact
-all-reduce of S would deliver), reproduce the unsharded step (dp = 1) bit
-for bit.  Every rank's master, m and v equal the unsharded ones restricted
-to its slices, and the bf16 slices the ranks write in place form the full
-weights the all-gather would distribute.  Σ_r S_r equals the global S up
-to the rounding of each S_r ("Distributed Training", ZeRO-1: each rank
-keeps its slice of the optimizer state and the step is unchanged)."""
+plan over the same full tensors, reproduce the unsharded step (dp = 1) bit
+for bit ("Distributed Training", ZeRO-1: each rank keeps its slice of the
+optimizer state and the step is unchanged).  The ranks exchange their norm
+as unrounded pairs (z1_grad_norm_sq_pair; the [D][2] array stands in for
+the all-gather) and z1_norm_combine gives every rank the same S, equal to
+the unsharded S.  Every rank's master, m, v and acc equal the unsharded ones
+restricted to its slices, and the bf16 slices the ranks write in place form
+the full weights the all-gather would distribute."""
 import dataclasses
 
 import pytest
@@ -50,6 +51,11 @@ def test_ranks_compose_to_the_unsharded_step(w, kind):
                 assert s == pos
                 pos += ln
             assert pos == n
+        f64 = dict(dtype=torch.float64, device=dev)
+        pairs = torch.zeros(D, 2, **f64)      # row r: rank r's (hi, lo), 16-byte aligned
+        ref_pair = torch.zeros(2, **f64)
+        S_one = torch.zeros(1, **f64)
+        S_global = torch.zeros(1, **f64)
         master = W.make_master(w, seed=0, device=dev)
         for st in [ref] + ranks:
             st.scatter_to_arena(st.master, master)
@@ -58,17 +64,21 @@ def test_ranks_compose_to_the_unsharded_step(w, kind):
         for t in (1, 2, 3):
             for k in range(K):
                 W.make_micro_grads(w, t, k, seed=0, device=dev, out=grads[k])
-            ref.step(hp)
-            S_sum = torch.zeros(1, dtype=torch.float64, device=dev)
-            for st in ranks:
+            ref.accumulate_range(0, K)
+            B.z1_grad_norm_sq_pair(ref.plan, ref_pair)
+            B.z1_norm_combine(ref_pair, 1, S_one)
+            ref.norm()
+            ref.adamw(hp, step=t)
+            for r, st in enumerate(ranks):
                 st.accumulate_range(0, K)
-                st.norm()
-                S_sum += st.d_S
-                # every rank clips with the global S, as after an all-reduce
-                B.z1_adamw_step(st.plan, d_S=ref.d_S, step=t, **hp)
+                B.z1_grad_norm_sq_pair(st.plan, pairs[r])
+            B.z1_norm_combine(pairs, D, S_global)
+            for st in ranks:
+                B.z1_adamw_step(st.plan, d_S=S_global, step=t, **hp)
             torch.cuda.synchronize()
-            S_ref = float(ref.d_S.item())
-            assert abs(float(S_sum.item()) - S_ref) <= 1e-14 * S_ref
+            S_ref = ref.d_S.item()
+            assert S_one.item() == S_ref, "one pair combined differs from z1_grad_norm_sq"
+            assert S_global.item() == S_ref, (t, S_global.item(), S_ref)
         # the state after 3 steps, slice by slice
         for st in ranks:
             for i, s, ln, off in st.slices():
