@@ -180,6 +180,19 @@ int main(void)
             CHECK_Z1(z1_accum_grads_range(pl, 0, K, NULL));
         }
         CHECK_Z1(z1_grad_norm_sq(pl, d_S, NULL));
+        if (t == 2) {
+            /* the norm as an unrounded pair, combined over one rank: the same S */
+            double *d_pair = NULL, *d_S1 = NULL, S_a = 0.0, S_b = 1.0;
+            CHECK_HIP(hipMalloc((void **)&d_pair, 16));
+            CHECK_HIP(hipMalloc((void **)&d_S1, 8));
+            CHECK_Z1(z1_grad_norm_sq_pair(pl, d_pair, NULL));
+            CHECK_Z1(z1_norm_combine(d_pair, 1, d_S1, NULL));
+            CHECK_HIP(hipMemcpy(&S_a, d_S, 8, hipMemcpyDeviceToHost));
+            CHECK_HIP(hipMemcpy(&S_b, d_S1, 8, hipMemcpyDeviceToHost));
+            bad += memcmp(&S_a, &S_b, 8) != 0;
+            CHECK_HIP(hipFree(d_pair));
+            CHECK_HIP(hipFree(d_S1));
+        }
         if (t == 4)
             CHECK_Z1(z1_adamw_step_scheduled(pl, sched, d_S, NULL));
         else
