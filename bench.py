@@ -357,8 +357,13 @@ def main():
                "cpu_model": _cpu_model()}
 
     out = {
-        "metric": "optimizer-step params/s (7B shard, full step: K accumulations + norm + "
-                  "clipped AdamW + bf16 cast)",
+        "metric": ("optimizer-step params/s and achieved HBM GB/s (% of MI355X peak), 7B shard"
+                   if w.name == "llama7b" else
+                   f"optimizer-step params/s and achieved HBM GB/s (% of MI355X peak), "
+                   f"{w.name} shard"),
+        "metric_detail": "value = shard params / step time; the step is K accumulations + "
+                         "norm + clipped AdamW + bf16 cast; GB/s and % of peak are under "
+                         "roofline (dominant kernel) and rates (each part of the step)",
         "value": value,
         "unit": "params/s",
         "n_gpus": 1,
