@@ -272,9 +272,10 @@ z1_status z1_accum_grads(z1_plan *plan, int32_t k, z1_stream stream);
  * same order ("Distributed Training", §2: the gradients of the K micro-batches
  * are summed, one optimizer step after them).  It is for callers that hold
  * several micro-batch gradients in device memory at once (K full-size bf16
- * gradient sets, 2 bytes per parameter each): up to 8 slots are read in one
- * pass, so the fp32 acc arena is read and written once per 8 slots instead of
- * once per slot.  For K = 4 that is 12 bytes per shard element instead of 36.
+ * gradient sets, 2 bytes per parameter each): the range is split into
+ * passes of at most 8 slots, as even as possible (10 slots: two passes of 5),
+ * so the fp32 acc arena is read and written once per pass instead of once
+ * per slot.  For K = 4 that is 12 bytes per shard element instead of 36.
  * A range that ends at K also writes the norm partials, as the k == K-1 pass
  * of z1_accum_grads does.  A range may follow single-slot calls and be
  * followed by them.
