@@ -44,7 +44,11 @@
  *     work.  Z1_EHIP means a launch failed (see each call).
  *   - A plan (or schedule, or pack) belongs to the GPU that is current when
  *     it is created; its calls take a stream of that GPU, with that GPU
- *     current.
+ *     current.  A call that would enqueue work with another GPU current, or
+ *     on a stream of another GPU, returns Z1_EINVAL and enqueues nothing;
+ *     so does a scheduled step whose schedule and plan belong to different
+ *     GPUs.  The destroy and query calls make the owning GPU current for
+ *     their duration and restore the caller's.
  *   - A plan is used from one host thread and one stream at a time.
  *   - No C++ exception crosses this interface.
  */

@@ -17,6 +17,7 @@ using z1::Chunk;
 using z1::DD;
 
 struct z1_plan {
+    int device = -1;  // the GPU current at creation; every call must run there
     int32_t n = 0, K = 0, dp = 0, rank = 0;
     int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
     int grid = 0;
@@ -38,6 +39,7 @@ struct z1_plan {
 };
 
 struct z1_schedule {
+    int device = -1;
     int64_t t_first = 1, n_steps = 0;
     bool clipping = false;
     AdamConsts *d_table = nullptr;  // [n_steps] constants of steps t_first ...
@@ -45,6 +47,7 @@ struct z1_schedule {
 };
 
 struct z1_pack {
+    int device = -1;
     int32_t n = 0, K = 0, dp = 0;
     int64_t seg = 0, n_chunks = 0;
     bool divide = false;
@@ -57,6 +60,63 @@ struct z1_pack {
 namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The GPU current on the calling thread, -1 if HIP reports none.
+int current_device()
+{
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return d;
+}
+
+// True when `stream` is a stream of GPU `dev`.  NULL and the legacy /
+// per-thread default handles always name a stream of the current GPU.
+bool stream_on(int dev, z1_stream stream)
+{
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!s || s == hipStreamLegacy || s == hipStreamPerThread)
+        return current_device() == dev;
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(s, &d) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return d == dev;
+}
+
+// A call on an object created on GPU `owner` may enqueue work only with that
+// GPU current and on one of its streams; otherwise its kernels would run on
+// another GPU with this one's pointers.
+bool on_owner(int owner, z1_stream stream)
+{
+    return current_device() == owner && stream_on(owner, stream);
+}
+
+// Makes GPU `dev` current for the scope and restores the previous one
+// (destroy and query calls, which any thread may make).
+class DeviceScope {
+  public:
+    explicit DeviceScope(int dev) : prev_(current_device())
+    {
+        if (dev >= 0 && prev_ >= 0 && dev != prev_ && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            prev_ = -1;
+        }
+        switched_ = dev >= 0 && prev_ >= 0 && dev != prev_;
+    }
+    ~DeviceScope()
+    {
+        if (switched_)
+            (void)hipSetDevice(prev_);
+    }
+
+  private:
+    int prev_;
+    bool switched_ = false;
+};
 
 void free_plan_memory(z1_plan *p)
 {
@@ -440,6 +500,14 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
 
+    if ((p->device = current_device()) < 0) {
+        delete p;
+        return Z1_EHIP;
+    }
+    if (!stream_on(p->device, stream)) {
+        delete p;
+        return Z1_EINVAL;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||
@@ -483,6 +551,7 @@ z1_status z1_plan_destroy(z1_plan *p)
 {
     if (!p)
         return Z1_OK;
+    DeviceScope on(p->device);
     (void)hipDeviceSynchronize();
     free_plan_memory(p);
     delete p;
@@ -520,6 +589,8 @@ z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
 {
     if (!p || k < 0 || k >= p->K)
         return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
+        return Z1_EINVAL;
     if (k != 0 && k != p->next_k)
         return Z1_ESTATE;
     const bool first = k == 0, last = k == p->K - 1;
@@ -541,6 +612,8 @@ z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
 z1_status z1_accum_grads_range(z1_plan *p, int32_t k_begin, int32_t k_end, z1_stream stream)
 {
     if (!p || k_begin < 0 || k_end > p->K || k_begin >= k_end)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (k_begin != 0 && k_begin != p->next_k)
         return Z1_ESTATE;
@@ -574,6 +647,8 @@ z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
 {
     if (!p || !d_S)
         return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
+        return Z1_EINVAL;
     if (!aligned(d_S, 8))
         return Z1_EALIGN;
     if (!p->acc_complete)
@@ -588,6 +663,8 @@ z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
 z1_status z1_grad_norm_sq_pair(z1_plan *p, double *d_pair, z1_stream stream)
 {
     if (!p || !d_pair)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (!aligned(d_pair, 16))
         return Z1_EALIGN;
@@ -621,6 +698,8 @@ z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_glo
     const bool clipping = hp->clip > 0.0;
     if (clipping && !d_S_global)
         return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
+        return Z1_EINVAL;
     if (d_S_global && !aligned(d_S_global, 8))
         return Z1_EALIGN;
     if (!p->acc_complete || (clipping && !p->norm_done))
@@ -639,6 +718,8 @@ z1_status z1_adamw_step(z1_plan *p, const z1_adamw_hp *hp, const double *d_S_glo
 z1_status z1_grad_norm_sq_acc(z1_plan *p, double *d_S, z1_stream stream)
 {
     if (!p || !d_S)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (!aligned(d_S, 8))
         return Z1_EALIGN;
@@ -732,6 +813,14 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
         delete p;
         return Z1_EINVAL;
     }
+    if ((p->device = current_device()) < 0) {
+        delete p;
+        return Z1_EHIP;
+    }
+    if (!stream_on(p->device, stream)) {
+        delete p;
+        return Z1_EINVAL;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void *dc = nullptr, *dg = nullptr;
     if (hipMalloc(&dc, (chunks.empty() ? 1 : chunks.size()) * sizeof(Chunk)) != hipSuccess ||
@@ -766,6 +855,7 @@ z1_status z1_pack_destroy(z1_pack *p)
 {
     if (!p)
         return Z1_OK;
+    DeviceScope on(p->device);
     (void)hipDeviceSynchronize();
     if (p->d_chunks)
         (void)hipFree(p->d_chunks);
@@ -778,6 +868,8 @@ z1_status z1_pack_destroy(z1_pack *p)
 z1_status z1_pack_accum(z1_pack *p, int32_t k, z1_stream stream)
 {
     if (!p || k < 0 || k >= p->K)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (k != 0 && k != p->next_k)
         return Z1_ESTATE;
@@ -795,6 +887,8 @@ z1_status z1_pack_accum(z1_pack *p, int32_t k, z1_stream stream)
 z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_stream stream)
 {
     if (!p || k_begin < 0 || k_end > p->K || k_begin >= k_end)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (k_begin != 0 && k_begin != p->next_k)
         return Z1_ESTATE;
@@ -848,6 +942,14 @@ z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
     sc->t_first = hp->step;
     sc->n_steps = n_steps;
     sc->clipping = hp->clip > 0.0;
+    if ((sc->device = current_device()) < 0) {
+        delete sc;
+        return Z1_EHIP;
+    }
+    if (!stream_on(sc->device, stream)) {
+        delete sc;
+        return Z1_EINVAL;
+    }
     auto fail = [&](z1_status st) {
         if (sc->d_table)
             (void)hipFree(sc->d_table);
@@ -880,6 +982,7 @@ z1_status z1_schedule_destroy(z1_schedule *sc)
 {
     if (!sc)
         return Z1_OK;
+    DeviceScope on(sc->device);
     (void)hipDeviceSynchronize();
     (void)hipFree(sc->d_table);
     (void)hipFree(sc->d_state);
@@ -891,6 +994,7 @@ z1_status z1_schedule_query(const z1_schedule *sc, int64_t *next_step, int64_t *
 {
     if (!sc)
         return Z1_EINVAL;
+    DeviceScope on(sc->device);
     int64_t st[2] = {0, 0};
     if (hipMemcpy(st, sc->d_state, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) {
         (void)hipGetLastError();
@@ -910,6 +1014,10 @@ z1_status z1_adamw_step_scheduled(z1_plan *p, z1_schedule *sc, const double *d_S
         return Z1_EINVAL;
     if (sc->clipping && !d_S_global)
         return Z1_EINVAL;
+    if (sc->device != p->device)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
+        return Z1_EINVAL;
     if (d_S_global && !aligned(d_S_global, 8))
         return Z1_EALIGN;
     if (!p->acc_complete || (sc->clipping && !p->norm_done))
@@ -926,6 +1034,8 @@ z1_status z1_adamw_step_scheduled(z1_plan *p, z1_schedule *sc, const double *d_S
 z1_status z1_probe_plan(z1_plan *p, int32_t kind, z1_stream stream)
 {
     if (!p || kind != Z1_PROBE_PLAN_ADAMW)
+        return Z1_EINVAL;
+    if (!on_owner(p->device, stream))
         return Z1_EINVAL;
     if (z1::launch_adamw_traffic(geom(p), p->d_weights, p->acc, p->master, p->exp_avg,
                                  p->exp_avg_sq, reinterpret_cast<hipStream_t>(stream)) !=
