@@ -211,12 +211,16 @@ class Plan:
     def __init__(self, handle: int, info: PlanInfo, keep):
         self.handle = handle
         self.info = info
-        self._keep = keep   # host arrays the bind pointed at, for the plan's life
+        # the host arrays the bind pointed at and the bound device tensors:
+        # the plan writes into those tensors until it is destroyed, so they
+        # must not return to torch's allocator before it is
+        self._keep = keep
 
     def close(self):
         if self.handle:
             _check(lib.z1_plan_destroy(self.handle), "z1_plan_destroy")
             self.handle = 0
+            self._keep = None
 
     def __del__(self):
         try:
@@ -277,7 +281,8 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
            "z1_plan_create")
     info = PlanInfo()
     _check(lib.z1_plan_query(h, ctypes.byref(info)), "z1_plan_query")
-    return Plan(h.value, info, (n, wp, gp, r, ls, ws))
+    return Plan(h.value, info, (n, wp, gp, r, ls, ws, weights, grads, master, exp_avg,
+                                exp_avg_sq, acc))
 
 
 def z1_plan_layout(plan: Plan):
@@ -396,12 +401,13 @@ class Pack:
     def __init__(self, handle: int, seg: int, keep):
         self.handle = handle
         self.seg = seg
-        self._keep = keep
+        self._keep = keep   # host arrays and the bound device tensors (as Plan)
 
     def close(self):
         if self.handle:
             _check(lib.z1_pack_destroy(self.handle), "z1_pack_destroy")
             self.handle = 0
+            self._keep = None
 
     def __del__(self):
         try:
@@ -428,7 +434,7 @@ def z1_pack_create(numel: Sequence[int], dp_size: int, grads: Sequence[Sequence]
     h = ctypes.c_void_p()
     _check(lib.z1_pack_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)), "z1_pack_create")
     seg = z1_pack_layout(n, dp_size, kind, r)
-    return Pack(h.value, seg, (n, r, gp))
+    return Pack(h.value, seg, (n, r, gp, grads, send))
 
 
 def z1_pack_accum(pack: Pack, k: int, stream=None) -> None:

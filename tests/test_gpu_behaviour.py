@@ -473,3 +473,54 @@ def test_adamw_wide_range_matches_oracle(clip, step):
         assert np.isnan(p).any()          # the negative-v elements took the NaN path
     finally:
         st.close()
+
+
+def _plan_from_temporaries(w):
+    """A plan over tensors that nothing but the plan references."""
+    start, ln, off, ae = B.z1_shard_plan(w.numel, w.dp_size, w.rank)
+    master_full = W.make_master(w, seed=0, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    master = torch.zeros(ae, **f32)
+    for i in range(len(w.shapes)):
+        if ln[i]:
+            master[off[i]:off[i] + ln[i]].copy_(
+                master_full[i].reshape(-1)[start[i]:start[i] + ln[i]])
+    weights = [m.to(torch.bfloat16) for m in master_full]
+    grads = [W.make_micro_grads(w, 1, k, seed=0, device="cuda") for k in range(w.n_micro)]
+    return B.z1_plan_create(w.numel, w.dp_size, w.rank, weights, grads, master,
+                            torch.zeros(ae, **f32), torch.zeros(ae, **f32), torch.zeros(ae, **f32))
+
+
+def test_plan_keeps_its_bound_tensors_alive():
+    """The binding holds every tensor a plan is bound to until the plan is
+    closed: a plan built from temporaries, stepped after same-sized NaN
+    tensors were allocated (they would take any freed block), stores the
+    bits of the same step on tensors the caller kept, and the NaN tensors
+    stay untouched."""
+    w = W.TINY
+    ref = _fresh(w)
+    plan = None
+    try:
+        _run_steps(ref, w, 1, 2)
+        plan = _plan_from_temporaries(w)
+        torch.cuda.synchronize()
+        junk = [torch.full((ref.arena_elems,), float("nan"), device="cuda") for _ in range(8)]
+        junk += [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda")
+                 for s in w.shapes for _ in range(1 + w.n_micro)]
+        d_S = torch.zeros(1, dtype=torch.float64, device="cuda")
+        B.z1_accum_grads_range(plan, 0, w.n_micro)
+        B.z1_grad_norm_sq(plan, d_S)
+        B.z1_adamw_step(plan, d_S=d_S, step=1, **w.hp())
+        torch.cuda.synchronize()
+        weights, _, master, m, v, acc = plan._keep[6:12]
+        for got, want in ((master, ref.master), (m, ref.exp_avg), (v, ref.exp_avg_sq),
+                          (acc, ref.acc)):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+        for got, want in zip(weights, ref.weights):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        assert d_S.item() == ref.d_S.item()
+        assert all(bool(torch.isnan(j.float()).all()) for j in junk)
+    finally:
+        if plan is not None:
+            plan.close()
+        ref.close()
