@@ -388,6 +388,9 @@ def main():
                      "launch_ms": adam_avg,
                      "same_traffic_twin_GBps": twin_gbps,
                      "vs_same_traffic_ceiling": (achieved / twin_gbps) if twin_gbps else None},
+        "plan_create_ms": st.plan_create_s * 1e3,
+        "plan_create_detail": "the shard plan and chunk table built on the host and uploaded "
+                              "once per parameter list (z1_plan_create); not part of the step",
         "kernels_ms": {"accum_all_K": accum_ms, "norm_fin": float(norm_ms.mean()),
                        "adamw": adam_avg, "adamw_median": float(np.median(adam_ms))},
         "rates": rates,

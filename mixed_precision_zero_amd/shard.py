@@ -12,6 +12,7 @@ the full-size tensors then serve only as staging for seeded inputs
 """
 from __future__ import annotations
 
+import time
 from typing import List, Optional, Sequence
 
 import torch
@@ -53,11 +54,13 @@ class ShardStep:
             self.w_packed = torch.zeros(n, **bf)
             self.g_packed = [torch.zeros(n, **bf) for _ in range(n_micro)]
             bind_w, bind_g = self.w_packed, self.g_packed
+        t0 = time.perf_counter()
         self.plan = B.z1_plan_create(self.numel, dp_size, rank, bind_w, bind_g,
                                      self.master, self.exp_avg, self.exp_avg_sq, self.acc,
                                      chunk_elems=chunk_elems, max_blocks=max_blocks, kind=kind,
                                      rows=self.rows if kind == "dim0" else None,
                                      lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
+        self.plan_create_s = time.perf_counter() - t0   # plan + chunk table + upload
         self.t = 0
 
     # -- layout helpers (torch copies; initialisation and inspection only) --
