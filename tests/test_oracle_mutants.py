@@ -76,6 +76,19 @@ MUTANTS = {
     "adamw_ignores_clip": [("double g = c * (double)acc[e];", "double g = (double)acc[e];")],
     "adamw_weight_from_old_master": [("w[e] = z1o_bf16_rne(p[e]);",
                                       "w[e] = z1o_bf16_rne((float)(double)acc[e] * 0.0f + p[e] * 0.999f);")],
+    "adamw_bias2_power_off_by_one": [("pow(hp->beta2, t)", "pow(hp->beta2, t + 1.0)")],
+    "adamw_t_from_zero": [("const double t = (double)hp->step;",
+                           "const double t = (double)(hp->step - 1);")],
+    "adamw_v_not_squared": [("(1.0 - hp->beta2) * g * g;", "(1.0 - hp->beta2) * g;")],
+    "adamw_v_unclipped": [("(1.0 - hp->beta2) * g * g;",
+                           "(1.0 - hp->beta2) * (double)acc[e] * (double)acc[e];")],
+    "acc_mean_not_sum": [("acc[e] = a;", "acc[e] = a / (float)K;")],
+    "lr_decay_from_zero": [("int64_t d = t - (warmup > 0 ? warmup : 0);", "int64_t d = t;")],
+    "rne_saturates": [("kept += 1u;", "kept += ((kept & 0x7FFFu) == 0x7F7Fu) ? 0u : 1u;")],
+    "rne_inf_becomes_nan": [("if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)",
+                             "if ((u & 0x7F800000u) == 0x7F800000u)")],
+    "clip_eps_inside_sqrt": [("double c = clip / (sqrt(S) + 1e-6);",
+                              "double c = clip / sqrt(S + 1e-6);")],
 }
 
 
