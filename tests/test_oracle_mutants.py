@@ -89,6 +89,14 @@ MUTANTS = {
                              "if ((u & 0x7F800000u) == 0x7F800000u)")],
     "clip_eps_inside_sqrt": [("double c = clip / (sqrt(S) + 1e-6);",
                               "double c = clip / sqrt(S + 1e-6);")],
+    "norm_square_in_float": [("double x = a * a;", "double x = (double)((float)a * (float)a);")],
+    # fp32 stores of the new state rounded toward minus infinity, not to nearest
+    "master_store_floor": [("p[e] = (float)pe;",
+                            "p[e] = (float)pe; if ((double)p[e] > pe) p[e] = nextafterf(p[e], -INFINITY);")],
+    "m_store_floor": [("m[e] = (float)me;",
+                       "m[e] = (float)me; if ((double)m[e] > me) m[e] = nextafterf(m[e], -INFINITY);")],
+    "v_store_floor": [("v[e] = (float)ve;",
+                       "v[e] = (float)ve; if ((double)v[e] > ve) v[e] = nextafterf(v[e], -INFINITY);")],
 }
 
 
