@@ -559,6 +559,15 @@ def check_step_vs_torch_tiny(o):
         assert_rel_rms(v, tv, 1e-6, f"Tiny v t={t}")
         tw = torch.from_numpy(p.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         assert (wbits == tw).all(), "bf16 weights differ from torch's cast of the master"
+        # one clipped update from the same stored state (both sides restart
+        # from torch's each step): the clipped gradient c * acc is formed in
+        # binary64 on both sides, so the fp32 stores agree but for rare 1-ulp
+        # straddles (torch's own norm and evaluation order)
+        for name, got, want, share in (("p", p, tp, 1e-3), ("m", m, tm, 1e-2), ("v", v, tv, 1e-3)):
+            d = _ulps_apart(got, want)
+            assert d.max() <= 1 and (d > 0).mean() <= share, \
+                f"Tiny {name} t={t}: {int((d > 0).sum())} stores differ, max {d.max()} ulp"
+        p[:], m[:], v[:] = (np.asarray(x, np.float32) for x in (tp, tm, tv))
 
 
 ALL = [check_plan_bruteforce, check_plan_large, check_plan_flat_bruteforce,

@@ -97,6 +97,19 @@ MUTANTS = {
                        "m[e] = (float)me; if ((double)m[e] > me) m[e] = nextafterf(m[e], -INFINITY);")],
     "v_store_floor": [("v[e] = (float)ve;",
                        "v[e] = (float)ve; if ((double)v[e] > ve) v[e] = nextafterf(v[e], -INFINITY);")],
+    "clip_g_in_float": [("double g = c * (double)acc[e];",
+                         "double g = (double)(float)(c * (double)acc[e]);")],
+    "bias_corrections_in_float": [
+        ("const double bc1 = 1.0 - pow(hp->beta1, t);",
+         "const double bc1 = (double)(1.0f - powf((float)hp->beta1, (float)t));"),
+        ("const double bc2 = 1.0 - pow(hp->beta2, t);",
+         "const double bc2 = (double)(1.0f - powf((float)hp->beta2, (float)t));")],
+    "acc_reverse_order": [("float a = bf16_to_f32(g[e]);",
+                           "float a = bf16_to_f32(g[(int64_t)(K - 1) * L + e]);"),
+                          ("float gk = bf16_to_f32(g[(int64_t)k * L + e]);",
+                           "float gk = bf16_to_f32(g[(int64_t)(K - 1 - k) * L + e]);")],
+    "lr_warmup_plus_one": [("return lr_max * (double)t / (double)warmup;",
+                            "return lr_max * (double)t / (double)(warmup + 1);")],
 }
 
 
