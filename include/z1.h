@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 6
+#define Z1_ABI_VERSION 7
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -99,10 +99,13 @@ const char *z1_strerror(z1_status status);
  *
  * arena_off[i] is where slice i lives in the fp32 arenas (master, m, v,
  * acc): offsets increase with i, slices do not overlap, and
- * arena_off[i] == start[i] (mod 8), so that element e of a slice sits at
- * the same position within a 16-byte word in a bf16 tensor and within a
- * 32-byte word in an fp32 arena.  *arena_elems is the arena length in
- * elements (the shard size plus at most 7 padding elements per tensor).
+ * arena_off[i] == start[i] (mod 32), so that element e of a slice sits at
+ * the same position within a 64-byte block of a bf16 tensor and within a
+ * 128-byte cache line of an fp32 arena: the pieces the step cuts at
+ * multiples of its work unit inside a tensor start on whole lines of every
+ * buffer.  *arena_elems is the arena length in elements (the shard size
+ * plus at most 31 padding elements per tensor).  (Before ABI version 7 the
+ * residue was taken mod 8.)
  *
  *   n_tensors   >= 0 (0 gives *arena_elems = 0)
  *   numel       host [n_tensors], each >= 0
@@ -467,7 +470,8 @@ z1_status z1_grad_norm_sq_acc(z1_plan *plan, double *d_S, z1_stream stream);
 typedef struct z1_pack z1_pack;
 
 /* Segment length: the largest arena of any rank, rounded up to a multiple of
- * 8 elements.  Errors as z1_shard_plan_kind. */
+ * 32 elements (so every segment starts on a 128-byte line).  Errors as
+ * z1_shard_plan_kind. */
 z1_status z1_pack_layout(int32_t kind, int32_t n_tensors, const int64_t *numel,
                          const int64_t *rows, int32_t dp_size, int64_t *seg_elems);
 
