@@ -99,13 +99,13 @@ const char *z1_strerror(z1_status status);
  *
  * arena_off[i] is where slice i lives in the fp32 arenas (master, m, v,
  * acc): offsets increase with i, slices do not overlap, and
- * arena_off[i] == start[i] (mod 32), so that element e of a slice sits at
- * the same position within a 64-byte block of a bf16 tensor and within a
- * 128-byte cache line of an fp32 arena: the pieces the step cuts at
- * multiples of its work unit inside a tensor start on whole lines of every
- * buffer.  *arena_elems is the arena length in elements (the shard size
- * plus at most 31 padding elements per tensor).  (Before ABI version 7 the
- * residue was taken mod 8.)
+ * arena_off[i] == start[i] (mod 64), so that element e of a slice sits at
+ * the same position within a 128-byte cache line of a bf16 tensor (or
+ * packed bf16 shard) and within a 256-byte block of an fp32 arena: the
+ * pieces the step cuts at multiples of its work unit inside a tensor start
+ * on whole lines of every buffer.  *arena_elems is the arena length in
+ * elements (the shard size plus at most 63 padding elements per tensor).
+ * (Before ABI version 7 the residue was taken mod 8.)
  *
  *   n_tensors   >= 0 (0 gives *arena_elems = 0)
  *   numel       host [n_tensors], each >= 0
@@ -470,7 +470,7 @@ z1_status z1_grad_norm_sq_acc(z1_plan *plan, double *d_S, z1_stream stream);
 typedef struct z1_pack z1_pack;
 
 /* Segment length: the largest arena of any rank, rounded up to a multiple of
- * 32 elements (so every segment starts on a 128-byte line).  Errors as
+ * 64 elements (so every segment starts on a 256-byte boundary).  Errors as
  * z1_shard_plan_kind. */
 z1_status z1_pack_layout(int32_t kind, int32_t n_tensors, const int64_t *numel,
                          const int64_t *rows, int32_t dp_size, int64_t *seg_elems);

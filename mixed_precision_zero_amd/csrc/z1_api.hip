@@ -310,10 +310,12 @@ z1_status z1_shard_plan_kind(int32_t kind, int32_t n_tensors, const int64_t *num
         base += numel[i];
         start[i] = s0;
         len[i] = ln;
-        // smallest offset >= next with the slice start's residue mod 32: the
+        // smallest offset >= next with the slice start's residue mod 64: the
         // pieces cut at multiples of chunk_elems inside the tensor then start
-        // on a 128-byte line of every fp32 arena, so no line is split between
-        // two workgroups (a 16-byte residue left ragged lists' AdamW 7-8% slower)
+        // on a 128-byte line of every fp32 arena and packed bf16 shard, so no
+        // line is split between two workgroups (a 32-byte residue left ragged
+        // lists' AdamW 7-8% slower, and a 64-byte one their packed
+        // accumulation 5%)
         const int64_t R = z1::kArenaResidue;
         const int64_t off = next + (((s0 - next) % R) + R) % R;
         arena_off[i] = off;
@@ -422,7 +424,7 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     if (packed && shard_elems > 0) {
         // one shard buffer per role; tensor i's pointer is placed so that
         // element start[i] + e lands on arena element arena_off[i] + e
-        // (arena_off[i] - start[i] is a multiple of 32: 64-byte aligned)
+        // (arena_off[i] - start[i] is a multiple of 64: 128-byte aligned)
         const void *wbase = b->weights[0];
         if (!wbase) {
             delete p;

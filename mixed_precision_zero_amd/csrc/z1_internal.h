@@ -19,14 +19,15 @@ constexpr int kMaxSlots = 8;     // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
 // Arena offsets share the slice start's residue mod kArenaResidue elements:
-// 32 fp32 elements are one 128-byte cache line, so a piece that starts at a
-// multiple of chunk_elems inside its tensor starts on a line in the arenas.
-constexpr int64_t kArenaResidue = 32;
+// 64 elements are one 128-byte cache line of bf16 (two of fp32), so a piece
+// that starts at a multiple of chunk_elems inside its tensor starts on a line
+// in the fp32 arenas and in a packed bf16 shard alike.
+constexpr int64_t kArenaResidue = 64;
 
 // One unit of work: a piece of one tensor's slice of at most chunk_elems
 // elements.  Pieces are cut at multiples of chunk_elems inside the tensor,
 // so every piece except a slice's first one starts on a 128-byte line of the
-// fp32 arenas (and a 64-byte boundary of the bf16 tensor).
+// fp32 arenas and of the bf16 buffers.
 struct alignas(32) Chunk {
     int64_t src;     // first element of the piece inside the full tensor
     int64_t dst;     // same element's index inside the fp32 arenas

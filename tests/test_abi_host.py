@@ -51,11 +51,11 @@ def test_plan_bitexact_vs_oracle(name):
 
 
 def _check_arena(start, ln, off, arena):
-    assert (off % 32 == start % 32).all(), "arena offset must share the slice's residue mod 32"
+    assert (off % 64 == start % 64).all(), "arena offset must share the slice's residue mod 64"
     end = off + ln
     assert (off[1:] >= end[:-1]).all(), "arena slices overlap or go backwards"
     assert (off >= 0).all() and (end <= arena).all()
-    assert arena - int(ln.sum()) <= 31 * len(ln), "more padding than 31 per tensor"
+    assert arena - int(ln.sum()) <= 63 * len(ln), "more padding than 63 per tensor"
     if len(ln):
         assert arena == int(end[-1])
 
@@ -257,7 +257,7 @@ def test_pack_layout_is_largest_rank_arena(kind):
             seg = B.z1_pack_layout(w.numel, D, kind, rows if kind == "dim0" else None)
             arenas = [B.z1_shard_plan(w.numel, D, r, kind=kind,
                                       rows=rows if kind == "dim0" else None)[3] for r in range(D)]
-            assert seg % 32 == 0 and seg - 32 < max(arenas) <= seg
+            assert seg % 64 == 0 and seg - 64 < max(arenas) <= seg
 
 
 def test_pack_create_rejects_before_device_work():
