@@ -60,6 +60,10 @@ enum { NT = 5, K = 3, D = 3, RANK = 2 };
 
 int main(void)
 {
+    if (z1_abi_version() != Z1_ABI_VERSION) {
+        fprintf(stderr, "library ABI %d, header ABI %d\n", (int)z1_abi_version(), Z1_ABI_VERSION);
+        return 5;
+    }
     const int64_t numel[NT] = {1000, 7, 4099, 1, 3000};
     int64_t start[NT], len[NT], off[NT], arena = 0;
     int64_t ostart[NT], olen[NT];
