@@ -6,9 +6,11 @@
 // slice, its lanes move 4 consecutive elements each with one 16-byte fp32
 // access per arena and one 8-byte bf16 access, consecutive lanes on
 // consecutive addresses.  The fp32 arenas are laid out so that an arena
-// element and its bf16 element share their position within a vector; only
-// the first and last vector of a slice can be partial and take a per-element
-// path.
+// element and its bf16 element share their position within a vector (the
+// arena offset matches the slice start mod 64 elements), so the pieces cut
+// at multiples of the chunk size inside a tensor start on whole 128-byte
+// lines of every buffer; only the first and last vector of a slice can be
+// partial and take a per-element path.
 //
 // Arithmetic follows the definition exactly (this file is built with
 // -ffp-contract=off and without fast-math):
