@@ -9,10 +9,14 @@ same functions run against deliberately broken copies of the oracle in
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 
 import numpy as np
 import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 ULP32 = 2.0 ** -23          # one fp32 ulp relative to the value's binade floor
@@ -474,9 +478,13 @@ def check_adamw_segments_vs_torch(o):
 
 
 def check_lr_schedule(o):
-    """Warmup/decay closed forms at their boundary points; cosine decay
-    against torch's CosineAnnealingLR (closed form in its documentation)."""
-    lmax, lmin, W_, D = 3e-3, 3e-4, 2000, 100000
+    """Warmup/decay closed forms at their boundary points, with the schedule
+    the Nanotron Guide's config.yaml prints (tests/golden/hyperparams.json);
+    cosine decay against torch's CosineAnnealingLR (closed form in its
+    documentation)."""
+    cfg = json.load(open(os.path.join(GOLDEN, "hyperparams.json")))["guide_config"]
+    lmax, lmin = cfg["learning_rate"], cfg["min_decay_lr"]
+    W_, D = cfg["lr_warmup_steps"], cfg["lr_decay_steps"]
     for style in (1, 2):
         lr = lambda t: o.lr_at(lmax, lmin, W_, D, style, t)  # noqa: E731
         assert lr(W_) == lmax and lr(W_ // 2) == lmax / 2 and lr(1) == lmax / W_
