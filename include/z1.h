@@ -50,7 +50,8 @@
  *     GPUs.  The destroy and query calls make the owning GPU current for
  *     their duration and restore the caller's.
  *   - A plan is used from one host thread and one stream at a time.
- *   - No C++ exception crosses this interface.
+ *   - No C++ exception crosses this interface: a host allocation that fails
+ *     while a call builds its tables returns Z1_ENOMEM.
  */
 #ifndef Z1_H
 #define Z1_H
@@ -67,7 +68,7 @@ typedef enum z1_status {
     Z1_OK = 0,
     Z1_EINVAL = 1, /* bad size, rank, micro-batch index, hyperparameter or null pointer */
     Z1_EALIGN = 2, /* a device base pointer is not 16-byte aligned (8 for d_S) */
-    Z1_ENOMEM = 3, /* a library-owned allocation failed */
+    Z1_ENOMEM = 3, /* a library-owned allocation failed (device or host) */
     Z1_EHIP = 4,   /* the HIP runtime reported an error (launch or copy) */
     Z1_ESTATE = 5  /* calls made out of order (see z1_accum_grads) */
 } z1_status;

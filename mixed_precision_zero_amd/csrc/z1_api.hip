@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <memory>
 #include <new>
 #include <vector>
 
@@ -141,6 +142,46 @@ void free_plan_memory(z1_plan *p)
     p->d_grads = nullptr;
     p->d_weights = nullptr;
     p->d_partials = nullptr;
+}
+
+// Owners of a plan or pack under construction: on any early return (or an
+// exception) the device memory allocated so far is released.
+struct PlanDeleter {
+    void operator()(z1_plan *p) const
+    {
+        if (p->d_chunks || p->d_grads || p->d_weights || p->d_partials || p->d_stage ||
+            p->d_counter || p->d_scales)
+            (void)hipDeviceSynchronize();  // an upload may still be in flight
+        free_plan_memory(p);
+        delete p;
+    }
+};
+
+struct PackDeleter {
+    void operator()(z1_pack *p) const
+    {
+        if (p->d_chunks || p->d_grads)
+            (void)hipDeviceSynchronize();
+        if (p->d_chunks)
+            (void)hipFree(p->d_chunks);
+        if (p->d_grads)
+            (void)hipFree(p->d_grads);
+        delete p;
+    }
+};
+
+// Runs the body of an entry point that builds host tables.  The only
+// operations in those bodies that can throw are host allocations
+// (std::vector growth), so any exception means the host ran out of memory;
+// it becomes Z1_ENOMEM and never crosses the C interface.
+template <typename F>
+z1_status no_throw(F &&body)
+{
+    try {
+        return body();
+    } catch (...) {
+        return Z1_ENOMEM;
+    }
 }
 
 template <typename T>
@@ -313,9 +354,10 @@ z1_status z1_shard_plan_kind(int32_t kind, int32_t n_tensors, const int64_t *num
         // smallest offset >= next with the slice start's residue mod 64: the
         // pieces cut at multiples of chunk_elems inside the tensor then start
         // on a 128-byte line of every fp32 arena and packed bf16 shard, so no
-        // line is split between two workgroups (a 32-byte residue left ragged
-        // lists' AdamW 7-8% slower, and a 64-byte one their packed
-        // accumulation 5%)
+        // line is split between two workgroups.  (Measured on a ragged list:
+        // matching only mod 8 made AdamW 7-8% slower; mod 32, which leaves
+        // packed bf16 pieces 64 bytes into a line, made the packed
+        // accumulation 5% slower.)
         const int64_t R = z1::kArenaResidue;
         const int64_t off = next + (((s0 - next) % R) + R) % R;
         arena_off[i] = off;
@@ -361,7 +403,7 @@ z1_status z1_lr_at(const z1_lr_schedule *sc, int64_t t, double *lr)
     return Z1_OK;
 }
 
-z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
+static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream stream)
 {
     if (!out)
         return Z1_EINVAL;
@@ -379,7 +421,8 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     if (!chunk_ok(chunk))
         return Z1_EINVAL;
 
-    z1_plan *p = new (std::nothrow) z1_plan();
+    std::unique_ptr<z1_plan, PlanDeleter> owner(new (std::nothrow) z1_plan());
+    z1_plan *p = owner.get();
     if (!p)
         return Z1_ENOMEM;
     p->n = n;
@@ -393,24 +436,18 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     z1_status st = z1_shard_plan_kind(b->plan_kind, n, b->numel, b->rows, b->dp_size, b->rank,
                                       p->start.data(), p->len.data(), p->arena_off.data(),
                                       &p->arena_elems);
-    if (st != Z1_OK) {
-        delete p;
+    if (st != Z1_OK)
         return st;
-    }
-    if (b->arena_elems < p->arena_elems) {
-        delete p;
+    if (b->arena_elems < p->arena_elems)
         return Z1_EINVAL;
-    }
 
     // per-tensor lr / weight-decay multipliers
     std::vector<z1::Scale> scales(n > 0 ? n : 1, z1::Scale{1.0, 1.0});
     for (int32_t i = 0; i < n; ++i) {
         const double ls = b->lr_scale ? b->lr_scale[i] : 1.0;
         const double ws = b->wd_scale ? b->wd_scale[i] : 1.0;
-        if (!isfinite(ls) || !isfinite(ws) || ws < 0.0) {
-            delete p;
+        if (!isfinite(ls) || !isfinite(ws) || ws < 0.0)
             return Z1_EINVAL;
-        }
         scales[i] = z1::Scale{ls, ws};
     }
 
@@ -426,23 +463,15 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
         // element start[i] + e lands on arena element arena_off[i] + e
         // (arena_off[i] - start[i] is a multiple of 64: 128-byte aligned)
         const void *wbase = b->weights[0];
-        if (!wbase) {
-            delete p;
+        if (!wbase)
             return Z1_EINVAL;
-        }
-        if (!aligned(wbase, 16)) {
-            delete p;
+        if (!aligned(wbase, 16))
             return Z1_EALIGN;
-        }
         for (int32_t k = 0; k < K; ++k) {
-            if (!b->grads[k]) {
-                delete p;
+            if (!b->grads[k])
                 return Z1_EINVAL;
-            }
-            if (!aligned(b->grads[k], 16)) {
-                delete p;
+            if (!aligned(b->grads[k], 16))
                 return Z1_EALIGN;
-            }
         }
         auto at = [&](const void *base, int32_t i) {
             return reinterpret_cast<uintptr_t>(base) +
@@ -460,29 +489,20 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
             gptr[(size_t)k * n + i] = static_cast<const uint16_t *>(b->grads[(size_t)k * n + i]);
         if (p->len[i] == 0)
             continue;
-        if (!wptr[i]) {
-            delete p;
+        if (!wptr[i])
             return Z1_EINVAL;
-        }
-        if (!aligned(wptr[i], 16)) {
-            delete p;
+        if (!aligned(wptr[i], 16))
             return Z1_EALIGN;
-        }
         for (int32_t k = 0; k < K; ++k) {
             const void *g = gptr[(size_t)k * n + i];
-            if (!g) {
-                delete p;
+            if (!g)
                 return Z1_EINVAL;
-            }
-            if (!aligned(g, 16)) {
-                delete p;
+            if (!aligned(g, 16))
                 return Z1_EALIGN;
-            }
         }
     }
     if (!aligned(b->master, 16) || !aligned(b->exp_avg, 16) || !aligned(b->exp_avg_sq, 16) ||
         !aligned(b->acc, 16)) {
-        delete p;
         return Z1_EALIGN;
     }
     p->master = b->master;
@@ -497,23 +517,17 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     append_chunks(chunks, n, p->start.data(), p->len.data(), p->arena_off.data(), 0, chunk);
     interleave_chunks(chunks);
     p->n_chunks = (int64_t)chunks.size();
-    if (p->n_chunks > INT32_MAX) {
-        delete p;
+    if (p->n_chunks > INT32_MAX)
         return Z1_EINVAL;
-    }
     int64_t grid = p->n_chunks;
     if (b->max_blocks > 0 && grid > b->max_blocks)
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
 
-    if ((p->device = current_device()) < 0) {
-        delete p;
+    if ((p->device = current_device()) < 0)
         return Z1_EHIP;
-    }
-    if (!stream_on(p->device, stream)) {
-        delete p;
+    if (!stream_on(p->device, stream))
         return Z1_EINVAL;
-    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||
@@ -522,8 +536,6 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
         (st = device_alloc(&p->d_stage, (size_t)z1::kFinStages)) != Z1_OK ||
         (st = device_alloc(&p->d_scales, scales.size())) != Z1_OK ||
         (st = device_alloc(&p->d_counter, 1)) != Z1_OK) {
-        free_plan_memory(p);
-        delete p;
         return st;
     }
     hipError_t e = hipSuccess;
@@ -544,12 +556,11 @@ z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
     if (e == hipSuccess)
         e = hipStreamSynchronize(s);  // host staging vectors die with this call
     if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);  // no upload may still read them
         (void)hipGetLastError();
-        free_plan_memory(p);
-        delete p;
         return Z1_EHIP;
     }
-    *out = p;
+    *out = owner.release();
     return Z1_OK;
 }
 
@@ -744,8 +755,8 @@ z1_status z1_grad_norm_sq_acc(z1_plan *p, double *d_S, z1_stream stream)
     return Z1_OK;
 }
 
-z1_status z1_pack_layout(int32_t kind, int32_t n, const int64_t *numel, const int64_t *rows,
-                         int32_t dp_size, int64_t *seg_elems)
+static z1_status pack_layout_body(int32_t kind, int32_t n, const int64_t *numel,
+                                  const int64_t *rows, int32_t dp_size, int64_t *seg_elems)
 {
     if (!seg_elems || n < 0 || dp_size < 1)
         return Z1_EINVAL;
@@ -764,7 +775,7 @@ z1_status z1_pack_layout(int32_t kind, int32_t n, const int64_t *numel, const in
     return Z1_OK;
 }
 
-z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
+static z1_status pack_create_body(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
 {
     if (!out)
         return Z1_EINVAL;
@@ -779,7 +790,7 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
     if (!chunk_ok(chunk))
         return Z1_EINVAL;
     int64_t seg = 0;
-    z1_status st = z1_pack_layout(b->plan_kind, n, b->numel, b->rows, D, &seg);
+    z1_status st = pack_layout_body(b->plan_kind, n, b->numel, b->rows, D, &seg);
     if (st != Z1_OK)
         return st;
     if (seg > 0 && b->send_elems / seg < D)
@@ -796,7 +807,8 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
         if (!aligned(gptr[j], 16))
             return Z1_EALIGN;
     }
-    z1_pack *p = new (std::nothrow) z1_pack();
+    std::unique_ptr<z1_pack, PackDeleter> owner(new (std::nothrow) z1_pack());
+    z1_pack *p = owner.get();
     if (!p)
         return Z1_ENOMEM;
     p->n = n;
@@ -815,18 +827,12 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
     }
     interleave_chunks(chunks);
     p->n_chunks = (int64_t)chunks.size();
-    if (p->n_chunks > INT32_MAX) {
-        delete p;
+    if (p->n_chunks > INT32_MAX)
         return Z1_EINVAL;
-    }
-    if ((p->device = current_device()) < 0) {
-        delete p;
+    if ((p->device = current_device()) < 0)
         return Z1_EHIP;
-    }
-    if (!stream_on(p->device, stream)) {
-        delete p;
+    if (!stream_on(p->device, stream))
         return Z1_EINVAL;
-    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void *dc = nullptr, *dg = nullptr;
     if (hipMalloc(&dc, (chunks.empty() ? 1 : chunks.size()) * sizeof(Chunk)) != hipSuccess ||
@@ -834,7 +840,6 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
         (void)hipGetLastError();
         if (dc)
             (void)hipFree(dc);
-        delete p;
         return Z1_ENOMEM;
     }
     p->d_chunks = static_cast<Chunk *>(dc);
@@ -847,13 +852,13 @@ z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
         e = hipMemcpyAsync(p->d_grads, gptr.data(), gptr.size() * sizeof(void *),
                            hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
-        e = hipStreamSynchronize(s);
+        e = hipStreamSynchronize(s);  // host staging vectors die with this call
     if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);  // no upload may still read them
         (void)hipGetLastError();
-        z1_pack_destroy(p);
         return Z1_EHIP;
     }
-    *out = p;
+    *out = owner.release();
     return Z1_OK;
 }
 
@@ -920,8 +925,9 @@ z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_str
     return Z1_OK;
 }
 
-z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
-                             const z1_lr_schedule *lr, int64_t n_steps, z1_stream stream)
+static z1_status schedule_create_body(z1_schedule **out, const z1_adamw_hp *hp,
+                                      const z1_lr_schedule *lr, int64_t n_steps,
+                                      z1_stream stream)
 {
     if (!out)
         return Z1_EINVAL;
@@ -977,6 +983,7 @@ z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
     if (e == hipSuccess)
         e = hipStreamSynchronize(s);  // the host table dies with this call
     if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);  // no upload may still read it
         (void)hipGetLastError();
         return fail(Z1_EHIP);
     }
@@ -1060,6 +1067,29 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
                    hipSuccess
                ? Z1_OK
                : Z1_EHIP;
+}
+
+// The entry points that build host tables, behind the exception guard.
+z1_status z1_plan_create(z1_plan **out, const z1_bind *b, z1_stream stream)
+{
+    return no_throw([&] { return plan_create_body(out, b, stream); });
+}
+
+z1_status z1_pack_layout(int32_t kind, int32_t n, const int64_t *numel, const int64_t *rows,
+                         int32_t dp_size, int64_t *seg_elems)
+{
+    return no_throw([&] { return pack_layout_body(kind, n, numel, rows, dp_size, seg_elems); });
+}
+
+z1_status z1_pack_create(z1_pack **out, const z1_pack_bind *b, z1_stream stream)
+{
+    return no_throw([&] { return pack_create_body(out, b, stream); });
+}
+
+z1_status z1_schedule_create(z1_schedule **out, const z1_adamw_hp *hp,
+                             const z1_lr_schedule *lr, int64_t n_steps, z1_stream stream)
+{
+    return no_throw([&] { return schedule_create_body(out, hp, lr, n_steps, stream); });
 }
 
 }  // extern "C"

@@ -319,3 +319,27 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libz1" in r.stderr
+
+
+def test_host_allocation_failure_is_a_status():
+    """No C++ exception crosses the C interface: a host allocation failure
+    inside an entry point returns Z1_ENOMEM.  A child process caps its
+    address space just above what it uses, then asks z1_schedule_create for
+    the largest table the header allows (2^24 steps, 1.3 GB of host
+    staging); the call must return Z1_ENOMEM, not abort."""
+    import subprocess
+    import sys
+    code = "\n".join([
+        "import ctypes, resource, sys",
+        f"sys.path.insert(0, {ROOT!r})",
+        "from mixed_precision_zero_amd import binding as B",
+        "vm = [int(l.split()[1]) for l in open('/proc/self/status') if l.startswith('VmSize')][0]",
+        "resource.setrlimit(resource.RLIMIT_AS, (vm * 1024 + (256 << 20), resource.RLIM_INFINITY))",
+        "hp = B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)",
+        "h = ctypes.c_void_p()",
+        "st = B.lib.z1_schedule_create(ctypes.byref(h), ctypes.byref(hp), None, 1 << 24, None)",
+        "print('status', st, flush=True)",
+    ])
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    assert f"status {B.Z1_ENOMEM}" in r.stdout, r.stdout
