@@ -43,9 +43,13 @@ class ShardStep:
         self.exp_avg_sq = torch.zeros(n, **f32)
         self.acc = torch.zeros(n, **f32)
         bf = dict(dtype=torch.bfloat16, device=self.device)
-        self.weights = weights if weights is not None else [torch.zeros(s, **bf) for s in self.shapes]
-        self.grads = grads if grads is not None else [
-            [torch.zeros(s, **bf) for s in self.shapes] for _ in range(n_micro)]
+        # the full-size bf16 weights and each micro-batch's gradients live in
+        # one flat buffer per role, one view per tensor (a contiguous
+        # parameter / gradient buffer, as data-parallel trainers keep them):
+        # one large allocation instead of one per tensor
+        self.weights = weights if weights is not None else self._flat_views(bf)
+        self.grads = grads if grads is not None else [self._flat_views(bf)
+                                                      for _ in range(n_micro)]
         self.d_S = torch.zeros(1, dtype=torch.float64, device=self.device)
         self.layout = layout
         self.w_packed = self.g_packed = None
@@ -62,6 +66,17 @@ class ShardStep:
                                      lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
         self.plan_create_s = time.perf_counter() - t0   # plan + chunk table + upload
         self.t = 0
+
+    def _flat_views(self, opts) -> List[torch.Tensor]:
+        # each tensor starts on a 128-byte line (64 bf16 elements), so every
+        # view keeps the 16-byte alignment the library requires and pieces
+        # cut at multiples of the chunk size inside a tensor stay line-aligned
+        starts, o = [], 0
+        for n in self.numel:
+            starts.append(o)
+            o += (n + 63) // 64 * 64
+        flat = torch.zeros(max(o, 1), **opts)
+        return [flat[a:a + n].view(shape) for a, n, shape in zip(starts, self.numel, self.shapes)]
 
     # -- layout helpers (torch copies; initialisation and inspection only) --
     def slices(self):
