@@ -418,12 +418,13 @@ def bench_pack(args, w, dev, log):
 
     from mixed_precision_zero_amd import binding as B
     from mixed_precision_zero_amd import workloads as W
+    from mixed_precision_zero_amd.shard import flat_views
     rows = [s[0] for s in w.shapes] if args.plan == "dim0" else None
     seg = B.z1_pack_layout(w.numel, w.dp_size, args.plan, rows)
     send = torch.zeros(w.dp_size * seg, dtype=torch.float32, device=dev)
     grads = []
     for k in range(w.n_micro):
-        gk = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in w.shapes]
+        gk = flat_views(w.shapes, dtype=torch.bfloat16, device=dev)   # one buffer per slot
         W.make_micro_grads(w, 1, k, seed=0, device=dev, out=gk)
         grads.append(gk)
     pack = B.z1_pack_create(w.numel, w.dp_size, grads, send, kind=args.plan, rows=rows,

@@ -20,6 +20,22 @@ import torch
 from . import binding as B
 
 
+def flat_views(shapes: Sequence[Sequence[int]], dtype=torch.bfloat16, device="cuda"
+               ) -> List[torch.Tensor]:
+    """Zeroed tensors of the given shapes as views into one flat buffer.
+
+    Each tensor starts on a 128-byte line (64 bf16 elements), so every view
+    keeps the 16-byte alignment the library requires and pieces cut at
+    multiples of the chunk size inside a tensor stay line-aligned."""
+    numel = [int(torch.Size(s).numel()) for s in shapes]
+    starts, o = [], 0
+    for n in numel:
+        starts.append(o)
+        o += (n + 63) // 64 * 64
+    flat = torch.zeros(max(o, 1), dtype=dtype, device=device)
+    return [flat[a:a + n].view(tuple(shape)) for a, n, shape in zip(starts, numel, shapes)]
+
+
 class ShardStep:
     def __init__(self, shapes: Sequence[Sequence[int]], dp_size: int, rank: int, n_micro: int,
                  device="cuda", chunk_elems: int = 0, max_blocks: int = 0,
@@ -68,15 +84,7 @@ class ShardStep:
         self.t = 0
 
     def _flat_views(self, opts) -> List[torch.Tensor]:
-        # each tensor starts on a 128-byte line (64 bf16 elements), so every
-        # view keeps the 16-byte alignment the library requires and pieces
-        # cut at multiples of the chunk size inside a tensor stay line-aligned
-        starts, o = [], 0
-        for n in self.numel:
-            starts.append(o)
-            o += (n + 63) // 64 * 64
-        flat = torch.zeros(max(o, 1), **opts)
-        return [flat[a:a + n].view(shape) for a, n, shape in zip(starts, self.numel, self.shapes)]
+        return flat_views(self.shapes, **opts)
 
     # -- layout helpers (torch copies; initialisation and inspection only) --
     def slices(self):
