@@ -56,6 +56,20 @@ def test_tiny_fifteen_slots_wide_passes():
     _run(w, 2, [(0, 15)], chunk_elems=1024)
 
 
+@pytest.mark.parametrize("K,ranges", [
+    (33, [(0, 33)]),                     # five passes: 7, 7, 7, 6, 6 slots
+    (64, [(0, 64)]),                     # eight passes of 8 slots
+    (37, [(0, 3), (3, 20), (20, 37)]),   # three calls, each split into even passes
+], ids=["k33", "k64", "k37_three_calls"])
+def test_tiny_many_slots_many_passes(K, ranges):
+    """Many resident micro-batches: a range longer than 8 slots is split into
+    as many passes as it needs, of nearly equal size; every split stores the
+    bits of one call per micro-batch (the oracle's in-order binary32 sum)."""
+    w = dataclasses.replace(W.TINY, name=f"tiny_k{K}", n_micro=K,
+                            shapes=((257, 63), (61,), (1030,)))
+    _run(w, 2, ranges, chunk_elems=1024)
+
+
 def test_ragged_small_three_slots():
     shapes = W.ragged_shapes(300, 12, seed=3)
     w = dataclasses.replace(W.RAGGED, name="ragged_small", shapes=shapes, n_micro=3,
