@@ -80,13 +80,16 @@ def test_step_graph_replays_bitexact(w, resident):
         st.close()
 
 
-@pytest.mark.parametrize("w", [W.TINY, RAGGED_SMALL], ids=lambda w: w.name)
-def test_scheduled_step_captured_once_trains_over_steps(w):
+@pytest.mark.parametrize("w,mup", [(W.TINY, False), (RAGGED_SMALL, False), (W.TINY, True)],
+                         ids=["tiny", "ragged_small", "tiny_mup"])
+def test_scheduled_step_captured_once_trains_over_steps(w, mup):
     """[accumulate all slots, norm, z1_adamw_step_scheduled] captured once and
     replayed for 6 steps of a warmup + cosine learning-rate schedule, with
     fresh gradients written between replays: every replay stores the bits of
     the eager step with that step's t and z1_lr_at(t).  A 7th replay finds
-    the table exhausted: master, m, v and the weights stay as they were."""
+    the table exhausted: master, m, v and the weights stay as they were.
+    With mup, both plans carry per-tensor lr / weight-decay multipliers,
+    which the scheduled kernel applies to each row's constants."""
     from mixed_precision_zero_amd import binding as B
     from mixed_precision_zero_amd.shard import ShardStep
     dev = torch.device("cuda")
@@ -94,8 +97,13 @@ def test_scheduled_step_captured_once_trains_over_steps(w):
     lr_sched = dict(lr_max=w.lr, lr_min=w.lr / 10, warmup_steps=2, decay_steps=3,
                     decay_style="cosine")
     hp = w.hp()
-    gs = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev)
-    es = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev)
+    lr_s = wd_s = None
+    if mup:
+        lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
+    gs = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev, lr_scale=lr_s,
+                   wd_scale=wd_s)
+    es = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev, lr_scale=lr_s,
+                   wd_scale=wd_s)
     sched = None
     try:
         master = W.make_master(w, seed=0, device=dev)
