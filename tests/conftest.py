@@ -8,5 +8,3 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "gpu_long: GPU runs of several minutes, selected explicitly "
-                            "with -m gpu_long (not part of -m gpu)")

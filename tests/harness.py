@@ -134,7 +134,11 @@ class Parity:
         return bool((self.st.len == self.o_len).all() and
                     (self.st.start[nz] == self.o_start[nz]).all())
 
-    def step(self, check=True) -> Optional[StepReport]:
+    def step(self, check=True, gpu_step=None, lr=None) -> Optional[StepReport]:
+        """One step on both sides from fresh seeded gradients.  gpu_step
+        replaces the eager library calls (for example a captured graph's
+        replay); lr replaces the workload's learning rate on the oracle side
+        (the rate a schedule gives this step)."""
         w, st = self.w, self.st
         self.t += 1
         t = self.t
@@ -145,11 +149,17 @@ class Parity:
             st.stage_grads(k)
             g[k] = self._packed_host_bf16(st.grads[k])
         t1 = time.time()
-        st.step(w.hp(), ranges=self.ranges)
+        if gpu_step is None:
+            st.step(w.hp(), ranges=self.ranges)
+        else:
+            gpu_step()
         torch.cuda.synchronize()
         t2 = time.time()
+        hp = w.hp()
+        if lr is not None:
+            hp["lr"] = lr
         S, c, _ = self.o.step(g, self.p, self.m, self.v, step=t, acc=self.acc, w=self.wbits,
-                              segments=self.segments, **w.hp())
+                              segments=self.segments, **hp)
         del g
         t3 = time.time()
         log(f"[parity] {w.name} step {t}: inputs {t1 - t0:.1f}s gpu {t2 - t1:.2f}s "

@@ -215,3 +215,69 @@ def test_scheduled_step_graph_7b_matches_eager():
         if sched is not None:
             sched.close()
         st.close()
+
+
+def _random_multipliers(n, seed):
+    """Seeded per-tensor lr / weight-decay multipliers (inputs of the step:
+    any finite lr scale, any non-negative wd scale, some tensors kept out of
+    decay)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    lr_s = [float(x) for x in rng.uniform(0.05, 2.0, n)]
+    wd_s = [float(x) for x in rng.choice([0.0, 0.5, 1.0, 2.0], n)]
+    return lr_s, wd_s
+
+
+@pytest.mark.parametrize("w,mult,style", [
+    (W.TINY, None, "cosine"),
+    (W.TINY, "mup", "cosine"),
+    (RAGGED_SMALL, None, "linear"),
+    (RAGGED_SMALL, "random", "cosine"),
+    (W.SMOLLM_135M, "mup", "cosine"),
+], ids=["tiny_cosine", "tiny_mup_cosine", "ragged_small_linear", "ragged_small_mult_cosine",
+        "smollm135m_mup_cosine"])
+def test_scheduled_graph_matches_oracle(w, mult, style):
+    """[accumulate all slots, norm, z1_adamw_step_scheduled] captured once and
+    replayed for 8 steps of a learning-rate schedule (3 warmup steps, 4 decay
+    steps, then the minimum), with fresh gradients before every replay.  Each
+    replay is compared element by element with the oracle's step t at the
+    oracle's own rate lr_at(t) (Nanotron Guide, config.yaml: learning_rate,
+    lr_warmup_steps, lr_decay_steps, min_decay_lr), with the per-tensor
+    multipliers as oracle segments: acc, S, master, m, v and the bf16 weights
+    bit for bit."""
+    import harness
+    from mixed_precision_zero_amd import binding as B
+    T, warm, decay = 8, 3, 4
+    lr_min = w.lr / 10
+    style_id = {"none": 0, "linear": 1, "cosine": 2}[style]
+    lr_sched = dict(lr_max=w.lr, lr_min=lr_min, warmup_steps=warm, decay_steps=decay,
+                    decay_style=style)
+    lr_s = wd_s = None
+    if mult == "mup":
+        lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
+    elif mult == "random":
+        lr_s, wd_s = _random_multipliers(len(w.shapes), seed=11)
+    h = harness.Parity(w, lr_scale=lr_s, wd_scale=wd_s, ranges=[(0, w.n_micro)])
+    sched = None
+    try:
+        assert h.plan_matches()
+        sched = B.z1_schedule_create(**w.hp(), step=1, n_steps=T, lr_schedule=lr_sched)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h.st.accumulate_range(0, w.n_micro)
+            h.st.norm()
+            h.st.adamw_scheduled(sched)
+        torch.cuda.synchronize()
+        for t in range(1, T + 1):
+            lr_t = h.o.lr_at(w.lr, lr_min, warm, decay, style_id, t)
+            rep = h.step(gpu_step=g.replay, lr=lr_t)
+            harness.log(f"[sched] {w.name} t={t} lr={lr_t:.6g}: S_rel={rep.S_rel:.2e} "
+                        f"not_bitexact={rep.not_bitexact}")
+            harness.assert_report(rep)
+            assert B.z1_schedule_query(sched) == (t + 1, 0)
+        assert h.canaries_intact()
+        del g
+    finally:
+        if sched is not None:
+            sched.close()
+        h.close()
