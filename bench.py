@@ -64,8 +64,9 @@ def parse():
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems (0 = library default)")
     ap.add_argument("--max-blocks", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time spent timing the oracle (0 = skip)")
+    ap.add_argument("--cpu-steps", type=int, default=3,
+                    help="whole-shard steps of the CPU oracle timed on the host cores "
+                         "(0 = skip)")
     ap.add_argument("--copy-gb", type=float, default=4.0, help="probe-copy size for the ceiling")
     ap.add_argument("--plan", default="per_tensor", choices=["per_tensor", "flat", "dim0"],
                     help="shard plan kind")
@@ -76,9 +77,14 @@ def parse():
                          "z1_accum_grads_range call (up to 8 slots per pass); slot: one "
                          "z1_accum_grads call per micro-batch; the other form is timed too "
                          "and reported beside")
-    ap.add_argument("--layout", default="full", choices=["full", "packed"],
-                    help="bf16 weights and gradients as full-size tensors (default) or as "
-                         "packed shards in arena order")
+    ap.add_argument("--layout", default="packed", choices=["full", "packed"],
+                    help="bf16 weights and gradients as packed shards in arena order "
+                         "(default: the reduce-scatter's output and the all-gather's input) "
+                         "or as full-size tensors; the other layout is timed too and "
+                         "reported beside")
+    ap.add_argument("--layout-steps", type=int, default=10,
+                    help="steps timed with the other bf16 layout over the same arenas, "
+                         "reported beside the headline (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps replayed from one captured HIP graph (z1_adamw_step_scheduled), "
                          "reported beside the eager headline; 0 = skip")
@@ -151,16 +157,6 @@ def main():
     master_full = W.make_master(w, seed=0, device=dev)
     st.scatter_to_arena(st.master, master_full)
     st.load_weights(master_full)
-    # a bounded sample for the CPU oracle: the first slices, in packed order
-    sample_target = 1 << 23
-    sample_idx = []
-    n_s = 0
-    for i, s, ln, _ in st.slices():
-        if ln and n_s < sample_target:
-            take = min(ln, sample_target - n_s)
-            sample_idx.append((i, s, take))
-            n_s += take
-    p_sample = torch.cat([master_full[i].reshape(-1)[s:s + n] for i, s, n in sample_idx]).cpu().numpy()
     del master_full
     for k in range(w.n_micro):
         W.make_micro_grads(w, 1, k, seed=0, device=dev, out=st.grads[k])
@@ -269,6 +265,95 @@ def main():
         del gr
         sched.close()
 
+    # the other bf16 layout over the same fp32 arenas: a second plan, the
+    # headline step (resident or per call) for a few steps, reported beside
+    other_layout = "full" if args.layout == "packed" else "packed"
+    layout_variants = {args.layout: {"ms_per_step": ms_step, "adamw_ms": adam_avg,
+                                     "accum_ms": accum_ms}}
+    if args.layout_steps > 0:
+        rows = st.rows if args.plan == "dim0" else None
+        if other_layout == "full":
+            w2, g2 = st.weights, st.grads
+        else:
+            w2 = torch.zeros(st.arena_elems, dtype=torch.bfloat16, device=dev)
+            g2 = [torch.zeros(st.arena_elems, dtype=torch.bfloat16, device=dev)
+                  for _ in range(w.n_micro)]
+            for k in range(w.n_micro):
+                st.scatter_to_arena(g2[k], st.grads[k])
+        plan2 = B.z1_plan_create(st.numel, w.dp_size, w.rank, w2, g2, st.master, st.exp_avg,
+                                 st.exp_avg_sq, st.acc, chunk_elems=args.chunk,
+                                 max_blocks=args.max_blocks, kind=args.plan, rows=rows,
+                                 lr_scale=lr_s, wd_scale=wd_s, layout=other_layout)
+        t2 = (alt["t_next"] if alt is not None else r["t_next"])
+        ev2 = []
+        for j in range(2 + args.layout_steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            if head_resident:
+                B.z1_accum_grads_range(plan2, 0, w.n_micro)
+            else:
+                for k in range(w.n_micro):
+                    B.z1_accum_grads(plan2, k)
+            B.z1_grad_norm_sq(plan2, st.d_S)
+            e[1].record(stream)
+            B.z1_adamw_step(plan2, d_S=st.d_S, step=t2 + j, **hp)
+            e[2].record(stream)
+            if j >= 2:
+                ev2.append(e)
+        torch.cuda.synchronize()
+        step2 = np.array([e[0].elapsed_time(e[2]) for e in ev2])
+        adam2 = np.array([e[1].elapsed_time(e[2]) for e in ev2])
+        layout_variants[other_layout] = {"ms_per_step": float(step2.mean()),
+                                         "adamw_ms": float(adam2.mean()),
+                                         "accum_norm_ms": float((step2 - adam2).mean()),
+                                         "steps": args.layout_steps}
+        plan2.close()
+        del w2, g2
+
+    # the CPU oracle on the whole shard, from the GPU's current state and the
+    # step's gradients (copied to the host before the probes below overwrite
+    # the arenas)
+    cpu = None
+    if args.cpu_steps > 0:
+        import oracle
+        o = oracle.get()
+        c_copy = time.perf_counter()
+
+        def shard_grads(k):
+            if st.layout == "packed":
+                return st.packed(st.g_packed[k])
+            return torch.cat([st.grads[k][i].reshape(-1)[a:a + n]
+                              for i, a, n, _ in st.slices() if n])
+        g_host = np.empty((w.n_micro, L), np.uint16)
+        for k in range(w.n_micro):
+            g_host[k] = shard_grads(k).view(torch.int16).cpu().numpy().view(np.uint16)
+        p_h, m_h, v_h = (st.packed(x).cpu().numpy() for x in (st.master, st.exp_avg,
+                                                               st.exp_avg_sq))
+        acc_h = np.empty(L, np.float32)
+        w_h = np.empty(L, np.uint16)
+        segments = None
+        if args.mup:
+            rows_o = [s_[0] if len(s_) else 1 for s_ in w.shapes]
+            _, o_len = o.plan(args.plan, w.numel, rows_o, w.dp_size, w.rank)
+            segments = (o_len, lr_s, wd_s)
+        c_copy = time.perf_counter() - c_copy
+        t_cpu = (alt["t_next"] if alt is not None else r["t_next"]) + 100
+        c0 = time.perf_counter()
+        for j in range(args.cpu_steps):
+            o.step(g_host, p_h, m_h, v_h, step=t_cpu + j, acc=acc_h, w=w_h,
+                   segments=segments, **hp)
+        cpu_s = (time.perf_counter() - c0) / args.cpu_steps
+        cpu = {"value": L / cpu_s, "unit": "params/s", "cores": o.num_threads(),
+               "kind": "oracle",
+               "sample": f"{args.cpu_steps} whole-shard steps of the {w.name} shard "
+                         f"({L} elements, K={w.n_micro}): accumulate, norm, clip, AdamW, "
+                         f"bf16 cast; binary64 C oracle, not a tuned CPU optimizer",
+               "ms_per_step": cpu_s * 1e3, "host_copy_s": c_copy,
+               "cpu_model": _cpu_model()}
+        del g_host, p_h, m_h, v_h, acc_h, w_h
+        log(f"[bench] cpu oracle: {cpu_s * 1e3:.0f} ms per whole-shard step "
+            f"({cpu['cores']} threads)")
+
     value = L / (ms_step / 1e3)
     adam_bytes = BYTES_ADAMW * L
     achieved = adam_bytes / (adam_avg / 1e3) / 1e9
@@ -303,11 +388,22 @@ def main():
         del src, dst
         nvL = L // 4
         half = torch.empty(nvL * 4, dtype=torch.bfloat16, device=dev)
+        # the AdamW mix over the step's own buffers: the four fp32 arenas and
+        # the bf16 weight buffer the step writes (the packed shard, or the
+        # start of the flat full-size weight buffer), so placement is shared
+        w_buf = (st.w_packed if st.layout == "packed"
+                 else st.weights[0].untyped_storage().data_ptr())
         ceilings["adamw_traffic"] = timed_gbps(
             lambda: B.z1_probe("adamw_traffic", [st.acc, st.master, st.exp_avg, st.exp_avg_sq,
-                                                 half], nvL), 30 * 4 * nvL)
+                                                 w_buf], nvL), 30 * 4 * nvL)
         ceilings["accum_traffic"] = timed_gbps(
             lambda: B.z1_probe("accum_traffic", [half, st.acc], nvL), 10 * 4 * nvL)
+        if head_resident and 2 <= w.n_micro <= MAX_SLOTS:
+            slots = [half] + [torch.empty_like(half) for _ in range(w.n_micro - 1)]
+            ceilings["slots_traffic"] = timed_gbps(
+                lambda: B.z1_probe("slots_traffic", slots + [st.acc], nvL),
+                (2 * w.n_micro + 4) * 4 * nvL)
+            del slots
         del half
     # k_adamw's own chunk walk over the step's own buffers with no arithmetic
     # (z1_probe_plan): the same-traffic ceiling on exactly this placement
@@ -317,44 +413,22 @@ def main():
     copy_gbps = ceilings["copy"] if ceilings else None
 
     # GB/s of each timed piece: algorithmic bytes / mean time, as a fraction of
-    # the 8 TB/s peak and of the copy probe measured in this process
-    def rate(nbytes, ms):
+    # the 8 TB/s peak and of a traffic-only probe with the same read/write mix
+    # measured in this process (where one exists)
+    def rate(nbytes, ms, probe=None):
         gbps = nbytes / (ms / 1e3) / 1e9
+        ref = ceilings.get(probe) if (ceilings and probe) else None
         return {"GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
-                "frac_of_copy": (gbps / copy_gbps) if copy_gbps else None}
+                "same_mix_probe": probe if ref else None,
+                "frac_of_same_mix_probe": (gbps / ref) if ref else None}
     acc_b = accum_bytes(w.n_micro, head_resident) * L
     norm_avg = float(norm_ms.mean())
-    rates = {"accum_all_K": rate(acc_b, accum_ms),
-             "adamw": rate(BYTES_ADAMW * L, adam_avg),
-             "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg),
+    acc_probe = ("slots_traffic" if head_resident and 2 <= w.n_micro <= MAX_SLOTS
+                 else None if head_resident else "accum_traffic")
+    rates = {"accum_all_K": rate(acc_b, accum_ms, acc_probe),
+             "adamw": rate(BYTES_ADAMW * L, adam_avg, "adamw_traffic"),
+             "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg, "adamw_traffic"),
              "H3_step": rate(acc_b + BYTES_ADAMW * L, ms_step)}
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        import oracle
-        o = oracle.get()
-        g_sample = np.stack([torch.cat([st.grads[k][i].reshape(-1)[s:s + n]
-                                        for i, s, n in sample_idx]).view(torch.int16).cpu().numpy()
-                             for k in range(w.n_micro)]).view(np.uint16)
-        p = p_sample.astype(np.float32).copy()
-        m = np.zeros_like(p)
-        v = np.zeros_like(p)
-        acc = np.empty_like(p)
-        wb = np.empty(p.size, np.uint16)
-        c0 = time.perf_counter()
-        steps = 0
-        while True:
-            steps += 1
-            o.step(g_sample, p, m, v, step=steps, acc=acc, w=wb, **hp)
-            if time.perf_counter() - c0 >= args.cpu_seconds:
-                break
-        cpu_s = (time.perf_counter() - c0) / steps
-        cpu = {"value": p.size / cpu_s, "unit": "params/s", "cores": o.num_threads(),
-               "kind": "oracle",
-               "sample": f"{p.size} shard elements (first slices of the {w.name} shard, "
-                         f"packed), K={w.n_micro}, {steps} full steps: accumulate, norm, "
-                         f"clip, AdamW, bf16; binary64 C oracle, not a tuned CPU optimizer",
-               "cpu_model": _cpu_model()}
 
     out = {
         "metric": ("optimizer-step params/s and achieved HBM GB/s (% of MI355X peak), 7B shard"
@@ -382,7 +456,8 @@ def main():
                    "chunk_elems": int(st.plan.info.chunk_elems),
                    "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
                    "mup": bool(args.mup), "accum": args.accum, "layout": args.layout},
-        "roofline": {"bound": "hbm", "kernel": "k_adamw", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_adamw_tiles + k_adamw_rest (z1_adamw_step)",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
                      "launch_ms": adam_avg,
@@ -395,6 +470,7 @@ def main():
                        "adamw": adam_avg, "adamw_median": float(np.median(adam_ms))},
         "rates": rates,
         "accum_variants": variants,
+        "layout_variants": layout_variants,
         "graph_replay": graph,
         "step_hbm_GBps": h3_bytes / (ms_step / 1e3) / 1e9,
         "step_bytes_per_param": h3_bytes // L if L else None,

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 7
+#define Z1_ABI_VERSION 8
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -327,7 +327,11 @@ z1_status z1_grad_norm_sq(z1_plan *plan, double *d_S, z1_stream stream);
  * rank then holds the same S, equal to what one rank holding the whole
  * model computes unless the exact sum lies within about D * 2^-106 of a
  * binary64 rounding boundary.  With D = 1 it equals z1_grad_norm_sq.
- * Errors: Z1_EINVAL (NULL, n < 1), Z1_EALIGN, Z1_EHIP.
+ * No plan owns z1_norm_combine: the GPU current at the call must own the
+ * stream and both buffers (device memory of that GPU, as the HIP runtime
+ * records it), else Z1_EINVAL and nothing is enqueued.
+ * Errors: Z1_EINVAL (NULL, n < 1, host memory, another GPU's memory or
+ * stream), Z1_EALIGN, Z1_EHIP (no GPU current, launch failure).
  * ------------------------------------------------------------------------ */
 z1_status z1_grad_norm_sq_pair(z1_plan *plan, double *d_pair, z1_stream stream);
 z1_status z1_norm_combine(const double *d_pairs, int32_t n, double *d_S, z1_stream stream);
@@ -536,13 +540,17 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
  *                           and the half-width bufs[4]: 30 B per element
  *   Z1_PROBE_ACCUM_TRAFFIC  read the half-width bufs[0] and bufs[1], write
  *                           bufs[1]: 10 B per element
+ *   Z1_PROBE_SLOTS_TRAFFIC  read the half-width bufs[0..G-1], write bufs[G]
+ *                           (G = n_bufs - 1 in [2, 8]): 2G + 4 B per element,
+ *                           the first resident-slot accumulation pass
  * The contents written are meaningless.  Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
  * ------------------------------------------------------------------------ */
 enum {
     Z1_PROBE_READ = 0,
     Z1_PROBE_WRITE = 1,
     Z1_PROBE_ADAMW_TRAFFIC = 2,
-    Z1_PROBE_ACCUM_TRAFFIC = 3
+    Z1_PROBE_ACCUM_TRAFFIC = 3,
+    Z1_PROBE_SLOTS_TRAFFIC = 4
 };
 z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, int64_t n_vec,
                    z1_stream stream);

@@ -33,7 +33,7 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_probe_plan", "z1_schedule_create", "z1_schedule_destroy", "z1_schedule_query",
            "z1_adamw_step_scheduled", "z1_grad_norm_sq_pair", "z1_norm_combine")
 
-PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3}
+PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3, "slots_traffic": 4}
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
 LAYOUTS = {"full": 0, "packed": 1}
@@ -173,6 +173,41 @@ def _dptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check_tensors(items) -> None:
+    """Reject tensors the library would read or write out of bounds or
+    misread.  items: (tensor, name, dtype, min_elems) with dtype None meaning
+    any dtype and min_elems then counted in bytes.  Every tensor is checked
+    for dtype, contiguity and size first, then every tensor for its device
+    (the current GPU).  None and int (a raw device address) pass unchecked:
+    the caller vouches for them."""
+    tensors = []
+    for t, name, dtype, min_elems in items:
+        if t is None or isinstance(t, int):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch tensor or a device address, "
+                            f"got {type(t).__name__}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: not contiguous")
+        have = t.numel() if dtype is not None else t.numel() * t.element_size()
+        if have < min_elems:
+            unit = "elements" if dtype is not None else "bytes"
+            raise ValueError(f"{name}: {have} {unit}, the call touches {min_elems}")
+        tensors.append((t, name))
+    for t, name in tensors:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: on {t.device}, expected the current GPU")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name}: on {t.device}, expected "
+                             f"cuda:{torch.cuda.current_device()}")
+
+
+def _check_tensor(t, name: str, dtype, min_elems: int) -> None:
+    _check_tensors([(t, name, dtype, min_elems)])
+
+
 def z1_abi_version() -> int:
     return int(lib.z1_abi_version())
 
@@ -244,7 +279,20 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
     the arenas are raw device addresses."""
     n = _i64(numel)
     K = len(grads)
+    if layout not in LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    if kind not in PLAN_KINDS:
+        raise ValueError(f"unknown plan kind {kind!r}")
+    # what the plan will touch: slice [start, start+len) of every tensor and
+    # arena_elems of every arena (and of each packed bf16 shard)
+    st_, ln_, _, need = z1_shard_plan(n, dp_size, rank, kind, rows)
+    bf16, f32 = torch.bfloat16, torch.float32
+    items = [(a, name, f32, need) for name, a in (("master", master), ("exp_avg", exp_avg),
+                                                  ("exp_avg_sq", exp_avg_sq), ("acc", acc))]
     if layout == "packed":
+        items.append((weights, "weights (packed shard)", bf16, need))
+        items += [(g, f"grads[{k}] (packed shard)", bf16, need) for k, g in enumerate(grads)]
+        _check_tensors(items)
         wp = (ctypes.c_void_p * 1)(_dptr(weights))
         gp = (ctypes.c_void_p * max(K, 1))(*[_dptr(g) for g in grads])
     else:
@@ -253,6 +301,13 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
                 raise ValueError("grads[k] must list one tensor per parameter")
         if len(weights) != n.size:
             raise ValueError("weights must list one tensor per parameter")
+        for i in range(n.size):
+            if ln_[i] == 0:
+                continue
+            end = int(st_[i] + ln_[i])
+            items.append((weights[i], f"weights[{i}]", bf16, end))
+            items += [(grads[k][i], f"grads[{k}][{i}]", bf16, end) for k in range(K)]
+        _check_tensors(items)
         wp = (ctypes.c_void_p * max(n.size, 1))(*[_dptr(w) for w in weights])
         gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
     arena = [master, exp_avg, exp_avg_sq, acc]
@@ -305,17 +360,21 @@ def z1_accum_grads_range(plan: Plan, k_begin: int, k_end: int, stream=None) -> N
 
 def z1_grad_norm_sq(plan: Plan, d_S, stream=None) -> None:
     """Writes S into the device float64 tensor d_S (first element)."""
+    _check_tensor(d_S, "d_S", torch.float64, 1)
     _check(lib.z1_grad_norm_sq(plan.handle, _dptr(d_S), _stream(stream)), "z1_grad_norm_sq")
 
 
 def z1_grad_norm_sq_pair(plan: Plan, d_pair, stream=None) -> None:
     """S of this rank as the pair (hi, lo) in the device float64 tensor d_pair[:2]."""
+    _check_tensor(d_pair, "d_pair", torch.float64, 2)
     _check(lib.z1_grad_norm_sq_pair(plan.handle, _dptr(d_pair), _stream(stream)),
            "z1_grad_norm_sq_pair")
 
 
 def z1_norm_combine(d_pairs, n: int, d_S, stream=None) -> None:
     """S from n gathered pairs (device float64 [n, 2]) added in order, into d_S."""
+    _check_tensors([(d_pairs, "d_pairs", torch.float64, 2 * int(n)),
+                    (d_S, "d_S", torch.float64, 1)])
     _check(lib.z1_norm_combine(_dptr(d_pairs), int(n), _dptr(d_S), _stream(stream)),
            "z1_norm_combine")
 
@@ -323,6 +382,7 @@ def z1_norm_combine(d_pairs, n: int, d_S, stream=None) -> None:
 def z1_adamw_step(plan: Plan, *, lr, beta1, beta2, eps, weight_decay, clip, step,
                   d_S=None, stream=None) -> None:
     hp = AdamWHP(lr, beta1, beta2, eps, weight_decay, clip, int(step))
+    _check_tensor(d_S, "d_S", torch.float64, 1)
     _check(lib.z1_adamw_step(plan.handle, ctypes.byref(hp), _dptr(d_S), _stream(stream)),
            "z1_adamw_step")
 
@@ -373,12 +433,14 @@ def z1_schedule_query(sched: Schedule):
 
 
 def z1_adamw_step_scheduled(plan: Plan, sched: Schedule, d_S=None, stream=None) -> None:
+    _check_tensor(d_S, "d_S", torch.float64, 1)
     _check(lib.z1_adamw_step_scheduled(plan.handle, sched.handle, _dptr(d_S), _stream(stream)),
            "z1_adamw_step_scheduled")
 
 
 def z1_grad_norm_sq_acc(plan: Plan, d_S, stream=None) -> None:
     """S of the acc arena as the caller filled it (e.g. by a reduce-scatter)."""
+    _check_tensor(d_S, "d_S", torch.float64, 1)
     _check(lib.z1_grad_norm_sq_acc(plan.handle, _dptr(d_S), _stream(stream)),
            "z1_grad_norm_sq_acc")
 
@@ -425,6 +487,12 @@ def z1_pack_create(numel: Sequence[int], dp_size: int, grads: Sequence[Sequence]
         if len(gk) != n.size:
             raise ValueError("grads[k] must list one tensor per parameter")
     r = _i64(rows) if rows is not None else None
+    if kind not in PLAN_KINDS:
+        raise ValueError(f"unknown plan kind {kind!r}")
+    seg_need = z1_pack_layout(n, dp_size, kind, r)
+    _check_tensors([(gk[i], f"grads[{k}][{i}]", torch.bfloat16, int(n[i]))
+                    for k, gk in enumerate(grads) for i in range(n.size) if n[i]] +
+                   [(send, "send", torch.float32, dp_size * seg_need)])
     gp = (ctypes.c_void_p * max(K * n.size, 1))(*[_dptr(g) for gk in grads for g in gk])
     b = PackBind(n_tensors=n.size, dp_size=dp_size, n_micro=K, plan_kind=PLAN_KINDS[kind],
                  numel=_p64(n), rows=_p64(r) if r is not None else None,
@@ -453,11 +521,18 @@ def z1_probe_plan(plan: Plan, kind: str = "adamw", stream=None) -> None:
 
 def z1_probe(kind: str, bufs: Sequence, n_vec: int, stream=None) -> None:
     """Traffic-only streaming kernel (see z1.h); bufs are tensors or addresses."""
+    nv = int(n_vec)
+    need = {"read": (16 * nv, 4), "write": (16 * nv,),
+            "adamw_traffic": (16 * nv,) * 4 + (8 * nv,),
+            "accum_traffic": (8 * nv, 16 * nv),
+            "slots_traffic": (8 * nv,) * (len(bufs) - 1) + (16 * nv,)}[kind]
+    _check_tensors([(b, f"bufs[{j}]", None, nb) for j, (b, nb) in enumerate(zip(bufs, need))])
     arr = (ctypes.c_void_p * max(len(bufs), 1))(*[_dptr(b) for b in bufs])
     _check(lib.z1_probe(PROBES[kind], arr, len(bufs), int(n_vec), _stream(stream)), "z1_probe")
 
 
 def z1_probe_copy(src, dst, n_bytes: int, stream=None) -> None:
+    _check_tensors([(src, "src", None, int(n_bytes)), (dst, "dst", None, int(n_bytes))])
     _check(lib.z1_probe_copy(_dptr(src), _dptr(dst), int(n_bytes), _stream(stream)),
            "z1_probe_copy")
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <memory>
 #include <new>
 #include <vector>
@@ -21,7 +22,8 @@ struct z1_plan {
     int device = -1;  // the GPU current at creation; every call must run there
     int32_t n = 0, K = 0, dp = 0, rank = 0;
     int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
-    int grid = 0;
+    int64_t n_tile = 0;   // leading whole-tile pieces of the table
+    int grid = 0, max_blocks = 0;
     std::vector<int64_t> start, len, arena_off;
     // device memory owned by the plan
     Chunk *d_chunks = nullptr;
@@ -86,6 +88,19 @@ bool stream_on(int dev, z1_stream stream)
         return false;
     }
     return d == dev;
+}
+
+// True when p is device memory of GPU `dev` (or managed memory), as the HIP
+// runtime records it; host memory, unknown pointers and another GPU's memory
+// are not.
+bool device_memory_on(int dev, const void *ptr)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) && a.device == dev;
 }
 
 // A call on an object created on GPU `owner` may enqueue work only with that
@@ -199,11 +214,18 @@ z1_status device_alloc(T **out, size_t count)
     return Z1_OK;
 }
 
-z1::LaunchGeom geom(const z1_plan *p) { return z1::LaunchGeom{p->d_chunks, p->n_chunks, p->grid}; }
+z1::LaunchGeom geom(const z1_plan *p)
+{
+    z1::LaunchGeom g{p->d_chunks, p->n_chunks, p->grid};
+    g.n_tile = p->n_tile;
+    g.max_blocks = p->max_blocks;
+    return g;
+}
 
 // Appends the pieces of slices [start[i], start[i]+len[i]) of tensors 0..n-1,
 // cut at multiples of `chunk` inside each tensor; element e of slice i lands
-// at dst_base + arena_off[i] + e.
+// at dst_base + arena_off[i] + e.  The table stays in this (tensor) order;
+// each kernel picks its own issue order over it on the device.
 void append_chunks(std::vector<Chunk> &chunks, int32_t n, const int64_t *start, const int64_t *len,
                    const int64_t *arena_off, int64_t dst_base, int64_t chunk)
 {
@@ -223,27 +245,6 @@ void append_chunks(std::vector<Chunk> &chunks, int32_t n, const int64_t *start, 
             s = e;
         }
     }
-}
-
-// Issue order: consecutive workgroups alternate between kInterleave distant
-// parts of the table (entry j is piece (j % P) * m + j / P).  The hardware
-// hands workgroups to the 8 XCDs round-robin, so with P = 8 each XCD walks
-// one contiguous eighth of the shard through its own L2.  Measured on the
-// 7B shard, P = 8 takes the accumulation pass from 1.44 to 1.38 ms; results
-// do not depend on the order (elements are independent, the norm is exactly
-// rounded).
-void interleave_chunks(std::vector<Chunk> &chunks)
-{
-    if (chunks.size() <= (size_t)z1::kInterleave)
-        return;
-    const size_t P = z1::kInterleave, N = chunks.size(), m = (N + P - 1) / P;
-    std::vector<Chunk> re;
-    re.reserve(N);
-    for (size_t i = 0; i < m; ++i)
-        for (size_t j = 0; j < P; ++j)
-            if (j * m + i < N)
-                re.push_back(chunks[j * m + i]);
-    chunks.swap(re);
 }
 
 int64_t chunk_or_default(int64_t c) { return c ? c : z1::kDefaultChunk; }
@@ -515,7 +516,12 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     for (int32_t i = 0; i < n; ++i)
         p->L += p->len[i];
     append_chunks(chunks, n, p->start.data(), p->len.data(), p->arena_off.data(), 0, chunk);
-    interleave_chunks(chunks);
+    // whole-tile pieces first (AdamW runs them in a straight-line kernel of
+    // their own), each group in tensor order
+    const auto is_tile = [](const Chunk &c) {
+        return c.src % z1::kVec == 0 && c.count == z1::kTileElems;
+    };
+    p->n_tile = std::stable_partition(chunks.begin(), chunks.end(), is_tile) - chunks.begin();
     p->n_chunks = (int64_t)chunks.size();
     if (p->n_chunks > INT32_MAX)
         return Z1_EINVAL;
@@ -523,6 +529,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if (b->max_blocks > 0 && grid > b->max_blocks)
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
+    p->max_blocks = b->max_blocks;
 
     if ((p->device = current_device()) < 0)
         return Z1_EHIP;
@@ -701,6 +708,14 @@ z1_status z1_norm_combine(const double *d_pairs, int32_t n, double *d_S, z1_stre
         return Z1_EINVAL;
     if (!aligned(d_pairs, 16) || !aligned(d_S, 8))
         return Z1_EALIGN;
+    // no plan owns this call: the current GPU must own the stream and both
+    // buffers, as a plan's GPU must for the calls on a plan
+    const int dev = current_device();
+    if (dev < 0)
+        return Z1_EHIP;
+    if (!stream_on(dev, stream) || !device_memory_on(dev, d_pairs) ||
+        !device_memory_on(dev, d_S))
+        return Z1_EINVAL;
     return z1::launch_norm_combine(reinterpret_cast<const DD *>(d_pairs), n, d_S,
                                    reinterpret_cast<hipStream_t>(stream)) == hipSuccess
                ? Z1_OK
@@ -825,7 +840,6 @@ static z1_status pack_create_body(z1_pack **out, const z1_pack_bind *b, z1_strea
                            ov.data(), &ae);
         append_chunks(chunks, n, sv.data(), lv.data(), ov.data(), (int64_t)r * seg, chunk);
     }
-    interleave_chunks(chunks);
     p->n_chunks = (int64_t)chunks.size();
     if (p->n_chunks > INT32_MAX)
         return Z1_EINVAL;

@@ -14,7 +14,14 @@ constexpr int kBlock = 256;
 constexpr int kVec = 4;
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxChunk = 1 << 20;
-constexpr int kInterleave = 8;  // chunk issue order: 8 interleaved regions
+// The chunk table is stored in tensor order.  The accumulation and norm
+// kernels issue it in kInterleave interleaved regions (consecutive workgroups
+// land on different XCDs, each XCD walking one contiguous region); AdamW
+// issues it in table order.
+constexpr int kInterleave = 8;
+// AdamW's straight-line unit: 4 vectors of 4 elements per lane.  A piece of
+// exactly this many elements starting on a vector boundary is a whole tile.
+constexpr int64_t kTileElems = 4 * kBlock * kVec;
 constexpr int kMaxSlots = 8;     // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
@@ -62,6 +69,11 @@ struct LaunchGeom {
     const Chunk *chunks;  // device
     int64_t n_chunks;
     int grid;             // workgroups for the chunk kernels
+    // a plan's table starts with its n_tile whole-tile pieces (kTileElems
+    // elements from a vector boundary), which AdamW runs in a kernel of their
+    // own; max_blocks > 0 caps each AdamW grid (0: one workgroup per piece)
+    int64_t n_tile = 0;
+    int max_blocks = 0;
 };
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,

@@ -53,12 +53,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef Z1_UNROLL_SLOTS_WIDE
 #define Z1_UNROLL_SLOTS_WIDE 2
 #endif
-#ifndef Z1_UNROLL_ADAM
-#define Z1_UNROLL_ADAM 4
-#endif
 
-template <typename T>
-__device__ __forceinline__ T ld_stream(const T *p)
+template <typename P>
+__device__ __forceinline__ auto ld_stream(P p)
 {
 #if Z1_NT_LOAD
     return __builtin_nontemporal_load(p);
@@ -67,14 +64,29 @@ __device__ __forceinline__ T ld_stream(const T *p)
 #endif
 }
 
-template <typename T>
-__device__ __forceinline__ void st_stream(T *p, T x)
+template <typename P, typename T>
+__device__ __forceinline__ void st_stream(P p, T x)
 {
 #if Z1_NT_STORE
     __builtin_nontemporal_store(x, p);
 #else
     *p = x;
 #endif
+}
+
+// A pointer read from one of the plan's pointer tables (bf16 weights,
+// gradient slots) is generic to the compiler, which then emits flat
+// accesses: those count against both the vector-memory and the LDS wait
+// counters and may complete out of order with global accesses, so every use
+// of a load then waits for all outstanding memory operations.  Every such
+// pointer is device memory; in the global address space the accesses are
+// global ones and each use waits only for its own loads.
+template <typename T>
+using gmem = __attribute__((address_space(1))) T;
+template <typename T>
+__device__ __forceinline__ gmem<T> *to_global(T *p)
+{
+    return (gmem<T> *)p;
 }
 
 // ---------------------------------------------------------------- bf16 ----
@@ -185,6 +197,31 @@ __device__ __forceinline__ Span span_of(const Chunk &ch)
     return s;
 }
 
+// Issue order of the accumulation and norm kernels: the c-th workgroup (or
+// grid-stride iteration) takes table entry issue_order(c).  The table is cut
+// into kInterleave regions of as equal size as possible (the first n mod
+// kInterleave one entry longer) and consecutive workgroups alternate between
+// them, entry i of region j going to workgroup i * kInterleave + j; the
+// entries left over after the last full round go to the longer regions.  The
+// hardware hands workgroups to the 8 XCDs round-robin, so each XCD walks one
+// contiguous region through its own L2.  A bijection on [0, n): results do
+// not depend on it (elements are independent, norm partials are indexed by
+// table entry and reduced in table order).
+__device__ __forceinline__ int64_t issue_order(int64_t c, int64_t n)
+{
+    constexpr int64_t P = kInterleave;
+    const int64_t q = n / P, r = n % P;
+    int64_t i, j;
+    if (c < P * q) {
+        i = c / P;
+        j = c % P;
+    } else {
+        i = q;
+        j = c - P * q;
+    }
+    return j * q + (j < r ? j : r) + i;
+}
+
 // Calls f(e) for every element of the partial vectors (piece-relative
 // element index e + lead, i.e. the index into the lead-adjusted pointers).
 template <typename F>
@@ -248,11 +285,12 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
     __shared__ DD lds[kBlock / 64];
     const int t = (int)threadIdx.x;
     for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const Chunk ch = chunks[c];
+        const int64_t ci = issue_order(c, n_chunks);
+        const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
-        const uint16_t *g = gtab[ch.tensor] + (ch.src - sp.lead);
+        const gmem<const uint16_t> *g = to_global(gtab[ch.tensor]) + (ch.src - sp.lead);
         float *a = acc + (ch.dst - sp.lead);
-        const u32x2 *gv = reinterpret_cast<const u32x2 *>(g);
+        const gmem<const u32x2> *gv = reinterpret_cast<const gmem<const u32x2> *>(g);
         f32x4 *av = reinterpret_cast<f32x4 *>(a);
         double hi = 0.0, lo = 0.0;
 
@@ -305,7 +343,7 @@ __global__ __launch_bounds__(kBlock) void k_accum(const Chunk *__restrict__ chun
         if (LAST) {
             block_reduce_dd<kBlock>(hi, lo, lds);
             if (t == 0)
-                partials[c] = DD{hi, lo};
+                partials[ci] = DD{hi, lo};
         }
     }
 }
@@ -329,12 +367,13 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
     __shared__ DD lds[kBlock / 64];
     const int t = (int)threadIdx.x;
     for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const Chunk ch = chunks[c];
+        const int64_t ci = issue_order(c, n_chunks);
+        const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
-        const uint16_t *g[G];
+        const gmem<const uint16_t> *g[G];
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            g[j] = gtab[(int64_t)j * slot_stride + ch.tensor] + (ch.src - sp.lead);
+            g[j] = to_global(gtab[(int64_t)j * slot_stride + ch.tensor]) + (ch.src - sp.lead);
         float *a = acc + (ch.dst - sp.lead);
         f32x4 *av = reinterpret_cast<f32x4 *>(a);
         double hi = 0.0, lo = 0.0;
@@ -348,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
                 const int q = q0 + u * kBlock + t;
 #pragma unroll
                 for (int j = 0; j < G; ++j)
-                    gr[j][u] = ld_stream(reinterpret_cast<const u32x2 *>(g[j]) + q);
+                    gr[j][u] = ld_stream(reinterpret_cast<const gmem<const u32x2> *>(g[j]) + q);
                 if (!FIRST)
                     ar[u] = ld_stream(av + q);
             }
@@ -373,7 +412,7 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
             f32x4 ar = {};
 #pragma unroll
             for (int j = 0; j < G; ++j)
-                gr[j] = ld_stream(reinterpret_cast<const u32x2 *>(g[j]) + q);
+                gr[j] = ld_stream(reinterpret_cast<const gmem<const u32x2> *>(g[j]) + q);
             if (!FIRST)
                 ar = ld_stream(av + q);
             f32x4 s = accum_vec<FIRST, false>(gr[0], ar);
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
         if (LAST) {
             block_reduce_dd<kBlock>(hi, lo, lds);
             if (t == 0)
-                partials[c] = DD{hi, lo};
+                partials[ci] = DD{hi, lo};
         }
     }
 }
@@ -419,7 +458,8 @@ __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ c
     __shared__ DD lds[kBlock / 64];
     const int t = (int)threadIdx.x;
     for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-        const Chunk ch = chunks[c];
+        const int64_t ci = issue_order(c, n_chunks);
+        const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
         const float *a = acc + (ch.dst - sp.lead);
         const f32x4 *av = reinterpret_cast<const f32x4 *>(a);
@@ -448,7 +488,7 @@ __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ c
         for_partial_elems(sp, [&](int e) { dd_add_sq(hi, lo, a[e]); });
         block_reduce_dd<kBlock>(hi, lo, lds);
         if (t == 0)
-            partials[c] = DD{hi, lo};
+            partials[ci] = DD{hi, lo};
     }
 }
 
@@ -578,93 +618,172 @@ __device__ __forceinline__ void traffic_vec(f32x4 a, f32x4 &p, f32x4 &m, f32x4 &
     w.y = (__float_as_uint(p.z) >> 16) | (__float_as_uint(p.w) & 0xFFFF0000u);
 }
 
-// MATH = false is a measurement twin: the same chunk walk, loads and stores
-// over the same buffers, with the arithmetic replaced by traffic_vec, so the
-// cost of the update itself can be read off on the step's own buffers.
-// TABLE = true takes the step's constants from row state[0] of a per-step
-// table instead of the kernel argument (a replayed graph then advances from
-// step to step); when the table is exhausted the whole grid returns at once.
-template <int U, bool MATH, bool TABLE>
-__global__ __launch_bounds__(kBlock) void k_adamw(const Chunk *__restrict__ chunks,
-                                                  int64_t n_chunks,
-                                                  uint16_t *const *__restrict__ wtab,
-                                                  const Scale *__restrict__ scales,
-                                                  const float *__restrict__ acc,
-                                                  float *__restrict__ master,
-                                                  float *__restrict__ exp_avg,
-                                                  float *__restrict__ exp_avg_sq,
-                                                  const AdamConsts k_arg,
-                                                  const double *__restrict__ S,
-                                                  const AdamConsts *__restrict__ table,
-                                                  int64_t n_rows,
-                                                  const int64_t *__restrict__ state)
+// The clip coefficient from the device S: clip / (sqrt(S) + 1e-6) clamped at
+// 1 (a NaN norm gives a NaN coefficient); 1 when clipping is off (S is then
+// not read, and may be NULL).
+__device__ __forceinline__ double clip_coef(const AdamConsts &k, const double *__restrict__ S)
 {
-    AdamConsts k = k_arg;
+    if (!(k.clip > 0.0))
+        return 1.0;
+    const double cc = k.clip / (sqrt(S[0]) + 1e-6);
+    return cc >= 1.0 ? 1.0 : cc;
+}
+
+// U consecutive vectors per lane (vector q0 + u * kBlock + t for u < U) of
+// the piece ch: all loads issued first, then the clip coefficient, the
+// tensor's rate and its bf16 pointer (lookups whose latency then hides behind
+// the loads), then update and store vector by vector.  MATH = false is the
+// measurement twin (traffic_vec).
+template <int U, bool MATH>
+__device__ __forceinline__ void adamw_vectors(int q0, const Chunk &ch, int lead,
+                                              const f32x4 *__restrict__ av,
+                                              f32x4 *__restrict__ pv, f32x4 *__restrict__ mv,
+                                              f32x4 *__restrict__ vv,
+                                              uint16_t *const *__restrict__ wtab,
+                                              const Scale *__restrict__ scales,
+                                              const AdamConsts &k, const double *__restrict__ S)
+{
+    // every access is a workgroup-uniform base (vector q0 of the stream) plus
+    // a 32-bit byte offset that depends only on the lane and u, so all of them
+    // take a scalar base and the lanes share U offset registers
+    const int t = (int)threadIdx.x;
+    const char *ab = reinterpret_cast<const char *>(av + q0);
+    char *pb = reinterpret_cast<char *>(pv + q0);
+    char *mb = reinterpret_cast<char *>(mv + q0);
+    char *vb = reinterpret_cast<char *>(vv + q0);
+    f32x4 ar[U], pr[U], mr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
+        ar[u] = ld_stream(reinterpret_cast<const f32x4 *>(ab + o));
+        pr[u] = ld_stream(reinterpret_cast<const f32x4 *>(pb + o));
+        mr[u] = ld_stream(reinterpret_cast<const f32x4 *>(mb + o));
+        vr[u] = ld_stream(reinterpret_cast<const f32x4 *>(vb + o));
+        // loads issued vector by vector, all ahead of the arithmetic: left to
+        // itself the scheduler reorders them and sinks the last ones below the
+        // first update, and the waits then drain every load before the rest
+        // of the tile is issued; in this order the update of vector u waits
+        // only for its own four loads
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const double c = MATH ? clip_coef(k, S) : 1.0;
+    const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
+    gmem<char> *wb8 = reinterpret_cast<gmem<char> *>(to_global(wtab[ch.tensor]) + (ch.src - lead)) +
+                      (int64_t)q0 * 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
+        u32x2 wb;
+        if constexpr (MATH)
+            adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
+        else
+            traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
+        st_stream(reinterpret_cast<f32x4 *>(pb + o), pr[u]);
+        st_stream(reinterpret_cast<f32x4 *>(mb + o), mr[u]);
+        st_stream(reinterpret_cast<f32x4 *>(vb + o), vr[u]);
+        st_stream(reinterpret_cast<gmem<u32x2> *>(wb8 + o / 2), wb);
+    }
+}
+
+// The step's constants: the kernel argument, or row state[0] of a per-step
+// table (false when the table is exhausted: the whole grid then returns at
+// once).
+template <bool TABLE>
+__device__ __forceinline__ bool adamw_setup(const AdamConsts &k_arg,
+                                            const AdamConsts *__restrict__ table, int64_t n_rows,
+                                            const int64_t *__restrict__ state, AdamConsts &k)
+{
+    k = k_arg;
     if constexpr (TABLE) {
         const int64_t row = state[0];
         if (row >= n_rows)
-            return;
+            return false;
         k = table[row];
     }
-    double c = 1.0;
-    if (MATH && k.clip > 0.0) {
-        const double cc = k.clip / (sqrt(S[0]) + 1e-6);
-        c = cc >= 1.0 ? 1.0 : cc;  // clamp at 1; a NaN norm gives a NaN coefficient
+    return true;
+}
+
+// AdamW over whole tiles: table entries [0, n) are pieces of exactly
+// kTileElems elements starting on a vector boundary (every piece of the
+// 7B-shaped lists but the norm weights' slices), one straight-line tile of 4
+// vectors per lane each, in table (tensor) order.  The only lookup before the
+// first vector load is the piece's descriptor, and with nothing else in the
+// kernel the update of each vector waits only for its own loads.  ONE: one
+// workgroup per piece and no loop, so no store of an earlier piece is in
+// flight when the loads are consumed (loads and stores share one counter).
+// Measured on the 7B shard against the earlier single kernel (8-way
+// interleaved issue order, 3 waves per SIMD): an 8-way order was 1-4% slower
+// for this kernel, whose five streams already spread every XCD over the
+// whole shard.
+// MATH = false is a measurement twin: the same walk, loads and stores over
+// the same buffers, with the arithmetic replaced by traffic_vec, so the cost
+// of the update itself can be read off on the step's own buffers.
+// TABLE = true takes the step's constants from the per-step table.
+template <bool MATH, bool TABLE, bool ONE>
+__global__ __launch_bounds__(kBlock) void k_adamw_tiles(
+    const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
+    const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
+    float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
+    const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
+    const int64_t *__restrict__ state)
+{
+    AdamConsts k;
+    if (!adamw_setup<TABLE>(k_arg, table, n_rows, state, k))
+        return;
+    for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
+        const Chunk ch = chunks[ci];
+        const int64_t off = ch.dst;
+        adamw_vectors<4, MATH>(0, ch, 0, reinterpret_cast<const f32x4 *>(acc + off),
+                               reinterpret_cast<f32x4 *>(master + off),
+                               reinterpret_cast<f32x4 *>(exp_avg + off),
+                               reinterpret_cast<f32x4 *>(exp_avg_sq + off), wtab, scales, k, S);
+        if constexpr (ONE)
+            break;
     }
+}
+
+// AdamW over any other pieces (table entries [0, n) of the pointer given):
+// whole tiles in a loop, else 2 vectors, then 1, per lane, and the partial
+// head and tail vectors element by element.
+template <bool MATH, bool TABLE>
+__global__ __launch_bounds__(kBlock) void k_adamw_rest(
+    const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
+    const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
+    float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
+    const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
+    const int64_t *__restrict__ state)
+{
+    AdamConsts k;
+    if (!adamw_setup<TABLE>(k_arg, table, n_rows, state, k))
+        return;
     const int t = (int)threadIdx.x;
-    for (int64_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
+    for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
         const Chunk ch = chunks[ci];
         const Span sp = span_of(ch);
-        const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
-        uint16_t *w = wtab[ch.tensor] + (ch.src - sp.lead);
         const int64_t off = ch.dst - sp.lead;
+        const f32x4 *av = reinterpret_cast<const f32x4 *>(acc + off);
+        f32x4 *pv = reinterpret_cast<f32x4 *>(master + off);
+        f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
+        f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
+        if (sp.lead == 0 && ch.count % kTileElems == 0) {
+            for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
+                adamw_vectors<4, MATH>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k, S);
+            continue;
+        }
+        int q0 = sp.qb;
+        for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
+            adamw_vectors<2, MATH>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+        for (int q = q0 + t; q < sp.qe; q += kBlock)
+            adamw_vectors<1, MATH>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+        if (sp.lead == 0 && sp.end % kVec == 0)
+            continue;
+        const double c = MATH ? clip_coef(k, S) : 1.0;
+        const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
+        gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
         const float *a = acc + off;
         float *p = master + off;
         float *m = exp_avg + off;
         float *v = exp_avg_sq + off;
-        const f32x4 *av = reinterpret_cast<const f32x4 *>(a);
-        f32x4 *pv = reinterpret_cast<f32x4 *>(p);
-        f32x4 *mv = reinterpret_cast<f32x4 *>(m);
-        f32x4 *vv = reinterpret_cast<f32x4 *>(v);
-        u32x2 *wv = reinterpret_cast<u32x2 *>(w);
-
-        int q0 = sp.qb;
-        for (; q0 + U * kBlock <= sp.qe; q0 += U * kBlock) {
-            f32x4 ar[U], pr[U], mr[U], vr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = q0 + u * kBlock + t;
-                ar[u] = ld_stream(av + q);
-                pr[u] = ld_stream(pv + q);
-                mr[u] = ld_stream(mv + q);
-                vr[u] = ld_stream(vv + q);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = q0 + u * kBlock + t;
-                u32x2 wb;
-                if constexpr (MATH)
-                    adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
-                else
-                    traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
-                st_stream(pv + q, pr[u]);
-                st_stream(mv + q, mr[u]);
-                st_stream(vv + q, vr[u]);
-                st_stream(wv + q, wb);
-            }
-        }
-        for (int q = q0 + t; q < sp.qe; q += kBlock) {
-            f32x4 pr = ld_stream(pv + q), mr = ld_stream(mv + q), vr = ld_stream(vv + q);
-            u32x2 wb;
-            if constexpr (MATH)
-                adamw_vec(ld_stream(av + q), pr, mr, vr, wb, k, tr, c);
-            else
-                traffic_vec(ld_stream(av + q), pr, mr, vr, wb);
-            st_stream(pv + q, pr);
-            st_stream(mv + q, mr);
-            st_stream(vv + q, vr);
-            st_stream(wv + q, wb);
-        }
         for_partial_elems(sp, [&](int e) {
             if constexpr (MATH) {
                 const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
@@ -846,15 +965,43 @@ hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_
     return hipGetLastError();
 }
 
+// AdamW over a plan's table: the leading whole-tile pieces in k_adamw_tiles
+// (one workgroup each unless max_blocks caps the grid), the rest in
+// k_adamw_rest, on the same stream.
+template <bool MATH, bool TABLE>
+void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
+                         const float *acc, float *master, float *m, float *v,
+                         const AdamConsts &k, const double *S, const AdamConsts *table,
+                         int64_t n_rows, const int64_t *state, hipStream_t s)
+{
+    const dim3 block(kBlock);
+    const int64_t nt = geo.n_tile, nr = geo.n_chunks - geo.n_tile;
+    if (nt > 0) {
+        if (geo.max_blocks > 0 && geo.max_blocks < nt)
+            k_adamw_tiles<MATH, TABLE, false><<<dim3((unsigned)geo.max_blocks), block, 0, s>>>(
+                geo.chunks, nt, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
+                state);
+        else
+            k_adamw_tiles<MATH, TABLE, true><<<dim3((unsigned)nt), block, 0, s>>>(
+                geo.chunks, nt, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
+                state);
+    }
+    if (nr > 0) {
+        const int64_t g = geo.max_blocks > 0 && geo.max_blocks < nr ? geo.max_blocks : nr;
+        k_adamw_rest<MATH, TABLE><<<dim3((unsigned)g), block, 0, s>>>(
+            geo.chunks + nt, nr, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
+            state);
+    }
+}
+
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                         const float *acc, float *master, float *m, float *v,
                         const AdamConsts &k, const double *S, hipStream_t s)
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
-    k_adamw<Z1_UNROLL_ADAM, true, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
-        geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, k, S, nullptr, 0,
-        nullptr);
+    launch_adamw_kernel<true, false>(geo, weight_tab, scales, acc, master, m, v, k, S, nullptr,
+                                     0, nullptr, s);
     return hipGetLastError();
 }
 
@@ -864,9 +1011,8 @@ hipError_t launch_adamw_scheduled(const LaunchGeom &geo, uint16_t *const *weight
                                   int64_t *state, const double *S, hipStream_t s)
 {
     if (geo.n_chunks > 0)
-        k_adamw<Z1_UNROLL_ADAM, true, true><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
-            geo.chunks, geo.n_chunks, weight_tab, scales, acc, master, m, v, AdamConsts{}, S,
-            table, n_rows, state);
+        launch_adamw_kernel<true, true>(geo, weight_tab, scales, acc, master, m, v, AdamConsts{},
+                                        S, table, n_rows, state, s);
     k_schedule_advance<<<dim3(1), dim3(64), 0, s>>>(state, n_rows);
     return hipGetLastError();
 }
@@ -877,9 +1023,8 @@ hipError_t launch_adamw_traffic(const LaunchGeom &geo, uint16_t *const *weight_t
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
-    k_adamw<Z1_UNROLL_ADAM, false, false><<<dim3(geo.grid), dim3(kBlock), 0, s>>>(
-        geo.chunks, geo.n_chunks, weight_tab, nullptr, acc, master, m, v, AdamConsts{}, nullptr,
-        nullptr, 0, nullptr);
+    launch_adamw_kernel<false, false>(geo, weight_tab, nullptr, acc, master, m, v, AdamConsts{},
+                                      nullptr, nullptr, 0, nullptr, s);
     return hipGetLastError();
 }
 

@@ -111,6 +111,51 @@ __global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict_
     }
 }
 
+// The first resident-slot pass's traffic: read G half-width streams, write
+// one fp32 stream (2G + 4 bytes per element); the G pointers come by value.
+struct SlotPtrs {
+    const u32x2 *p[kMaxSlots];
+};
+
+template <int G>
+__global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__restrict__ acc,
+                                                             int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    u32x2 gr[G][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                gr[j][u] = ld(sp.p[j] + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kBlock;
+        if (i < n) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                s.x += __uint_as_float(gr[j][u].x << 16);
+                s.y += __uint_as_float(gr[j][u].y << 16);
+            }
+            st(acc + i, s);
+        }
+    }
+}
+
+template <int G>
+void launch_slots_probe(void *const *bufs, int64_t n_vec, dim3 grid, hipStream_t s)
+{
+    SlotPtrs sp{};
+    for (int j = 0; j < G; ++j)
+        sp.p[j] = static_cast<const u32x2 *>(bufs[j]);
+    k_probe_slots<G><<<grid, dim3(kBlock), 0, s>>>(sp, static_cast<f32x4 *>(bufs[G]), n_vec);
+}
+
 }  // namespace
 }  // namespace z1
 
@@ -118,11 +163,14 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
                               z1_stream stream)
 {
     using namespace z1;
-    static const int32_t need[] = {2, 1, 5, 2};
-    if (kind < Z1_PROBE_READ || kind > Z1_PROBE_ACCUM_TRAFFIC || !bufs || n_vec < 0 ||
+    static const int32_t need[] = {2, 1, 5, 2, 3};
+    if (kind < Z1_PROBE_READ || kind > Z1_PROBE_SLOTS_TRAFFIC || !bufs || n_vec < 0 ||
         n_bufs < need[kind])
         return Z1_EINVAL;
-    for (int32_t i = 0; i < need[kind]; ++i) {
+    if (kind == Z1_PROBE_SLOTS_TRAFFIC && n_bufs > kMaxSlots + 1)
+        return Z1_EINVAL;
+    const int32_t used = kind == Z1_PROBE_SLOTS_TRAFFIC ? n_bufs : need[kind];
+    for (int32_t i = 0; i < used; ++i) {
         if (!bufs[i])
             return Z1_EINVAL;
         if (reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0)
@@ -149,9 +197,21 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
             static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
             static_cast<u32x2 *>(bufs[4]), n_vec);
         break;
-    default:
+    case Z1_PROBE_ACCUM_TRAFFIC:
         k_probe_accum<<<grid, block, 0, s>>>(static_cast<const u32x2 *>(bufs[0]),
                                              static_cast<f32x4 *>(bufs[1]), n_vec);
+        break;
+    default:
+        static_assert(kMaxSlots == 8, "one case per slot count 2..kMaxSlots");
+        switch (n_bufs - 1) {
+        case 2: launch_slots_probe<2>(bufs, n_vec, grid, s); break;
+        case 3: launch_slots_probe<3>(bufs, n_vec, grid, s); break;
+        case 4: launch_slots_probe<4>(bufs, n_vec, grid, s); break;
+        case 5: launch_slots_probe<5>(bufs, n_vec, grid, s); break;
+        case 6: launch_slots_probe<6>(bufs, n_vec, grid, s); break;
+        case 7: launch_slots_probe<7>(bufs, n_vec, grid, s); break;
+        default: launch_slots_probe<8>(bufs, n_vec, grid, s); break;
+        }
         break;
     }
     return hipGetLastError() == hipSuccess ? Z1_OK : Z1_EHIP;
