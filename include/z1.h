@@ -460,6 +460,35 @@ z1_status z1_adamw_step_scheduled(z1_plan *plan, z1_schedule *schedule,
 z1_status z1_grad_norm_sq_acc(z1_plan *plan, double *d_S, z1_stream stream);
 
 /* ------------------------------------------------------------------------
+ * z1_grad_norm_sq_flat_noalloc -- z1_grad_norm_sq_acc for a contiguous fp32
+ * gradient shard, with no plan and no allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It needs
+ * no plan (whose creation allocates) and calls no hipMalloc / hipFree: its
+ * per-tile partials, the second-level stage and the arrival counter live in
+ * a fixed device array inside the library (4 MiB + 4.25 KiB per GPU, held
+ * until the process ends).  The first call on a GPU resolves that array's
+ * address there (hipGetSymbolAddress); make one call before capturing.
+ *
+ * Writes S = sum over e < n of acc[e]^2, the exact sum of the binary64
+ * squares rounded once to binary64 (the same value z1_grad_norm_sq_acc gives
+ * for a plan whose shard is these n elements in this order), to the DEVICE
+ * double *d_S.
+ *   acc    DEVICE, n floats, 16-byte aligned (may be NULL when n == 0)
+ *   n      0 <= n <= Z1_NORM_FLAT_MAX_ELEMS (2^30)
+ *   d_S    DEVICE, 8-byte aligned
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller; calls on different GPUs are independent.
+ * Errors: Z1_EINVAL (n out of range, NULL, host memory, another GPU's memory
+ * or stream), Z1_EALIGN, Z1_EHIP (no GPU current, launch failure).
+ * ------------------------------------------------------------------------ */
+#define Z1_NORM_FLAT_MAX_ELEMS (1LL << 30)
+z1_status z1_grad_norm_sq_flat_noalloc(const float *acc, int64_t n, double *d_S,
+                                       z1_stream stream);
+
+/* ------------------------------------------------------------------------
  * The step before the shard path: full-tensor accumulation into the
  * reduce-scatter send buffer.
  *

@@ -31,7 +31,8 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_grad_norm_sq_acc", "z1_pack_layout", "z1_pack_create", "z1_pack_destroy",
            "z1_pack_accum", "z1_probe", "z1_accum_grads_range", "z1_pack_accum_range",
            "z1_probe_plan", "z1_schedule_create", "z1_schedule_destroy", "z1_schedule_query",
-           "z1_adamw_step_scheduled", "z1_grad_norm_sq_pair", "z1_norm_combine")
+           "z1_adamw_step_scheduled", "z1_grad_norm_sq_pair", "z1_norm_combine",
+           "z1_grad_norm_sq_flat_noalloc")
 
 PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3, "slots_traffic": 4}
 
@@ -128,6 +129,7 @@ def _load():
         "z1_schedule_destroy": ([P], ctypes.c_int),
         "z1_schedule_query": ([P, PI64, PI64], ctypes.c_int),
         "z1_adamw_step_scheduled": ([P, P, P, P], ctypes.c_int),
+        "z1_grad_norm_sq_flat_noalloc": ([P, I64, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -443,6 +445,17 @@ def z1_grad_norm_sq_acc(plan: Plan, d_S, stream=None) -> None:
     _check_tensor(d_S, "d_S", torch.float64, 1)
     _check(lib.z1_grad_norm_sq_acc(plan.handle, _dptr(d_S), _stream(stream)),
            "z1_grad_norm_sq_acc")
+
+
+NORM_FLAT_MAX_ELEMS = 1 << 30
+
+
+def z1_grad_norm_sq_flat_noalloc(acc, n: int, d_S, stream=None) -> None:
+    """S of the first n elements of a contiguous fp32 buffer, into d_S; no
+    plan, no device allocation (the library's fixed scratch array)."""
+    _check_tensors([(acc, "acc", torch.float32, int(n)), (d_S, "d_S", torch.float64, 1)])
+    _check(lib.z1_grad_norm_sq_flat_noalloc(_dptr(acc), int(n), _dptr(d_S), _stream(stream)),
+           "z1_grad_norm_sq_flat_noalloc")
 
 
 def z1_pack_layout(numel: Sequence[int], dp_size: int, kind: str = "per_tensor",

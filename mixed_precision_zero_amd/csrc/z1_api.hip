@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -59,6 +60,46 @@ struct z1_pack {
     const uint16_t **d_grads = nullptr;  // [K][n]
     int32_t next_k = 0;
 };
+
+// --------------------------------------------------------------------------
+// Scratch of the entry point that allocates nothing (z1_grad_norm_sq_flat_noalloc):
+// the per-tile norm partials, the finalise's second-level stage and its
+// arrival counter, in one file-scope device array.  Each GPU the library runs
+// on holds its own copy until the process ends; every call on a GPU shares it.
+constexpr int64_t kFlatMaxTiles = Z1_NORM_FLAT_MAX_ELEMS / z1::kTileElems;
+constexpr size_t kScratchPartials = (size_t)kFlatMaxTiles * sizeof(DD);  // 4 MiB
+constexpr size_t kScratchStage = (size_t)z1::kFinStages * sizeof(DD);     // 4 KiB
+constexpr size_t kScratchBytes = kScratchPartials + kScratchStage + 256;  // + counter
+static_assert(Z1_NORM_FLAT_MAX_ELEMS % z1::kTileElems == 0, "whole tiles");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on each GPU, resolved once per GPU (with that
+// GPU current) by hipGetSymbolAddress: in host code the array's name stands
+// for a host-side placeholder, never for device memory.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+void *scratch_on(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -1069,6 +1110,31 @@ z1_status z1_probe_plan(z1_plan *p, int32_t kind, z1_stream stream)
         hipSuccess)
         return Z1_EHIP;
     return Z1_OK;
+}
+
+z1_status z1_grad_norm_sq_flat_noalloc(const float *acc, int64_t n, double *d_S,
+                                       z1_stream stream)
+{
+    if (!d_S || n < 0 || n > Z1_NORM_FLAT_MAX_ELEMS || (n > 0 && !acc))
+        return Z1_EINVAL;
+    if ((n > 0 && !aligned(acc, 16)) || !aligned(d_S, 8))
+        return Z1_EALIGN;
+    const int dev = current_device();
+    if (dev < 0)
+        return Z1_EHIP;
+    if (!stream_on(dev, stream) || !device_memory_on(dev, d_S) ||
+        (n > 0 && !device_memory_on(dev, acc)))
+        return Z1_EINVAL;
+    char *base = static_cast<char *>(scratch_on(dev));
+    if (!base)
+        return Z1_EHIP;
+    DD *partials = reinterpret_cast<DD *>(base);
+    DD *stage = reinterpret_cast<DD *>(base + kScratchPartials);
+    unsigned int *counter = reinterpret_cast<unsigned int *>(base + kScratchPartials + kScratchStage);
+    return z1::launch_norm_flat(acc, n, partials, stage, counter, d_S,
+                                reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? Z1_OK
+               : Z1_EHIP;
 }
 
 z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream)

@@ -93,6 +93,11 @@ hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials
 hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
                            unsigned int *counter, double *S, hipStream_t s,
                            DD *pair = nullptr);
+// S of a contiguous acc buffer of n elements: per-tile partials (one per
+// kTileElems elements) into `partials`, then the finalise into *S; the first
+// kernel clears *counter
+hipError_t launch_norm_flat(const float *acc, int64_t n, DD *partials, DD *stage,
+                           unsigned int *counter, double *S, hipStream_t s);
 // S from n pairs added in index order
 hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_t s);
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,

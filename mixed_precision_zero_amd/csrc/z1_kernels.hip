@@ -492,6 +492,57 @@ __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ c
     }
 }
 
+// ------------------------------------------------- norm of a flat acc ----
+// Per-tile double-double partials of sum(acc^2) over a contiguous buffer of n
+// elements: tile b covers elements [b * kTileElems, min(n, (b + 1) *
+// kTileElems)), one workgroup per tile, the same exact squares and pair
+// arithmetic as the plan's passes.  Workgroup 0 also clears the finalise's
+// arrival counter (the buffer holding it keeps whatever the last call left).
+__global__ __launch_bounds__(kBlock) void k_norm_flat(const float *__restrict__ acc, int64_t n,
+                                                      DD *__restrict__ partials,
+                                                      unsigned int *__restrict__ counter)
+{
+    __shared__ DD lds[kBlock / 64];
+    const int t = (int)threadIdx.x;
+    if (blockIdx.x == 0 && t == 0)
+        counter[0] = 0u;
+    const int64_t b = blockIdx.x;
+    const int64_t e0 = b * kTileElems;
+    if (e0 >= n)
+        return;
+    const float *a = acc + e0;
+    const f32x4 *av = reinterpret_cast<const f32x4 *>(a);
+    double hi = 0.0, lo = 0.0;
+    if (e0 + kTileElems <= n) {
+        f32x4 ar[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            ar[u] = ld_stream(av + u * kBlock + t);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            dd_add_sq(hi, lo, ar[u].x);
+            dd_add_sq(hi, lo, ar[u].y);
+            dd_add_sq(hi, lo, ar[u].z);
+            dd_add_sq(hi, lo, ar[u].w);
+        }
+    } else {
+        const int m = (int)(n - e0);  // 1 .. kTileElems - 1
+        for (int q = t; q < m / kVec; q += kBlock) {
+            const f32x4 x = ld_stream(av + q);
+            dd_add_sq(hi, lo, x.x);
+            dd_add_sq(hi, lo, x.y);
+            dd_add_sq(hi, lo, x.z);
+            dd_add_sq(hi, lo, x.w);
+        }
+        const int e = (m / kVec) * kVec + t;
+        if (t < kVec && e < m)
+            dd_add_sq(hi, lo, a[e]);
+    }
+    block_reduce_dd<kBlock>(hi, lo, lds);
+    if (t == 0)
+        partials[b] = DD{hi, lo};
+}
+
 // ------------------------------------------------------ norm finalise ----
 // Two levels in one launch: workgroup b sums the per-chunk partials of a
 // fixed contiguous range, writes its double-double to stage[b], and the
@@ -957,6 +1008,18 @@ hipError_t launch_norm_fin(const DD *partials, int64_t n_chunks, DD *stage,
     k_norm_fin<<<dim3((unsigned)g), dim3(kFinBlock), 0, s>>>(partials, n_chunks, stage, counter,
                                                              S, pair);
     return hipGetLastError();
+}
+
+hipError_t launch_norm_flat(const float *acc, int64_t n, DD *partials, DD *stage,
+                           unsigned int *counter, double *S, hipStream_t s)
+{
+    const int64_t tiles = (n + kTileElems - 1) / kTileElems;
+    k_norm_flat<<<dim3((unsigned)(tiles > 0 ? tiles : 1)), dim3(kBlock), 0, s>>>(acc, n, partials,
+                                                                              counter);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_norm_fin(partials, tiles, stage, counter, S, s);
 }
 
 hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_t s)

@@ -169,3 +169,16 @@ def test_norm_combine_host_checks():
     if not torch.cuda.is_available():
         assert L.z1_norm_combine(0x1000, 1, 0x2000, None) == B.Z1_EHIP
 
+
+def test_norm_flat_noalloc_host_checks():
+    """The entry point that allocates nothing refuses, before any device
+    query, a size beyond its stated maximum, a negative size and NULL."""
+    L = B.lib
+    assert L.z1_grad_norm_sq_flat_noalloc(0x1000, (1 << 30) + 1, 0x2000, None) == B.Z1_EINVAL
+    assert L.z1_grad_norm_sq_flat_noalloc(0x1000, -1, 0x2000, None) == B.Z1_EINVAL
+    assert L.z1_grad_norm_sq_flat_noalloc(None, 5, 0x2000, None) == B.Z1_EINVAL
+    assert L.z1_grad_norm_sq_flat_noalloc(0x1000, 5, None, None) == B.Z1_EINVAL
+    assert L.z1_grad_norm_sq_flat_noalloc(0x1004, 5, 0x2000, None) == B.Z1_EALIGN
+    assert L.z1_grad_norm_sq_flat_noalloc(0x1000, 5, 0x2004, None) == B.Z1_EALIGN
+    with pytest.raises(ValueError, match="acc: 9 elements"):
+        B.z1_grad_norm_sq_flat_noalloc(torch.zeros(9), 10, torch.zeros(1, dtype=torch.float64))
