@@ -456,7 +456,7 @@ def main():
                    "chunk_elems": int(st.plan.info.chunk_elems),
                    "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
                    "mup": bool(args.mup), "accum": args.accum, "layout": args.layout},
-        "roofline": {"bound": "hbm", "kernel": "k_adamw_tiles + k_adamw_rest (z1_adamw_step)",
+        "roofline": {"bound": "hbm", "kernel": "k_adamw",
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,

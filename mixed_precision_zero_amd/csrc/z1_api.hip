@@ -6,7 +6,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <algorithm>
 #include <memory>
 #include <mutex>
 #include <new>
@@ -23,8 +22,7 @@ struct z1_plan {
     int device = -1;  // the GPU current at creation; every call must run there
     int32_t n = 0, K = 0, dp = 0, rank = 0;
     int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
-    int64_t n_tile = 0;   // leading whole-tile pieces of the table
-    int grid = 0, max_blocks = 0;
+    int grid = 0;
     std::vector<int64_t> start, len, arena_off;
     // device memory owned by the plan
     Chunk *d_chunks = nullptr;
@@ -255,13 +253,7 @@ z1_status device_alloc(T **out, size_t count)
     return Z1_OK;
 }
 
-z1::LaunchGeom geom(const z1_plan *p)
-{
-    z1::LaunchGeom g{p->d_chunks, p->n_chunks, p->grid};
-    g.n_tile = p->n_tile;
-    g.max_blocks = p->max_blocks;
-    return g;
-}
+z1::LaunchGeom geom(const z1_plan *p) { return z1::LaunchGeom{p->d_chunks, p->n_chunks, p->grid}; }
 
 // Appends the pieces of slices [start[i], start[i]+len[i]) of tensors 0..n-1,
 // cut at multiples of `chunk` inside each tensor; element e of slice i lands
@@ -557,12 +549,6 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     for (int32_t i = 0; i < n; ++i)
         p->L += p->len[i];
     append_chunks(chunks, n, p->start.data(), p->len.data(), p->arena_off.data(), 0, chunk);
-    // whole-tile pieces first (AdamW runs them in a straight-line kernel of
-    // their own), each group in tensor order
-    const auto is_tile = [](const Chunk &c) {
-        return c.src % z1::kVec == 0 && c.count == z1::kTileElems;
-    };
-    p->n_tile = std::stable_partition(chunks.begin(), chunks.end(), is_tile) - chunks.begin();
     p->n_chunks = (int64_t)chunks.size();
     if (p->n_chunks > INT32_MAX)
         return Z1_EINVAL;
@@ -570,7 +556,6 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if (b->max_blocks > 0 && grid > b->max_blocks)
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
-    p->max_blocks = b->max_blocks;
 
     if ((p->device = current_device()) < 0)
         return Z1_EHIP;

@@ -69,11 +69,6 @@ struct LaunchGeom {
     const Chunk *chunks;  // device
     int64_t n_chunks;
     int grid;             // workgroups for the chunk kernels
-    // a plan's table starts with its n_tile whole-tile pieces (kTileElems
-    // elements from a vector boundary), which AdamW runs in a kernel of their
-    // own; max_blocks > 0 caps each AdamW grid (0: one workgroup per piece)
-    int64_t n_tile = 0;
-    int max_blocks = 0;
 };
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,

@@ -754,50 +754,26 @@ __device__ __forceinline__ bool adamw_setup(const AdamConsts &k_arg,
     return true;
 }
 
-// AdamW over whole tiles: table entries [0, n) are pieces of exactly
-// kTileElems elements starting on a vector boundary (every piece of the
-// 7B-shaped lists but the norm weights' slices), one straight-line tile of 4
-// vectors per lane each, in table (tensor) order.  The only lookup before the
-// first vector load is the piece's descriptor, and with nothing else in the
-// kernel the update of each vector waits only for its own loads.  ONE: one
-// workgroup per piece and no loop, so no store of an earlier piece is in
-// flight when the loads are consumed (loads and stores share one counter).
-// Measured on the 7B shard against the earlier single kernel (8-way
-// interleaved issue order, 3 waves per SIMD): an 8-way order was 1-4% slower
-// for this kernel, whose five streams already spread every XCD over the
-// whole shard.
+// AdamW: one workgroup per piece, pieces in table (tensor) order.  A whole
+// tile (exactly kTileElems elements from a vector boundary: every piece of
+// the 7B-shaped lists but the norm weights' slices, every interior piece at
+// the default chunk size) runs as one straight-line tile of 4 vectors per
+// lane; any other piece runs whole tiles in a loop or 2 vectors, then 1, per
+// lane, and its partial head and tail vectors element by element.  The only
+// lookup before the first vector load is the piece's descriptor; with every
+// access global, the update of each vector waits only for its own loads.
+// ONE: one workgroup per piece and no loop over pieces, so no store of an
+// earlier piece is in flight when the loads are consumed (loads and stores
+// share one counter).  Measured on the 7B shard against the earlier kernel
+// (8-way interleaved issue order, 3 waves per SIMD): an 8-way order was 1-4%
+// slower for this kernel, whose five streams already spread every XCD over
+// the whole shard.
 // MATH = false is a measurement twin: the same walk, loads and stores over
 // the same buffers, with the arithmetic replaced by traffic_vec, so the cost
 // of the update itself can be read off on the step's own buffers.
 // TABLE = true takes the step's constants from the per-step table.
 template <bool MATH, bool TABLE, bool ONE>
-__global__ __launch_bounds__(kBlock) void k_adamw_tiles(
-    const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
-    const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
-    float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
-    const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
-    const int64_t *__restrict__ state)
-{
-    AdamConsts k;
-    if (!adamw_setup<TABLE>(k_arg, table, n_rows, state, k))
-        return;
-    for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
-        const Chunk ch = chunks[ci];
-        const int64_t off = ch.dst;
-        adamw_vectors<4, MATH>(0, ch, 0, reinterpret_cast<const f32x4 *>(acc + off),
-                               reinterpret_cast<f32x4 *>(master + off),
-                               reinterpret_cast<f32x4 *>(exp_avg + off),
-                               reinterpret_cast<f32x4 *>(exp_avg_sq + off), wtab, scales, k, S);
-        if constexpr (ONE)
-            break;
-    }
-}
-
-// AdamW over any other pieces (table entries [0, n) of the pointer given):
-// whole tiles in a loop, else 2 vectors, then 1, per lane, and the partial
-// head and tail vectors element by element.
-template <bool MATH, bool TABLE>
-__global__ __launch_bounds__(kBlock) void k_adamw_rest(
+__global__ __launch_bounds__(kBlock) void k_adamw(
     const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
     const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
     float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
@@ -816,40 +792,44 @@ __global__ __launch_bounds__(kBlock) void k_adamw_rest(
         f32x4 *pv = reinterpret_cast<f32x4 *>(master + off);
         f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
         f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
-        if (sp.lead == 0 && ch.count % kTileElems == 0) {
+        if (sp.lead == 0 && ch.count == kTileElems) {
+            adamw_vectors<4, MATH>(0, ch, 0, av, pv, mv, vv, wtab, scales, k, S);
+        } else if (sp.lead == 0 && ch.count % kTileElems == 0) {
             for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
                 adamw_vectors<4, MATH>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k, S);
-            continue;
-        }
-        int q0 = sp.qb;
-        for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
-            adamw_vectors<2, MATH>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
-        for (int q = q0 + t; q < sp.qe; q += kBlock)
-            adamw_vectors<1, MATH>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
-        if (sp.lead == 0 && sp.end % kVec == 0)
-            continue;
-        const double c = MATH ? clip_coef(k, S) : 1.0;
-        const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
-        gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
-        const float *a = acc + off;
-        float *p = master + off;
-        float *m = exp_avg + off;
-        float *v = exp_avg_sq + off;
-        for_partial_elems(sp, [&](int e) {
-            if constexpr (MATH) {
-                const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
-                p[e] = r.p;
-                m[e] = r.m;
-                v[e] = r.v;
-                w[e] = (uint16_t)bf16_rne(r.p);
-            } else {
-                const float x = p[e] + a[e];
-                p[e] = x;
-                m[e] = m[e] + a[e];
-                v[e] = v[e] + a[e];
-                w[e] = (uint16_t)(__float_as_uint(x) >> 16);
+        } else {
+            int q0 = sp.qb;
+            for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
+                adamw_vectors<2, MATH>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+            for (int q = q0 + t; q < sp.qe; q += kBlock)
+                adamw_vectors<1, MATH>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+            if (sp.lead != 0 || sp.end % kVec != 0) {
+                const double c = MATH ? clip_coef(k, S) : 1.0;
+                const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
+                gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
+                const float *a = acc + off;
+                float *p = master + off;
+                float *m = exp_avg + off;
+                float *v = exp_avg_sq + off;
+                for_partial_elems(sp, [&](int e) {
+                    if constexpr (MATH) {
+                        const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
+                        p[e] = r.p;
+                        m[e] = r.m;
+                        v[e] = r.v;
+                        w[e] = (uint16_t)bf16_rne(r.p);
+                    } else {
+                        const float x = p[e] + a[e];
+                        p[e] = x;
+                        m[e] = m[e] + a[e];
+                        v[e] = v[e] + a[e];
+                        w[e] = (uint16_t)(__float_as_uint(x) >> 16);
+                    }
+                });
             }
-        });
+        }
+        if constexpr (ONE)
+            break;
     }
 }
 
@@ -1028,9 +1008,8 @@ hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_
     return hipGetLastError();
 }
 
-// AdamW over a plan's table: the leading whole-tile pieces in k_adamw_tiles
-// (one workgroup each unless max_blocks caps the grid), the rest in
-// k_adamw_rest, on the same stream.
+// AdamW over a plan's table: one workgroup per piece (the loop-free
+// variant), or max_blocks workgroups looping over the pieces.
 template <bool MATH, bool TABLE>
 void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                          const float *acc, float *master, float *m, float *v,
@@ -1038,23 +1017,13 @@ void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, con
                          int64_t n_rows, const int64_t *state, hipStream_t s)
 {
     const dim3 block(kBlock);
-    const int64_t nt = geo.n_tile, nr = geo.n_chunks - geo.n_tile;
-    if (nt > 0) {
-        if (geo.max_blocks > 0 && geo.max_blocks < nt)
-            k_adamw_tiles<MATH, TABLE, false><<<dim3((unsigned)geo.max_blocks), block, 0, s>>>(
-                geo.chunks, nt, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
-                state);
-        else
-            k_adamw_tiles<MATH, TABLE, true><<<dim3((unsigned)nt), block, 0, s>>>(
-                geo.chunks, nt, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
-                state);
-    }
-    if (nr > 0) {
-        const int64_t g = geo.max_blocks > 0 && geo.max_blocks < nr ? geo.max_blocks : nr;
-        k_adamw_rest<MATH, TABLE><<<dim3((unsigned)g), block, 0, s>>>(
-            geo.chunks + nt, nr, weight_tab, scales, acc, master, m, v, k, S, table, n_rows,
-            state);
-    }
+    const int64_t n = geo.n_chunks;
+    if (geo.grid < n)
+        k_adamw<MATH, TABLE, false><<<dim3((unsigned)geo.grid), block, 0, s>>>(
+            geo.chunks, n, weight_tab, scales, acc, master, m, v, k, S, table, n_rows, state);
+    else
+        k_adamw<MATH, TABLE, true><<<dim3((unsigned)n), block, 0, s>>>(
+            geo.chunks, n, weight_tab, scales, acc, master, m, v, k, S, table, n_rows, state);
 }
 
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
