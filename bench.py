@@ -37,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, vendor figure
 BYTES_ADAMW = 30                 # read acc, p, m, v (16); write p, m, v (12) + bf16 (2)
 BYTES_ACC_FIRST = 6              # read bf16 g (2); write acc (4)
 BYTES_ACC_NEXT = 10              # read bf16 g (2) + acc (4); write acc (4)
-MAX_SLOTS = 8                    # micro-batch slots per multi-slot pass
+MAX_SLOTS = 16                   # micro-batch slots per multi-slot pass
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "z1_kernels.hip")
 
@@ -47,7 +47,7 @@ def accum_bytes(K: int, resident: bool) -> int:
     if not resident:
         return BYTES_ACC_FIRST + BYTES_ACC_NEXT * (K - 1)
     total, k = 0, 0
-    while k < K:   # the library's split: passes of at most 8 slots, as even as possible
+    while k < K:   # the library's split: passes of at most 16 slots, as even as possible
         left = K - k
         passes = (left + MAX_SLOTS - 1) // MAX_SLOTS
         g = (left + passes - 1) // passes
@@ -74,7 +74,7 @@ def parse():
                     help="per-tensor muP lr multipliers and no decay on norms")
     ap.add_argument("--accum", default="resident", choices=["resident", "slot"],
                     help="resident (default): the K resident micro-batch gradients in one "
-                         "z1_accum_grads_range call (up to 8 slots per pass); slot: one "
+                         "z1_accum_grads_range call (up to 16 slots per pass); slot: one "
                          "z1_accum_grads call per micro-batch; the other form is timed too "
                          "and reported beside")
     ap.add_argument("--layout", default="packed", choices=["full", "packed"],

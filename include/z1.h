@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 8
+#define Z1_ABI_VERSION 9
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -281,9 +281,11 @@ z1_status z1_accum_grads(z1_plan *plan, int32_t k, z1_stream stream);
  * are summed, one optimizer step after them).  It is for callers that hold
  * several micro-batch gradients in device memory at once (K full-size bf16
  * gradient sets, 2 bytes per parameter each): the range is split into
- * passes of at most 8 slots, as even as possible (10 slots: two passes of 5),
- * so the fp32 acc arena is read and written once per pass instead of once
- * per slot.  For K = 4 that is 12 bytes per shard element instead of 36.
+ * passes of at most 16 slots, as even as possible (20 slots: two passes of
+ * 10), so the fp32 acc arena is read and written once per pass instead of
+ * once per slot.  For K = 4 that is 12 bytes per shard element instead of 36;
+ * for K = 16, 36 instead of 132.  (Before ABI version 9 a pass read at most
+ * 8 slots.)
  * A range that ends at K also writes the norm partials, as the k == K-1 pass
  * of z1_accum_grads does.  A range may follow single-slot calls and be
  * followed by them.
@@ -542,7 +544,7 @@ z1_status z1_pack_destroy(z1_pack *pack);
 z1_status z1_pack_accum(z1_pack *pack, int32_t k, z1_stream stream);
 
 /* Micro-batches k_begin .. k_end-1 in one call: bit for bit what
- * z1_pack_accum(pack, k) for each k in order stores, reading up to 8 slots
+ * z1_pack_accum(pack, k) for each k in order stores, reading up to 16 slots
  * per pass (see z1_accum_grads_range).  Order and errors as
  * z1_accum_grads_range. */
 z1_status z1_pack_accum_range(z1_pack *pack, int32_t k_begin, int32_t k_end, z1_stream stream);
@@ -570,7 +572,7 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
  *   Z1_PROBE_ACCUM_TRAFFIC  read the half-width bufs[0] and bufs[1], write
  *                           bufs[1]: 10 B per element
  *   Z1_PROBE_SLOTS_TRAFFIC  read the half-width bufs[0..G-1], write bufs[G]
- *                           (G = n_bufs - 1 in [2, 8]): 2G + 4 B per element,
+ *                           (G = n_bufs - 1 in [2, 16]): 2G + 4 B per element,
  *                           the first resident-slot accumulation pass
  * The contents written are meaningless.  Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
  * ------------------------------------------------------------------------ */

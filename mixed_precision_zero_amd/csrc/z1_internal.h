@@ -22,7 +22,7 @@ constexpr int kInterleave = 8;
 // AdamW's straight-line unit: 4 vectors of 4 elements per lane.  A piece of
 // exactly this many elements starting on a vector boundary is a whole tile.
 constexpr int64_t kTileElems = 4 * kBlock * kVec;
-constexpr int kMaxSlots = 8;     // micro-batch slots one multi-slot pass reads
+constexpr int kMaxSlots = 16;    // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
 // Arena offsets share the slice start's residue mod kArenaResidue elements:

@@ -49,7 +49,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #endif
 // Multi-slot passes keep G x U gradient vectors per lane in flight; above 6
 // slots U = 2 (7B shard, 8 slots: 5.1 -> 5.95 TB/s; at 6 slots U = 4 and 2
-// are within 1%).
+// are within 1%; at 16 slots U = 2 was 1-2% faster than U = 1, with 128
+// VGPRs and 4 waves per SIMD).
 #ifndef Z1_UNROLL_SLOTS_WIDE
 #define Z1_UNROLL_SLOTS_WIDE 2
 #endif
@@ -953,7 +954,7 @@ hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad
         return hipSuccess;
     if (last && divide)
         return hipErrorInvalidValue;
-    static_assert(kMaxSlots == 8, "one case per slot count 2..kMaxSlots");
+    static_assert(kMaxSlots == 16, "one case per slot count 2..kMaxSlots");
     switch (n_slots) {
     case 2: launch_slots_g<2>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     case 3: launch_slots_g<3>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
@@ -962,6 +963,14 @@ hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad
     case 6: launch_slots_g<6>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     case 7: launch_slots_g<7>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     case 8: launch_slots_g<8>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 9: launch_slots_g<9>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 10: launch_slots_g<10>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 11: launch_slots_g<11>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 12: launch_slots_g<12>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 13: launch_slots_g<13>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 14: launch_slots_g<14>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 15: launch_slots_g<15>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    case 16: launch_slots_g<16>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -113,36 +113,43 @@ __global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict_
 
 // The first resident-slot pass's traffic: read G half-width streams, write
 // one fp32 stream (2G + 4 bytes per element); the G pointers come by value.
+// U vectors per lane at a time, as in the accumulation kernel (4 up to 6
+// slots, 2 above), over the same 1024-vector tile per workgroup.
 struct SlotPtrs {
     const u32x2 *p[kMaxSlots];
 };
 
-template <int G>
+template <int G, int U>
 __global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__restrict__ acc,
                                                              int64_t n)
 {
-    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
-    u32x2 gr[G][4];
+    static_assert(4 % U == 0, "U divides the tile's 4 vectors per lane");
+    const int64_t tile = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t i = base + u * kBlock;
-        if (i < n) {
+    for (int r = 0; r < 4 / U; ++r) {
+        const int64_t base = tile + (int64_t)r * U * kBlock;
+        u32x2 gr[G][U];
 #pragma unroll
-            for (int j = 0; j < G; ++j)
-                gr[j][u] = ld(sp.p[j] + i);
-        }
-    }
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * kBlock;
+            if (i < n) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t i = base + u * kBlock;
-        if (i < n) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                s.x += __uint_as_float(gr[j][u].x << 16);
-                s.y += __uint_as_float(gr[j][u].y << 16);
+                for (int j = 0; j < G; ++j)
+                    gr[j][u] = ld(sp.p[j] + i);
             }
-            st(acc + i, s);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * kBlock;
+            if (i < n) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    s.x += __uint_as_float(gr[j][u].x << 16);
+                    s.y += __uint_as_float(gr[j][u].y << 16);
+                }
+                st(acc + i, s);
+            }
         }
     }
 }
@@ -153,7 +160,8 @@ void launch_slots_probe(void *const *bufs, int64_t n_vec, dim3 grid, hipStream_t
     SlotPtrs sp{};
     for (int j = 0; j < G; ++j)
         sp.p[j] = static_cast<const u32x2 *>(bufs[j]);
-    k_probe_slots<G><<<grid, dim3(kBlock), 0, s>>>(sp, static_cast<f32x4 *>(bufs[G]), n_vec);
+    k_probe_slots<G, (G <= 6 ? 4 : 2)><<<grid, dim3(kBlock), 0, s>>>(
+        sp, static_cast<f32x4 *>(bufs[G]), n_vec);
 }
 
 }  // namespace
@@ -202,7 +210,7 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
                                              static_cast<f32x4 *>(bufs[1]), n_vec);
         break;
     default:
-        static_assert(kMaxSlots == 8, "one case per slot count 2..kMaxSlots");
+        static_assert(kMaxSlots == 16, "one case per slot count 2..kMaxSlots");
         switch (n_bufs - 1) {
         case 2: launch_slots_probe<2>(bufs, n_vec, grid, s); break;
         case 3: launch_slots_probe<3>(bufs, n_vec, grid, s); break;
@@ -210,7 +218,15 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
         case 5: launch_slots_probe<5>(bufs, n_vec, grid, s); break;
         case 6: launch_slots_probe<6>(bufs, n_vec, grid, s); break;
         case 7: launch_slots_probe<7>(bufs, n_vec, grid, s); break;
-        default: launch_slots_probe<8>(bufs, n_vec, grid, s); break;
+        case 8: launch_slots_probe<8>(bufs, n_vec, grid, s); break;
+        case 9: launch_slots_probe<9>(bufs, n_vec, grid, s); break;
+        case 10: launch_slots_probe<10>(bufs, n_vec, grid, s); break;
+        case 11: launch_slots_probe<11>(bufs, n_vec, grid, s); break;
+        case 12: launch_slots_probe<12>(bufs, n_vec, grid, s); break;
+        case 13: launch_slots_probe<13>(bufs, n_vec, grid, s); break;
+        case 14: launch_slots_probe<14>(bufs, n_vec, grid, s); break;
+        case 15: launch_slots_probe<15>(bufs, n_vec, grid, s); break;
+        default: launch_slots_probe<16>(bufs, n_vec, grid, s); break;
         }
         break;
     }

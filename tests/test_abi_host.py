@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 8
+    assert B.z1_abi_version() == 9
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"

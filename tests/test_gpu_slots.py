@@ -43,31 +43,66 @@ def test_tiny_two_slots_one_pass():
     _run(W.TINY, 3, [(0, 2)])
 
 
-def test_tiny_eleven_slots_two_passes_small_chunks():
-    """K = 11: passes of 6 and 5 slots; 1024-element chunks on 3 workgroups."""
+def test_tiny_eleven_slots_one_pass_small_chunks():
+    """K = 11 in one pass; 1024-element chunks on 3 workgroups."""
     w = dataclasses.replace(W.TINY, name="tiny_k11", n_micro=11)
     _run(w, 2, [(0, 11)], chunk_elems=1024, max_blocks=3)
 
 
-def test_tiny_fifteen_slots_wide_passes():
-    """K = 15: passes of 8 and 7 slots (the two-vectors-per-lane form), on
-    1024-element chunks so every workgroup loops and takes partial vectors."""
+def test_tiny_fifteen_slots_wide_pass():
+    """K = 15 in one pass (the two-vectors-per-lane form), on 1024-element
+    chunks so every workgroup loops and takes partial vectors."""
     w = dataclasses.replace(W.TINY, name="tiny_k15", n_micro=15, shapes=((257, 63), (61,), (1030,)))
     _run(w, 2, [(0, 15)], chunk_elems=1024)
 
 
 @pytest.mark.parametrize("K,ranges", [
-    (33, [(0, 33)]),                     # five passes: 7, 7, 7, 6, 6 slots
-    (64, [(0, 64)]),                     # eight passes of 8 slots
-    (37, [(0, 3), (3, 20), (20, 37)]),   # three calls, each split into even passes
+    (33, [(0, 33)]),                     # three passes of 11 slots
+    (64, [(0, 64)]),                     # four passes of 16 slots
+    (37, [(0, 3), (3, 20), (20, 37)]),   # three calls: 3; 9 + 8; 9 + 8 slots
 ], ids=["k33", "k64", "k37_three_calls"])
 def test_tiny_many_slots_many_passes(K, ranges):
-    """Many resident micro-batches: a range longer than 8 slots is split into
+    """Many resident micro-batches: a range longer than 16 slots is split into
     as many passes as it needs, of nearly equal size; every split stores the
     bits of one call per micro-batch (the oracle's in-order binary32 sum)."""
     w = dataclasses.replace(W.TINY, name=f"tiny_k{K}", n_micro=K,
                             shapes=((257, 63), (61,), (1030,)))
     _run(w, 2, ranges, chunk_elems=1024)
+
+
+def _wide_pass_partitions(K):
+    """Per step, the ranges of one step's calls: every pass size from 9 to 16
+    once as a step's first pass (it overwrites acc), once between two other
+    passes, and once as the last (it also writes the norm partials)."""
+    steps = []
+    for g in range(9, 17):
+        steps.append([(0, g), (g, K)])
+        steps.append([(0, 1), (1, 1 + g), (1 + g, K)])
+        steps.append([(0, K - g), (K - g, K)])
+    return steps
+
+
+def test_tiny_wide_passes_every_size_and_position():
+    """K = 18 on 1024-element chunks: each of the 9- to 16-slot passes as the
+    first, a middle and the last pass of a step, 24 steps in a row, every step
+    bit-exact against the oracle."""
+    import harness
+    K = 18
+    w = dataclasses.replace(W.TINY, name="tiny_k18", n_micro=K, shapes=((257, 63), (61,), (1030,)))
+    steps = _wide_pass_partitions(K)
+    h = harness.Parity(w, ranges=steps[0], chunk_elems=1024)
+    try:
+        assert h.plan_matches()
+        for ranges in steps:
+            h.ranges = ranges
+            rep = h.step()
+            harness.log(f"[slots] {w.name} ranges={ranges} t={rep.step}: "
+                        f"not_bitexact={rep.not_bitexact}")
+            harness.assert_report(rep)
+        assert h.canaries_intact()
+        assert h.weights_outside_slices_intact()
+    finally:
+        h.close()
 
 
 def test_ragged_small_three_slots():
@@ -90,7 +125,7 @@ def test_plan_flat_ragged_small_range():
 
 
 def test_ragged_full_sixteen_slots():
-    """K = 16 in two passes of 8; 533 empty and 181 single-element slices."""
+    """K = 16 in one pass; 533 empty and 181 single-element slices."""
     _run(W.RAGGED, 2, [(0, 16)])
 
 
@@ -134,6 +169,9 @@ PACK_CASES = [
                          n_micro=3, hot_tensors=()), "flat", True, [(0, 1), (1, 3)]),
     (dataclasses.replace(W.SMOLLM_135M, dp_size=8, rank=0), "per_tensor", False, [(0, 4)]),
     (dataclasses.replace(W.SMOLLM_135M, dp_size=7, rank=0, n_micro=9), "dim0", True, [(0, 9)]),
+    (dataclasses.replace(W.TINY, name="tiny_k18", n_micro=18), "per_tensor", True, [(0, 18)]),
+    (dataclasses.replace(W.TINY, name="tiny_k16", n_micro=16), "flat", True, [(0, 1), (1, 16)]),
+    (dataclasses.replace(W.TINY, name="tiny_k12", n_micro=12), "per_tensor", True, [(0, 12)]),
 ]
 
 
