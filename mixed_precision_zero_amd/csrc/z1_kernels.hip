@@ -681,19 +681,40 @@ __device__ __forceinline__ double clip_coef(const AdamConsts &k, const double *_
     return cc >= 1.0 ? 1.0 : cc;
 }
 
+// The step's constants: the kernel argument, or row `row` of a per-step
+// table (false when the table is exhausted: nothing may then be stored).  The
+// kernel reads the row index as it starts, and the row itself is read here,
+// after a piece's loads are issued, so neither lookup delays them.
+template <bool TABLE>
+__device__ __forceinline__ bool step_consts(const AdamConsts &k_arg,
+                                            const AdamConsts *__restrict__ table, int64_t row,
+                                            int64_t n_rows, AdamConsts &k)
+{
+    k = k_arg;
+    if constexpr (TABLE) {
+        if (row >= n_rows)
+            return false;
+        k = table[row];
+    }
+    return true;
+}
+
 // U consecutive vectors per lane (vector q0 + u * kBlock + t for u < U) of
-// the piece ch: all loads issued first, then the clip coefficient, the
-// tensor's rate and its bf16 pointer (lookups whose latency then hides behind
-// the loads), then update and store vector by vector.  MATH = false is the
-// measurement twin (traffic_vec).
-template <int U, bool MATH>
-__device__ __forceinline__ void adamw_vectors(int q0, const Chunk &ch, int lead,
+// the piece ch: all loads issued first, then the step's constants, the clip
+// coefficient, the tensor's rate and its bf16 pointer (lookups whose latency
+// then hides behind the loads), then update and store vector by vector.
+// False (nothing stored) when the per-step table is exhausted.  MATH = false
+// is the measurement twin (traffic_vec).
+template <int U, bool MATH, bool TABLE>
+__device__ __forceinline__ bool adamw_vectors(int q0, const Chunk &ch, int lead,
                                               const f32x4 *__restrict__ av,
                                               f32x4 *__restrict__ pv, f32x4 *__restrict__ mv,
                                               f32x4 *__restrict__ vv,
                                               uint16_t *const *__restrict__ wtab,
                                               const Scale *__restrict__ scales,
-                                              const AdamConsts &k, const double *__restrict__ S)
+                                              const AdamConsts &k_arg,
+                                              const AdamConsts *__restrict__ table, int64_t row,
+                                              int64_t n_rows, const double *__restrict__ S)
 {
     // every access is a workgroup-uniform base (vector q0 of the stream) plus
     // a 32-bit byte offset that depends only on the lane and u, so all of them
@@ -718,6 +739,9 @@ __device__ __forceinline__ void adamw_vectors(int q0, const Chunk &ch, int lead,
         // only for its own four loads
         __builtin_amdgcn_sched_barrier(0);
     }
+    AdamConsts k;
+    if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
+        return false;
     const double c = MATH ? clip_coef(k, S) : 1.0;
     const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
     gmem<char> *wb8 = reinterpret_cast<gmem<char> *>(to_global(wtab[ch.tensor]) + (ch.src - lead)) +
@@ -734,23 +758,6 @@ __device__ __forceinline__ void adamw_vectors(int q0, const Chunk &ch, int lead,
         st_stream(reinterpret_cast<f32x4 *>(mb + o), mr[u]);
         st_stream(reinterpret_cast<f32x4 *>(vb + o), vr[u]);
         st_stream(reinterpret_cast<gmem<u32x2> *>(wb8 + o / 2), wb);
-    }
-}
-
-// The step's constants: the kernel argument, or row state[0] of a per-step
-// table (false when the table is exhausted: the whole grid then returns at
-// once).
-template <bool TABLE>
-__device__ __forceinline__ bool adamw_setup(const AdamConsts &k_arg,
-                                            const AdamConsts *__restrict__ table, int64_t n_rows,
-                                            const int64_t *__restrict__ state, AdamConsts &k)
-{
-    k = k_arg;
-    if constexpr (TABLE) {
-        const int64_t row = state[0];
-        if (row >= n_rows)
-            return false;
-        k = table[row];
     }
     return true;
 }
@@ -772,7 +779,10 @@ __device__ __forceinline__ bool adamw_setup(const AdamConsts &k_arg,
 // MATH = false is a measurement twin: the same walk, loads and stores over
 // the same buffers, with the arithmetic replaced by traffic_vec, so the cost
 // of the update itself can be read off on the step's own buffers.
-// TABLE = true takes the step's constants from the per-step table.
+// TABLE = true takes the step's constants from row state[0] of the per-step
+// table.  The row index is read as the kernel starts, next to the piece's
+// descriptor, and the row itself after the piece's loads are issued; when
+// the table is exhausted every workgroup returns before its first store.
 template <bool MATH, bool TABLE, bool ONE>
 __global__ __launch_bounds__(kBlock) void k_adamw(
     const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
@@ -781,9 +791,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw(
     const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
     const int64_t *__restrict__ state)
 {
-    AdamConsts k;
-    if (!adamw_setup<TABLE>(k_arg, table, n_rows, state, k))
-        return;
+    const int64_t row = TABLE ? state[0] : 0;
     const int t = (int)threadIdx.x;
     for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
         const Chunk ch = chunks[ci];
@@ -794,17 +802,28 @@ __global__ __launch_bounds__(kBlock) void k_adamw(
         f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
         f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
         if (sp.lead == 0 && ch.count == kTileElems) {
-            adamw_vectors<4, MATH>(0, ch, 0, av, pv, mv, vv, wtab, scales, k, S);
+            if (!adamw_vectors<4, MATH, TABLE>(0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg, table,
+                                               row, n_rows, S))
+                return;
         } else if (sp.lead == 0 && ch.count % kTileElems == 0) {
             for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
-                adamw_vectors<4, MATH>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k, S);
+                if (!adamw_vectors<4, MATH, TABLE>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg,
+                                                   table, row, n_rows, S))
+                    return;
         } else {
             int q0 = sp.qb;
             for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
-                adamw_vectors<2, MATH>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+                if (!adamw_vectors<2, MATH, TABLE>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales,
+                                                   k_arg, table, row, n_rows, S))
+                    return;
             for (int q = q0 + t; q < sp.qe; q += kBlock)
-                adamw_vectors<1, MATH>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales, k, S);
+                if (!adamw_vectors<1, MATH, TABLE>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales,
+                                                   k_arg, table, row, n_rows, S))
+                    return;
             if (sp.lead != 0 || sp.end % kVec != 0) {
+                AdamConsts k;
+                if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
+                    return;
                 const double c = MATH ? clip_coef(k, S) : 1.0;
                 const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
                 gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
