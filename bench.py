@@ -393,16 +393,19 @@ def main():
         # start of the flat full-size weight buffer), so placement is shared
         w_buf = (st.w_packed if st.layout == "packed"
                  else st.weights[0].untyped_storage().data_ptr())
-        ceilings["adamw_traffic"] = timed_gbps(
-            lambda: B.z1_probe("adamw_traffic", [st.acc, st.master, st.exp_avg, st.exp_avg_sq,
-                                                 w_buf], nvL), 30 * 4 * nvL)
+        adam_bufs = [st.acc, st.master, st.exp_avg, st.exp_avg_sq, w_buf]
+        for kind in ("adamw_traffic", "adamw_traffic_wave"):
+            ceilings[kind] = timed_gbps(lambda: B.z1_probe(kind, adam_bufs, nvL), 30 * 4 * nvL)
         ceilings["accum_traffic"] = timed_gbps(
             lambda: B.z1_probe("accum_traffic", [half, st.acc], nvL), 10 * 4 * nvL)
         if head_resident and 2 <= w.n_micro <= MAX_SLOTS:
-            slots = [half] + [torch.empty_like(half) for _ in range(w.n_micro - 1)]
-            ceilings["slots_traffic"] = timed_gbps(
-                lambda: B.z1_probe("slots_traffic", slots + [st.acc], nvL),
-                (2 * w.n_micro + 4) * 4 * nvL)
+            # the step's own gradient slots (packed shards, or the start of
+            # each flat full-size gradient buffer) and acc arena
+            slots = ([g for g in st.g_packed] if st.layout == "packed" else
+                     [st.grads[k][0].untyped_storage().data_ptr() for k in range(w.n_micro)])
+            for kind in ("slots_traffic", "slots_traffic_one"):
+                ceilings[kind] = timed_gbps(lambda: B.z1_probe(kind, slots + [st.acc], nvL),
+                                            (2 * w.n_micro + 4) * 4 * nvL)
             del slots
         del half
     # k_adamw's own chunk walk over the step's own buffers with no arithmetic
@@ -413,21 +416,24 @@ def main():
     copy_gbps = ceilings["copy"] if ceilings else None
 
     # GB/s of each timed piece: algorithmic bytes / mean time, as a fraction of
-    # the 8 TB/s peak and of a traffic-only probe with the same read/write mix
-    # measured in this process (where one exists)
-    def rate(nbytes, ms, probe=None):
+    # the 8 TB/s peak and of the fastest traffic-only probe with the same
+    # read/write mix measured in this process (where one exists)
+    def rate(nbytes, ms, probes=()):
         gbps = nbytes / (ms / 1e3) / 1e9
-        ref = ceilings.get(probe) if (ceilings and probe) else None
+        have = [(ceilings[k], k) for k in probes if ceilings and ceilings.get(k)]
+        ref, name = max(have) if have else (None, None)
         return {"GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
-                "same_mix_probe": probe if ref else None,
+                "same_mix_probe": name,
                 "frac_of_same_mix_probe": (gbps / ref) if ref else None}
     acc_b = accum_bytes(w.n_micro, head_resident) * L
     norm_avg = float(norm_ms.mean())
-    acc_probe = ("slots_traffic" if head_resident and 2 <= w.n_micro <= MAX_SLOTS
-                 else None if head_resident else "accum_traffic")
-    rates = {"accum_all_K": rate(acc_b, accum_ms, acc_probe),
-             "adamw": rate(BYTES_ADAMW * L, adam_avg, "adamw_traffic"),
-             "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg, "adamw_traffic"),
+    acc_probes = (("slots_traffic", "slots_traffic_one")
+                  if head_resident and 2 <= w.n_micro <= MAX_SLOTS
+                  else () if head_resident else ("accum_traffic",))
+    adam_probes = ("adamw_traffic", "adamw_traffic_wave")
+    rates = {"accum_all_K": rate(acc_b, accum_ms, acc_probes),
+             "adamw": rate(BYTES_ADAMW * L, adam_avg, adam_probes),
+             "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg, adam_probes),
              "H3_step": rate(acc_b + BYTES_ADAMW * L, ms_step)}
 
     out = {

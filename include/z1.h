@@ -552,8 +552,9 @@ z1_status z1_pack_accum_range(z1_pack *pack, int32_t k_begin, int32_t k_end, z1_
 /* ------------------------------------------------------------------------
  * Measurement aid (not part of the step): a streaming copy of n_bytes
  * (a multiple of 16, both pointers 16-byte aligned, non-overlapping) from
- * device src to device dst with 16-byte loads and stores, used to measure
- * the achievable HBM bandwidth and to calibrate byte counters.
+ * device src to device dst with 16-byte loads and stores (one per lane, one
+ * 256-lane workgroup per 4 KB), used to measure the achievable HBM bandwidth
+ * and to calibrate byte counters.
  * Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
  * ------------------------------------------------------------------------ */
 z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream stream);
@@ -574,14 +575,24 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
  *   Z1_PROBE_SLOTS_TRAFFIC  read the half-width bufs[0..G-1], write bufs[G]
  *                           (G = n_bufs - 1 in [2, 16]): 2G + 4 B per element,
  *                           the first resident-slot accumulation pass
- * The contents written are meaningless.  Errors: Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
+ *   Z1_PROBE_ADAMW_TRAFFIC_WAVE  as Z1_PROBE_ADAMW_TRAFFIC, in one-wave (64-lane)
+ *                           workgroups: the shape at which this mix streams
+ *                           fastest without arithmetic
+ *   Z1_PROBE_SLOTS_TRAFFIC_ONE   as Z1_PROBE_SLOTS_TRAFFIC, one vector per lane
+ *                           (256 vectors per workgroup)
+ * The step kernels' own shape is the default: 256-lane workgroups with 4
+ * vectors per lane.  The contents written are meaningless.  Z1_EINVAL also
+ * when n_vec needs more than 2^31 - 1 workgroups of 256 vectors.  Errors:
+ * Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
  * ------------------------------------------------------------------------ */
 enum {
     Z1_PROBE_READ = 0,
     Z1_PROBE_WRITE = 1,
     Z1_PROBE_ADAMW_TRAFFIC = 2,
     Z1_PROBE_ACCUM_TRAFFIC = 3,
-    Z1_PROBE_SLOTS_TRAFFIC = 4
+    Z1_PROBE_SLOTS_TRAFFIC = 4,
+    Z1_PROBE_ADAMW_TRAFFIC_WAVE = 5,
+    Z1_PROBE_SLOTS_TRAFFIC_ONE = 6
 };
 z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, int64_t n_vec,
                    z1_stream stream);

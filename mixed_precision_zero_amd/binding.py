@@ -34,7 +34,8 @@ EXPORTS = ("z1_abi_version", "z1_strerror", "z1_shard_plan", "z1_shard_plan_kind
            "z1_adamw_step_scheduled", "z1_grad_norm_sq_pair", "z1_norm_combine",
            "z1_grad_norm_sq_flat_noalloc")
 
-PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3, "slots_traffic": 4}
+PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3, "slots_traffic": 4,
+          "adamw_traffic_wave": 5, "slots_traffic_one": 6}
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
 LAYOUTS = {"full": 0, "packed": 1}
@@ -535,10 +536,12 @@ def z1_probe_plan(plan: Plan, kind: str = "adamw", stream=None) -> None:
 def z1_probe(kind: str, bufs: Sequence, n_vec: int, stream=None) -> None:
     """Traffic-only streaming kernel (see z1.h); bufs are tensors or addresses."""
     nv = int(n_vec)
+    slots = (8 * nv,) * (len(bufs) - 1) + (16 * nv,)
     need = {"read": (16 * nv, 4), "write": (16 * nv,),
             "adamw_traffic": (16 * nv,) * 4 + (8 * nv,),
+            "adamw_traffic_wave": (16 * nv,) * 4 + (8 * nv,),
             "accum_traffic": (8 * nv, 16 * nv),
-            "slots_traffic": (8 * nv,) * (len(bufs) - 1) + (16 * nv,)}[kind]
+            "slots_traffic": slots, "slots_traffic_one": slots}[kind]
     _check_tensors([(b, f"bufs[{j}]", None, nb) for j, (b, nb) in enumerate(zip(bufs, need))])
     arr = (ctypes.c_void_p * max(len(bufs), 1))(*[_dptr(b) for b in bufs])
     _check(lib.z1_probe(PROBES[kind], arr, len(bufs), int(n_vec), _stream(stream)), "z1_probe")

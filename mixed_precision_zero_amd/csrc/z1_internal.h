@@ -11,6 +11,7 @@ namespace z1 {
 // (16-byte fp32 accesses, 8-byte bf16 accesses), so one workgroup touches
 // 1024 consecutive elements per vector step.
 constexpr int kBlock = 256;
+constexpr int kWave = 64;       // lanes of one wavefront
 constexpr int kVec = 4;
 constexpr int64_t kDefaultChunk = 4096;
 constexpr int64_t kMaxChunk = 1 << 20;

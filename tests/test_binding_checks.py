@@ -146,6 +146,10 @@ def test_probe_checks():
     half = torch.zeros(4 * nv, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match=r"bufs\[4\]: 798 bytes"):
         B.z1_probe("adamw_traffic", [f, f, f, f, half[:-1]], nv)
+    with pytest.raises(ValueError, match=r"bufs\[4\]: 798 bytes"):
+        B.z1_probe("adamw_traffic_wave", [f, f, f, f, half[:-1]], nv)
+    with pytest.raises(ValueError, match=r"bufs\[2\]: 1596 bytes"):
+        B.z1_probe("slots_traffic_one", [half, half, f[:-1]], nv)
     with pytest.raises(ValueError, match=r"bufs\[0\]: 1596 bytes"):
         B.z1_probe("read", [f[:-1], f], nv)
     with pytest.raises(ValueError, match="src: 1596 bytes"):

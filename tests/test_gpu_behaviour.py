@@ -173,9 +173,22 @@ def test_traffic_probes_run():
     B.z1_probe("read", [bufs[0], sink], n)
     B.z1_probe("write", [bufs[1]], n)
     B.z1_probe("adamw_traffic", [bufs[0], bufs[1], bufs[2], bufs[3], half], n)
+    B.z1_probe("adamw_traffic_wave", [bufs[0], bufs[1], bufs[2], bufs[3], half], n)
     B.z1_probe("accum_traffic", [half, bufs[2]], n)
     torch.cuda.synchronize()
     assert float(sink.sum()) == 0.0 and bool((bufs[0] == 1).all())
+    # the slot mixes write sum_j bf16(g_j) into every vector of the fp32
+    # stream, in both shapes and for every slot count up to 16
+    halves = [torch.full((n * 4,), 0.5, dtype=torch.bfloat16, device="cuda") for _ in range(16)]
+    out = torch.zeros(n * 4 + 4, device="cuda")
+    for kind in ("slots_traffic", "slots_traffic_one"):
+        for G in (2, 7, 16):
+            out.zero_()
+            B.z1_probe(kind, halves[:G] + [out], n)
+            torch.cuda.synchronize()
+            v = out[:n * 4].view(n, 4)
+            assert bool((v[:, 0] == 0.5 * G).all()) and bool((v[:, 1] == 0.5 * G).all())
+            assert float(out[n * 4:].abs().sum()) == 0.0
     with pytest.raises(B.Z1Error):
         B.z1_probe("adamw_traffic", [bufs[0]], n)
 
