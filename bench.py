@@ -82,6 +82,10 @@ def parse():
                          "(default: the reduce-scatter's output and the all-gather's input) "
                          "or as full-size tensors; the other layout is timed too and "
                          "reported beside")
+    ap.add_argument("--walk", default="auto", choices=["auto", "chunks", "arena_tiles"],
+                    help="how the AdamW step walks the shard (z1_walk; auto: the arena "
+                         "tiles of a packed plan with at most 1%% boundary tiles, else the "
+                         "chunk table)")
     ap.add_argument("--layout-steps", type=int, default=10,
                     help="steps timed with the other bf16 layout over the same arenas, "
                          "reported beside the headline (0 = skip)")
@@ -152,7 +156,7 @@ def main():
         lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
     st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=dev,
                    chunk_elems=args.chunk, max_blocks=args.max_blocks, kind=args.plan,
-                   lr_scale=lr_s, wd_scale=wd_s, layout=args.layout)
+                   lr_scale=lr_s, wd_scale=wd_s, layout=args.layout, walk=args.walk)
     L = int(st.plan.info.shard_elems)
     master_full = W.make_master(w, seed=0, device=dev)
     st.scatter_to_arena(st.master, master_full)
@@ -461,7 +465,10 @@ def main():
                    "dp_size": w.dp_size, "rank": w.rank, "micro_batches": w.n_micro,
                    "chunk_elems": int(st.plan.info.chunk_elems),
                    "n_chunks": int(st.plan.info.n_chunks), "plan": args.plan,
-                   "mup": bool(args.mup), "accum": args.accum, "layout": args.layout},
+                   "mup": bool(args.mup), "accum": args.accum, "layout": args.layout,
+                   "adamw_walk": "arena_tiles" if st.plan.info.adamw_tiles else "chunks",
+                   "adamw_tiles": int(st.plan.info.adamw_tiles),
+                   "boundary_tiles": int(st.plan.info.boundary_tiles)},
         "roofline": {"bound": "hbm", "kernel": "k_adamw",
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -204,7 +204,8 @@ typedef struct z1_bind {
     const double *lr_scale;
     const double *wd_scale;
     int32_t layout;         /* z1_layout of weights and grads (0 = full)    */
-    int32_t reserved;       /* must be 0                                    */
+    int32_t walk;           /* z1_walk: how the AdamW step walks the shard
+                               (0 = the library's choice)                   */
 } z1_bind;
 
 /* Where the bf16 weights and gradients live (z1_bind.layout).  The packed
@@ -217,14 +218,44 @@ typedef enum z1_layout {
     Z1_LAYOUT_PACKED = 1
 } z1_layout;
 
+/* How the AdamW step walks the shard (z1_bind.walk); the arithmetic and the
+ * bits stored are the same either way.
+ *   Z1_WALK_CHUNKS       one workgroup per entry of the chunk table (the
+ *                        accumulation and norm kernels always walk it).
+ *   Z1_WALK_ARENA_TILES  packed layout only: one workgroup per 4096-element
+ *                        tile of the arena, every stream addressed by arena
+ *                        position, so a tile's loads depend on nothing
+ *                        fetched first.  A tile inside one slice takes its
+ *                        tensor from a per-tile tag read after its loads are
+ *                        issued; a tile that crosses a slice boundary (or
+ *                        the arena's end) runs its slice segments one by one
+ *                        (padding is never written).
+ *   Z1_WALK_AUTO         arena tiles for a packed plan with at most 1% of
+ *                        its tiles crossing a slice boundary (the loads of
+ *                        such a tile are issued before its tag is known and
+ *                        then discarded), otherwise the chunk table.
+ * The arena walk runs one workgroup per tile, so AUTO keeps the chunk table
+ * when max_blocks caps the grid.  Z1_WALK_ARENA_TILES with the full layout or
+ * with max_blocks > 0, or any other value, is Z1_EINVAL at plan creation. */
+typedef enum z1_walk {
+    Z1_WALK_AUTO = 0,
+    Z1_WALK_CHUNKS = 1,
+    Z1_WALK_ARENA_TILES = 2
+} z1_walk;
+
 /* Geometry of a created plan. */
 typedef struct z1_plan_info {
     int32_t n_tensors;
     int32_t n_micro;
-    int64_t shard_elems;  /* L = sum of len[i]                    */
-    int64_t arena_elems;  /* arena length required                */
-    int64_t chunk_elems;  /* work unit in elements                */
-    int64_t n_chunks;     /* entries of the device chunk table    */
+    int64_t shard_elems;    /* L = sum of len[i]                          */
+    int64_t arena_elems;    /* arena length required                      */
+    int64_t chunk_elems;    /* work unit in elements                      */
+    int64_t n_chunks;       /* entries of the device chunk table          */
+    int64_t adamw_tiles;    /* arena tiles the AdamW step walks
+                               (Z1_WALK_ARENA_TILES), 0 when it walks the
+                               chunk table                                */
+    int64_t boundary_tiles; /* of those, tiles that cross a slice boundary
+                               or the arena's end                         */
 } z1_plan_info;
 
 /* ------------------------------------------------------------------------

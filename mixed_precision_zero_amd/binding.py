@@ -39,6 +39,7 @@ PROBES = {"read": 0, "write": 1, "adamw_traffic": 2, "accum_traffic": 3, "slots_
 
 PLAN_KINDS = {"per_tensor": 0, "flat": 1, "dim0": 2}
 LAYOUTS = {"full": 0, "packed": 1}
+WALKS = {"auto": 0, "chunks": 1, "arena_tiles": 2}
 DECAY_STYLES = {"none": 0, "linear": 1, "cosine": 2}
 
 
@@ -61,7 +62,7 @@ class Bind(ctypes.Structure):
                 ("rows", ctypes.POINTER(ctypes.c_int64)),
                 ("lr_scale", ctypes.POINTER(ctypes.c_double)),
                 ("wd_scale", ctypes.POINTER(ctypes.c_double)),
-                ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("layout", ctypes.c_int32), ("walk", ctypes.c_int32)]
 
 
 class LRSchedule(ctypes.Structure):
@@ -82,7 +83,8 @@ class PackBind(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_tensors", ctypes.c_int32), ("n_micro", ctypes.c_int32),
                 ("shard_elems", ctypes.c_int64), ("arena_elems", ctypes.c_int64),
-                ("chunk_elems", ctypes.c_int64), ("n_chunks", ctypes.c_int64)]
+                ("chunk_elems", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+                ("adamw_tiles", ctypes.c_int64), ("boundary_tiles", ctypes.c_int64)]
 
 
 class AdamWHP(ctypes.Structure):
@@ -273,19 +275,23 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
                    kind: str = "per_tensor", rows: Optional[Sequence[int]] = None,
                    lr_scale: Optional[Sequence[float]] = None,
                    wd_scale: Optional[Sequence[float]] = None,
-                   layout: str = "full", arena_elems: Optional[int] = None) -> Plan:
+                   layout: str = "full", arena_elems: Optional[int] = None,
+                   walk: str = "auto") -> Plan:
     """Bind device buffers, the four arenas fp32 of arena_elems.
     layout "full": weights[i] and grads[k][i] are full-size bf16 tensors (or
     raw device addresses).  layout "packed": weights is one packed bf16
     shard and grads[k] one packed bf16 shard per micro-batch, in arena order.
     arena_elems defaults to the smallest arena tensor's length; pass it when
-    the arenas are raw device addresses."""
+    the arenas are raw device addresses.  walk ("auto", "chunks",
+    "arena_tiles"): how the AdamW step walks the shard (z1_walk)."""
     n = _i64(numel)
     K = len(grads)
     if layout not in LAYOUTS:
         raise ValueError(f"unknown layout {layout!r}")
     if kind not in PLAN_KINDS:
         raise ValueError(f"unknown plan kind {kind!r}")
+    if walk not in WALKS:
+        raise ValueError(f"unknown walk {walk!r}")
     # what the plan will touch: slice [start, start+len) of every tensor and
     # arena_elems of every arena (and of each packed bf16 shard)
     st_, ln_, _, need = z1_shard_plan(n, dp_size, rank, kind, rows)
@@ -333,7 +339,7 @@ def z1_plan_create(numel: Sequence[int], dp_size: int, rank: int, weights: Seque
              rows=_p64(r) if r is not None else None,
              lr_scale=ls.ctypes.data_as(PD) if ls is not None else None,
              wd_scale=ws.ctypes.data_as(PD) if ws is not None else None,
-             layout=LAYOUTS[layout], reserved=0)
+             layout=LAYOUTS[layout], walk=WALKS[walk])
     h = ctypes.c_void_p()
     _check(lib.z1_plan_create(ctypes.byref(h), ctypes.byref(b), _stream(stream)),
            "z1_plan_create")

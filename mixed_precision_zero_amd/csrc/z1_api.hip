@@ -32,6 +32,11 @@ struct z1_plan {
     DD *d_stage = nullptr;               // [kFinStages] second-level norm partials
     unsigned int *d_counter = nullptr;   // norm reduction arrival counter (zero between launches)
     z1::Scale *d_scales = nullptr;       // [n] per-tensor lr / weight-decay multipliers
+    // AdamW's arena walk (packed plans; n_tiles == 0 when AdamW walks the chunk table)
+    int32_t *d_tags = nullptr;           // [n_tiles]
+    Chunk *d_segs = nullptr;             // [n_segs]
+    int64_t n_tiles = 0, n_full = 0, n_segs = 0, n_boundary = 0;
+    uint16_t *wbase = nullptr;
     // caller's arenas
     float *master = nullptr, *exp_avg = nullptr, *exp_avg_sq = nullptr, *acc = nullptr;
     // call order: next micro-batch index expected; norm enqueued since the last pass
@@ -189,7 +194,13 @@ void free_plan_memory(z1_plan *p)
         (void)hipFree(p->d_counter);
     if (p->d_scales)
         (void)hipFree(p->d_scales);
+    if (p->d_tags)
+        (void)hipFree(p->d_tags);
+    if (p->d_segs)
+        (void)hipFree(p->d_segs);
     p->d_scales = nullptr;
+    p->d_tags = nullptr;
+    p->d_segs = nullptr;
     p->d_stage = nullptr;
     p->d_counter = nullptr;
     p->d_chunks = nullptr;
@@ -204,7 +215,7 @@ struct PlanDeleter {
     void operator()(z1_plan *p) const
     {
         if (p->d_chunks || p->d_grads || p->d_weights || p->d_partials || p->d_stage ||
-            p->d_counter || p->d_scales)
+            p->d_counter || p->d_scales || p->d_tags || p->d_segs)
             (void)hipDeviceSynchronize();  // an upload may still be in flight
         free_plan_memory(p);
         delete p;
@@ -253,7 +264,59 @@ z1_status device_alloc(T **out, size_t count)
     return Z1_OK;
 }
 
-z1::LaunchGeom geom(const z1_plan *p) { return z1::LaunchGeom{p->d_chunks, p->n_chunks, p->grid}; }
+z1::LaunchGeom geom(const z1_plan *p)
+{
+    z1::LaunchGeom g{p->d_chunks, p->n_chunks, p->grid};
+    if (p->n_tiles > 0) {
+        g.arena.tags = p->d_tags;
+        g.arena.segs = p->d_segs;
+        g.arena.n_tiles = p->n_tiles;
+        g.arena.n_full = p->n_full;
+        g.arena.n_segs = p->n_segs;
+        g.arena.wbase = p->wbase;
+    }
+    return g;
+}
+
+// AdamW's arena walk of a packed plan: tile j covers arena elements
+// [j * T, (j + 1) * T) with T = kTileElems.  tags[j] is the tensor whose
+// slice holds the whole tile, -1 for a tile that crosses a slice boundary or
+// the arena's end (and for a tile no slice touches); the parts of slices in
+// such tiles become segments in the chunk table's format (src, dst, tensor,
+// count), in arena order.  Padding between slices is in no segment.
+void arena_walk(int32_t n, const int64_t *start, const int64_t *len, const int64_t *arena_off,
+                int64_t arena_elems, std::vector<int32_t> &tags, std::vector<Chunk> &segs,
+                int64_t &n_full, int64_t &n_boundary)
+{
+    const int64_t T = z1::kTileElems;
+    const int64_t n_tiles = (arena_elems + T - 1) / T;
+    n_full = arena_elems / T;
+    tags.assign((size_t)n_tiles, -1);
+    segs.clear();
+    for (int32_t i = 0; i < n; ++i) {
+        if (len[i] == 0)
+            continue;
+        const int64_t a = arena_off[i], e = a + len[i];
+        for (int64_t j = a / T; j * T < e; ++j) {
+            const int64_t lo = a > j * T ? a : j * T;
+            const int64_t hi = e < (j + 1) * T ? e : (j + 1) * T;
+            if (lo == j * T && hi == (j + 1) * T && j < n_full) {
+                tags[(size_t)j] = i;
+                continue;
+            }
+            Chunk c;
+            c.src = start[i] + (lo - a);
+            c.dst = lo;
+            c.tensor = i;
+            c.count = (int32_t)(hi - lo);
+            c.pad = 0;
+            segs.push_back(c);
+        }
+    }
+    n_boundary = 0;
+    for (int32_t t : tags)
+        n_boundary += t < 0;
+}
 
 // Appends the pieces of slices [start[i], start[i]+len[i]) of tensors 0..n-1,
 // cut at multiples of `chunk` inside each tensor; element e of slice i lands
@@ -443,8 +506,12 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         return Z1_EINVAL;
     *out = nullptr;
     if (!b || b->n_tensors < 0 || b->n_micro < 1 || b->dp_size < 1 || b->rank < 0 ||
-        b->rank >= b->dp_size || b->max_blocks < 0 || b->reserved != 0 ||
+        b->rank >= b->dp_size || b->max_blocks < 0 ||
         (b->layout != Z1_LAYOUT_FULL && b->layout != Z1_LAYOUT_PACKED))
+        return Z1_EINVAL;
+    if (b->walk != Z1_WALK_AUTO && b->walk != Z1_WALK_CHUNKS && b->walk != Z1_WALK_ARENA_TILES)
+        return Z1_EINVAL;
+    if (b->walk == Z1_WALK_ARENA_TILES && (b->layout != Z1_LAYOUT_PACKED || b->max_blocks > 0))
         return Z1_EINVAL;
     const int32_t n = b->n_tensors, K = b->n_micro;
     if (n > 0 && (!b->numel || !b->weights || !b->grads))
@@ -501,6 +568,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
             return Z1_EINVAL;
         if (!aligned(wbase, 16))
             return Z1_EALIGN;
+        p->wbase = static_cast<uint16_t *>(const_cast<void *>(wbase));
         for (int32_t k = 0; k < K; ++k) {
             if (!b->grads[k])
                 return Z1_EINVAL;
@@ -557,6 +625,31 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
 
+    // AdamW's arena walk: forced, or chosen for a packed plan whose tiles
+    // cross slice boundaries rarely (at most 1 in 100; the loads such a tile
+    // issues before reading its tag are wasted)
+    std::vector<int32_t> tags;
+    std::vector<Chunk> segs;
+    if (packed && b->max_blocks == 0 && b->walk != Z1_WALK_CHUNKS && p->arena_elems > 0) {
+        int64_t n_full = 0, n_boundary = 0;
+        arena_walk(n, p->start.data(), p->len.data(), p->arena_off.data(), p->arena_elems, tags,
+                   segs, n_full, n_boundary);
+        const int64_t n_tiles = (int64_t)tags.size();
+        const bool fits = n_tiles + (int64_t)segs.size() <= INT32_MAX;
+        if (b->walk == Z1_WALK_ARENA_TILES && !fits)
+            return Z1_EINVAL;
+        if (fits && (b->walk == Z1_WALK_ARENA_TILES || n_boundary * 100 <= n_tiles)) {
+            p->n_tiles = n_tiles;
+            p->n_full = n_full;
+            p->n_segs = (int64_t)segs.size();
+            p->n_boundary = n_boundary;
+        }
+    }
+    if (p->n_tiles == 0) {
+        tags.clear();
+        segs.clear();
+    }
+
     if ((p->device = current_device()) < 0)
         return Z1_EHIP;
     if (!stream_on(p->device, stream))
@@ -568,7 +661,9 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         (st = device_alloc(&p->d_partials, (size_t)p->n_chunks)) != Z1_OK ||
         (st = device_alloc(&p->d_stage, (size_t)z1::kFinStages)) != Z1_OK ||
         (st = device_alloc(&p->d_scales, scales.size())) != Z1_OK ||
-        (st = device_alloc(&p->d_counter, 1)) != Z1_OK) {
+        (st = device_alloc(&p->d_counter, 1)) != Z1_OK ||
+        (p->n_tiles > 0 && ((st = device_alloc(&p->d_tags, tags.size())) != Z1_OK ||
+                            (st = device_alloc(&p->d_segs, segs.size())) != Z1_OK))) {
         return st;
     }
     hipError_t e = hipSuccess;
@@ -583,6 +678,12 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
                            hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(p->d_scales, scales.data(), scales.size() * sizeof(z1::Scale),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !tags.empty())
+        e = hipMemcpyAsync(p->d_tags, tags.data(), tags.size() * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !segs.empty())
+        e = hipMemcpyAsync(p->d_segs, segs.data(), segs.size() * sizeof(Chunk),
                            hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
         e = hipMemsetAsync(p->d_counter, 0, sizeof(unsigned int), s);
@@ -618,6 +719,8 @@ z1_status z1_plan_query(const z1_plan *p, z1_plan_info *info)
     info->arena_elems = p->arena_elems;
     info->chunk_elems = p->chunk_elems;
     info->n_chunks = p->n_chunks;
+    info->adamw_tiles = p->n_tiles;
+    info->boundary_tiles = p->n_boundary;
     return Z1_OK;
 }
 

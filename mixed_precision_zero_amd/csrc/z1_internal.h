@@ -66,10 +66,25 @@ struct alignas(16) Scale {
     double lr, wd;
 };
 
+// The arena walk of a packed plan: tile j covers arena elements
+// [j * kTileElems, (j + 1) * kTileElems).  tags[j] >= 0 is the tensor whose
+// slice holds the whole tile; -1 marks a tile that crosses a slice boundary
+// or the arena's end, whose slice segments (pieces in the chunk table's
+// format) are listed in segs, each run by a workgroup of its own.
+struct ArenaWalk {
+    const int32_t *tags = nullptr;   // device [n_tiles]
+    const Chunk *segs = nullptr;     // device [n_segs]
+    int64_t n_tiles = 0;             // 0: the plan walks the chunk table
+    int64_t n_full = 0;              // tiles that end inside the arena
+    int64_t n_segs = 0;
+    uint16_t *wbase = nullptr;       // the packed bf16 weight shard
+};
+
 struct LaunchGeom {
     const Chunk *chunks;  // device
     int64_t n_chunks;
     int grid;             // workgroups for the chunk kernels
+    ArenaWalk arena{};    // AdamW's arena walk, when n_tiles > 0
 };
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,

@@ -762,14 +762,85 @@ __device__ __forceinline__ bool adamw_vectors(int q0, const Chunk &ch, int lead,
     return true;
 }
 
-// AdamW: one workgroup per piece, pieces in table (tensor) order.  A whole
-// tile (exactly kTileElems elements from a vector boundary: every piece of
-// the 7B-shaped lists but the norm weights' slices, every interior piece at
-// the default chunk size) runs as one straight-line tile of 4 vectors per
-// lane; any other piece runs whole tiles in a loop or 2 vectors, then 1, per
-// lane, and its partial head and tail vectors element by element.  The only
-// lookup before the first vector load is the piece's descriptor; with every
-// access global, the update of each vector waits only for its own loads.
+// One piece of AdamW, on the whole workgroup.  A whole tile (exactly
+// kTileElems elements from a vector boundary: every piece of the 7B-shaped
+// lists but the norm weights' slices, every interior piece at the default
+// chunk size) runs as one straight-line tile of 4 vectors per lane; any other
+// piece runs whole tiles in a loop or 2 vectors, then 1, per lane, and its
+// partial head and tail vectors element by element.  False (nothing more
+// stored) when the per-step table is exhausted.
+template <bool MATH, bool TABLE>
+__device__ __forceinline__ bool adamw_piece(const Chunk &ch, uint16_t *const *__restrict__ wtab,
+                                            const Scale *__restrict__ scales,
+                                            const float *__restrict__ acc,
+                                            float *__restrict__ master,
+                                            float *__restrict__ exp_avg,
+                                            float *__restrict__ exp_avg_sq,
+                                            const AdamConsts &k_arg,
+                                            const double *__restrict__ S,
+                                            const AdamConsts *__restrict__ table, int64_t row,
+                                            int64_t n_rows)
+{
+    const int t = (int)threadIdx.x;
+    const Span sp = span_of(ch);
+    const int64_t off = ch.dst - sp.lead;
+    const f32x4 *av = reinterpret_cast<const f32x4 *>(acc + off);
+    f32x4 *pv = reinterpret_cast<f32x4 *>(master + off);
+    f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
+    f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
+    if (sp.lead == 0 && ch.count == kTileElems)
+        return adamw_vectors<4, MATH, TABLE>(0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg, table,
+                                             row, n_rows, S);
+    if (sp.lead == 0 && ch.count % kTileElems == 0) {
+        for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
+            if (!adamw_vectors<4, MATH, TABLE>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg,
+                                               table, row, n_rows, S))
+                return false;
+        return true;
+    }
+    int q0 = sp.qb;
+    for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
+        if (!adamw_vectors<2, MATH, TABLE>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k_arg,
+                                           table, row, n_rows, S))
+            return false;
+    for (int q = q0 + t; q < sp.qe; q += kBlock)
+        if (!adamw_vectors<1, MATH, TABLE>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales,
+                                           k_arg, table, row, n_rows, S))
+            return false;
+    if (sp.lead != 0 || sp.end % kVec != 0) {
+        AdamConsts k;
+        if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
+            return false;
+        const double c = MATH ? clip_coef(k, S) : 1.0;
+        const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
+        gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
+        const float *a = acc + off;
+        float *p = master + off;
+        float *m = exp_avg + off;
+        float *v = exp_avg_sq + off;
+        for_partial_elems(sp, [&](int e) {
+            if constexpr (MATH) {
+                const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
+                p[e] = r.p;
+                m[e] = r.m;
+                v[e] = r.v;
+                w[e] = (uint16_t)bf16_rne(r.p);
+            } else {
+                const float x = p[e] + a[e];
+                p[e] = x;
+                m[e] = m[e] + a[e];
+                v[e] = v[e] + a[e];
+                w[e] = (uint16_t)(__float_as_uint(x) >> 16);
+            }
+        });
+    }
+    return true;
+}
+
+// AdamW over the chunk table: one workgroup per piece, pieces in table
+// (tensor) order.  The only lookup before the first vector load is the
+// piece's descriptor; with every access global, the update of each vector
+// waits only for its own loads.
 // ONE: one workgroup per piece and no loop over pieces, so no store of an
 // earlier piece is in flight when the loads are consumed (loads and stores
 // share one counter).  Measured on the 7B shard against the earlier kernel
@@ -792,64 +863,85 @@ __global__ __launch_bounds__(kBlock) void k_adamw(
     const int64_t *__restrict__ state)
 {
     const int64_t row = TABLE ? state[0] : 0;
-    const int t = (int)threadIdx.x;
     for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
-        const Chunk ch = chunks[ci];
-        const Span sp = span_of(ch);
-        const int64_t off = ch.dst - sp.lead;
-        const f32x4 *av = reinterpret_cast<const f32x4 *>(acc + off);
-        f32x4 *pv = reinterpret_cast<f32x4 *>(master + off);
-        f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
-        f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
-        if (sp.lead == 0 && ch.count == kTileElems) {
-            if (!adamw_vectors<4, MATH, TABLE>(0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg, table,
-                                               row, n_rows, S))
-                return;
-        } else if (sp.lead == 0 && ch.count % kTileElems == 0) {
-            for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
-                if (!adamw_vectors<4, MATH, TABLE>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg,
-                                                   table, row, n_rows, S))
-                    return;
-        } else {
-            int q0 = sp.qb;
-            for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
-                if (!adamw_vectors<2, MATH, TABLE>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales,
-                                                   k_arg, table, row, n_rows, S))
-                    return;
-            for (int q = q0 + t; q < sp.qe; q += kBlock)
-                if (!adamw_vectors<1, MATH, TABLE>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales,
-                                                   k_arg, table, row, n_rows, S))
-                    return;
-            if (sp.lead != 0 || sp.end % kVec != 0) {
-                AdamConsts k;
-                if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
-                    return;
-                const double c = MATH ? clip_coef(k, S) : 1.0;
-                const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
-                gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
-                const float *a = acc + off;
-                float *p = master + off;
-                float *m = exp_avg + off;
-                float *v = exp_avg_sq + off;
-                for_partial_elems(sp, [&](int e) {
-                    if constexpr (MATH) {
-                        const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
-                        p[e] = r.p;
-                        m[e] = r.m;
-                        v[e] = r.v;
-                        w[e] = (uint16_t)bf16_rne(r.p);
-                    } else {
-                        const float x = p[e] + a[e];
-                        p[e] = x;
-                        m[e] = m[e] + a[e];
-                        v[e] = v[e] + a[e];
-                        w[e] = (uint16_t)(__float_as_uint(x) >> 16);
-                    }
-                });
-            }
-        }
+        if (!adamw_piece<MATH, TABLE>(chunks[ci], wtab, scales, acc, master, exp_avg, exp_avg_sq,
+                                      k_arg, S, table, row, n_rows))
+            return;
         if constexpr (ONE)
             break;
+    }
+}
+
+// AdamW over the arena of a packed plan (ArenaWalk): workgroup j < n_tiles
+// takes 4096-element tile j, workgroup n_tiles + i the i-th boundary segment.
+// Every stream of a packed plan is addressed by arena position, so a tile
+// that ends inside the arena is loaded whole first, at addresses that depend
+// on nothing fetched; its tag, read after the loads are issued, names the
+// tensor whose slice holds the tile.  A tile that crosses a slice boundary
+// (or the arena's end) stores nothing, and neither does any tile when the
+// per-step table is exhausted; those leave through a branch that consumes
+// the loaded registers, so the compiler keeps the loads ahead of the tag
+// test, and the update and stores of a live tile stay one unconditional
+// sequence whose waits count its own stores.  The slice segments of boundary
+// tiles run on their own workgroups as chunk-table pieces.  Same arithmetic,
+// constants, table handling and twin (MATH = false) as k_adamw.
+template <bool MATH, bool TABLE>
+__global__ __launch_bounds__(kBlock) void k_adamw_tiles(
+    const int32_t *__restrict__ tags, const Chunk *__restrict__ segs, int64_t n_tiles,
+    int64_t n_full, uint16_t *__restrict__ wbase, uint16_t *const *__restrict__ wtab,
+    const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
+    float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
+    const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
+    const int64_t *__restrict__ state)
+{
+    const int64_t row = TABLE ? state[0] : 0;
+    const int t = (int)threadIdx.x;
+    const int64_t j = blockIdx.x;
+    if (j >= n_tiles) {
+        adamw_piece<MATH, TABLE>(segs[j - n_tiles], wtab, scales, acc, master, exp_avg,
+                                 exp_avg_sq, k_arg, S, table, row, n_rows);
+        return;
+    }
+    if (j >= n_full)
+        return;
+    const int64_t q0 = j * (kTileElems / kVec);
+    const char *ab = reinterpret_cast<const char *>(reinterpret_cast<const f32x4 *>(acc) + q0);
+    char *pb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(master) + q0);
+    char *mb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(exp_avg) + q0);
+    char *vb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(exp_avg_sq) + q0);
+    f32x4 ar[4], pr[4], mr[4], vr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
+        ar[u] = ld_stream(reinterpret_cast<const f32x4 *>(ab + o));
+        pr[u] = ld_stream(reinterpret_cast<const f32x4 *>(pb + o));
+        mr[u] = ld_stream(reinterpret_cast<const f32x4 *>(mb + o));
+        vr[u] = ld_stream(reinterpret_cast<const f32x4 *>(vb + o));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int32_t tag = tags[j];
+    AdamConsts k;
+    if (!step_consts<TABLE>(k_arg, table, row, n_rows, k) || tag < 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            __asm__ volatile("" ::"v"(ar[u]), "v"(pr[u]), "v"(mr[u]), "v"(vr[u]));
+        return;
+    }
+    const double c = MATH ? clip_coef(k, S) : 1.0;
+    const TensorRate tr = MATH ? tensor_rate(k, scales[tag]) : TensorRate{};
+    gmem<char> *wb8 = reinterpret_cast<gmem<char> *>(to_global(wbase)) + q0 * 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
+        u32x2 wb;
+        if constexpr (MATH)
+            adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
+        else
+            traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
+        st_stream(reinterpret_cast<f32x4 *>(pb + o), pr[u]);
+        st_stream(reinterpret_cast<f32x4 *>(mb + o), mr[u]);
+        st_stream(reinterpret_cast<f32x4 *>(vb + o), vr[u]);
+        st_stream(reinterpret_cast<gmem<u32x2> *>(wb8 + o / 2), wb);
     }
 }
 
@@ -1037,6 +1129,13 @@ void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, con
 {
     const dim3 block(kBlock);
     const int64_t n = geo.n_chunks;
+    if (geo.arena.n_tiles > 0) {
+        const ArenaWalk &aw = geo.arena;
+        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)(aw.n_tiles + aw.n_segs)), block, 0, s>>>(
+            aw.tags, aw.segs, aw.n_tiles, aw.n_full, aw.wbase, weight_tab, scales, acc, master, m,
+            v, k, S, table, n_rows, state);
+        return;
+    }
     if (geo.grid < n)
         k_adamw<MATH, TABLE, false><<<dim3((unsigned)geo.grid), block, 0, s>>>(
             geo.chunks, n, weight_tab, scales, acc, master, m, v, k, S, table, n_rows, state);

@@ -43,7 +43,8 @@ class ShardStep:
                  grads: Optional[List[List[torch.Tensor]]] = None,
                  arena_pad: int = 0, kind: str = "per_tensor",
                  lr_scale: Optional[Sequence[float]] = None,
-                 wd_scale: Optional[Sequence[float]] = None, layout: str = "full"):
+                 wd_scale: Optional[Sequence[float]] = None, layout: str = "full",
+                 walk: str = "auto"):
         self.shapes = [tuple(s) for s in shapes]
         self.numel = [int(torch.Size(s).numel()) for s in self.shapes]
         self.rows = [int(s[0]) if len(s) else 1 for s in self.shapes]
@@ -79,7 +80,8 @@ class ShardStep:
                                      self.master, self.exp_avg, self.exp_avg_sq, self.acc,
                                      chunk_elems=chunk_elems, max_blocks=max_blocks, kind=kind,
                                      rows=self.rows if kind == "dim0" else None,
-                                     lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
+                                     lr_scale=lr_scale, wd_scale=wd_scale, layout=layout,
+                                     walk=walk)
         self.plan_create_s = time.perf_counter() - t0   # plan + chunk table + upload
         self.t = 0
 

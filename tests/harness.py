@@ -68,7 +68,7 @@ class Parity:
 
     def __init__(self, w: W.Workload, device="cuda", chunk_elems=0, max_blocks=0,
                  seed=0, canaries=True, kind="per_tensor", lr_scale=None, wd_scale=None,
-                 ranges=None, layout="full"):
+                 ranges=None, layout="full", walk="auto"):
         self.w = w
         self.ranges = ranges     # None: one accumulation call per micro-batch
         self.dev = torch.device(device)
@@ -78,7 +78,7 @@ class Parity:
         self.st = ShardStep(w.shapes, w.dp_size, w.rank, w.n_micro, device=self.dev,
                             chunk_elems=chunk_elems, max_blocks=max_blocks,
                             arena_pad=64 if canaries else 0, kind=kind,
-                            lr_scale=lr_scale, wd_scale=wd_scale, layout=layout)
+                            lr_scale=lr_scale, wd_scale=wd_scale, layout=layout, walk=walk)
         rows = [s[0] if len(s) else 1 for s in w.shapes]
         self.o_start, self.o_len = self.o.plan(kind, w.numel, rows, w.dp_size, w.rank)
         self.segments = None

@@ -125,7 +125,9 @@ def _bind(**over):
     (dict(master=0), B.Z1_EINVAL), (dict(w0=0), B.Z1_EINVAL), (dict(g1=0), B.Z1_EINVAL),
     (dict(w0=0x10008), B.Z1_EALIGN), (dict(g1=0x30002), B.Z1_EALIGN),
     (dict(acc=0x70004), B.Z1_EALIGN),
-    (dict(layout=2), B.Z1_EINVAL), (dict(reserved=1), B.Z1_EINVAL),
+    (dict(layout=2), B.Z1_EINVAL), (dict(walk=3), B.Z1_EINVAL), (dict(walk=-1), B.Z1_EINVAL),
+    (dict(walk=2), B.Z1_EINVAL),                       # arena tiles need the packed layout
+    (dict(walk=2, layout=1, max_blocks=4), B.Z1_EINVAL),   # ... and one workgroup per tile
     (dict(layout=1, w0=0), B.Z1_EINVAL), (dict(layout=1, g1=0), B.Z1_EINVAL),
     (dict(layout=1, w0=0x10008), B.Z1_EALIGN), (dict(layout=1, g1=0x30002), B.Z1_EALIGN),
 ])

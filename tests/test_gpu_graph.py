@@ -228,15 +228,18 @@ def _random_multipliers(n, seed):
     return lr_s, wd_s
 
 
-@pytest.mark.parametrize("w,mult,style", [
-    (W.TINY, None, "cosine"),
-    (W.TINY, "mup", "cosine"),
-    (RAGGED_SMALL, None, "linear"),
-    (RAGGED_SMALL, "random", "cosine"),
-    (W.SMOLLM_135M, "mup", "cosine"),
+@pytest.mark.parametrize("w,mult,style,walk", [
+    (W.TINY, None, "cosine", None),
+    (W.TINY, "mup", "cosine", None),
+    (RAGGED_SMALL, None, "linear", None),
+    (RAGGED_SMALL, "random", "cosine", None),
+    (W.SMOLLM_135M, "mup", "cosine", None),
+    (W.TINY, "mup", "cosine", "arena_tiles"),
+    (RAGGED_SMALL, "random", "linear", "arena_tiles"),
 ], ids=["tiny_cosine", "tiny_mup_cosine", "ragged_small_linear", "ragged_small_mult_cosine",
-        "smollm135m_mup_cosine"])
-def test_scheduled_graph_matches_oracle(w, mult, style):
+        "smollm135m_mup_cosine", "tiny_mup_cosine_packed_arena",
+        "ragged_small_mult_linear_packed_arena"])
+def test_scheduled_graph_matches_oracle(w, mult, style, walk):
     """[accumulate all slots, norm, z1_adamw_step_scheduled] captured once and
     replayed for 8 steps of a learning-rate schedule (3 warmup steps, 4 decay
     steps, then the minimum), with fresh gradients before every replay.  Each
@@ -244,7 +247,8 @@ def test_scheduled_graph_matches_oracle(w, mult, style):
     oracle's own rate lr_at(t) (Nanotron Guide, config.yaml: learning_rate,
     lr_warmup_steps, lr_decay_steps, min_decay_lr), with the per-tensor
     multipliers as oracle segments: acc, S, master, m, v and the bf16 weights
-    bit for bit."""
+    bit for bit.  With walk set, the plan is packed and AdamW takes that
+    walk."""
     import harness
     from mixed_precision_zero_amd import binding as B
     T, warm, decay = 8, 3, 4
@@ -257,7 +261,8 @@ def test_scheduled_graph_matches_oracle(w, mult, style):
         lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
     elif mult == "random":
         lr_s, wd_s = _random_multipliers(len(w.shapes), seed=11)
-    h = harness.Parity(w, lr_scale=lr_s, wd_scale=wd_s, ranges=[(0, w.n_micro)])
+    layout = dict(layout="packed", walk=walk) if walk else {}
+    h = harness.Parity(w, lr_scale=lr_s, wd_scale=wd_s, ranges=[(0, w.n_micro)], **layout)
     sched = None
     try:
         assert h.plan_matches()
