@@ -469,7 +469,8 @@ def main():
                    "adamw_walk": "arena_tiles" if st.plan.info.adamw_tiles else "chunks",
                    "adamw_tiles": int(st.plan.info.adamw_tiles),
                    "boundary_tiles": int(st.plan.info.boundary_tiles)},
-        "roofline": {"bound": "hbm", "kernel": "k_adamw",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_adamw_tiles" if st.plan.info.adamw_tiles else "k_adamw",
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_param": BYTES_ADAMW,
