@@ -17,6 +17,11 @@ On about 20k sampled elements (the ends of each slice, the neighbourhoods of
 the 2^31 and 2^32 crossings, uniform picks, all of the small tensor) the
 accumulated gradient, master, m, v and the bf16 weights must equal the
 oracle's bits; weights outside this rank's slices must stay untouched.
+
+The packed case binds packed bf16 shards (gradients and weights at arena
+positions past 2^31) and forces AdamW's arena walk, whose tiles then sit
+more than 2^31 elements (8 GB of fp32) into the arenas; the padding of the
+packed weight shard must stay untouched.
 """
 import numpy as np
 import pytest
@@ -60,14 +65,20 @@ def _gather(st, picks):
     """Sampled acc / master / m / v (fp32), weights and grads (bf16 bits)."""
     f32 = {name: [] for name in ("acc", "master", "exp_avg", "exp_avg_sq")}
     w, g = [], [[] for _ in range(st.n_micro)]
+    packed = st.layout == "packed"
     for i, s, off, j in picks:
         a_idx = torch.from_numpy(off + j).cuda()
         f_idx = torch.from_numpy(s + j).cuda()
         for name in f32:
             f32[name].append(getattr(st, name)[a_idx].cpu().numpy())
-        w.append(st.weights[i].view(torch.int16)[f_idx].cpu().numpy().view(np.uint16))
+        if packed:
+            w.append(st.w_packed.view(torch.int16)[a_idx].cpu().numpy().view(np.uint16))
+        else:
+            w.append(st.weights[i].view(torch.int16)[f_idx].cpu().numpy().view(np.uint16))
         for k in range(st.n_micro):
-            g[k].append(st.grads[k][i].view(torch.int16)[f_idx].cpu().numpy().view(np.uint16))
+            src = st.g_packed[k] if packed else st.grads[k][i]
+            idx = a_idx if packed else f_idx
+            g[k].append(src.view(torch.int16)[idx].cpu().numpy().view(np.uint16))
     cat = {k: np.ascontiguousarray(np.concatenate(v)) for k, v in f32.items()}
     return cat, np.concatenate(w), np.stack([np.concatenate(x) for x in g])
 
@@ -76,19 +87,26 @@ def _bits(x):
     return np.ascontiguousarray(x).view(np.uint32)
 
 
-def test_shard_past_32_bit_indexes_matches_oracle():
+@pytest.mark.parametrize("layout", ["full", "packed_arena"])
+def test_shard_past_32_bit_indexes_matches_oracle(layout):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     O = oracle.get()
-    st = ShardStep([(BIG,), (SMALL,)], 2, 1, 2, device="cuda")
+    packed = layout == "packed_arena"
+    kw = dict(layout="packed", walk="arena_tiles") if packed else {}
+    st = ShardStep([(BIG,), (SMALL,)], 2, 1, 2, device="cuda", **kw)
     try:
         n_shard = int(st.len.sum())
         assert int(st.start[0]) == (1 << 31) + 5 and int(st.len[0]) == (1 << 31) + 5
         assert int(st.arena_off[1]) + int(st.len[1]) > (1 << 31)
         gen = torch.Generator(device="cuda")
         gen.manual_seed(20240607)
-        for i, shape in enumerate(st.shapes):
-            _fill_signs([st.grads[k][i] for k in range(st.n_micro)], shape[0], gen)
+        if packed:
+            assert st.plan.info.adamw_tiles > (1 << 19)
+            _fill_signs(st.g_packed, st.g_packed[0].numel(), gen)
+        else:
+            for i, shape in enumerate(st.shapes):
+                _fill_signs([st.grads[k][i] for k in range(st.n_micro)], shape[0], gen)
         st.master.normal_(0.0, 0.02, generator=gen)
         torch.cuda.synchronize()
 
@@ -125,11 +143,20 @@ def test_shard_past_32_bit_indexes_matches_oracle():
                 assert bad.size == 0, f"step {t}: {name} differs at {bad.size} samples"
             assert np.array_equal(w_got, w_ref), f"step {t}: bf16 weights"
 
-        # the other rank's part of every tensor is never written
-        for i, s, ln, _ in st.slices():
-            lo = max(0, s - 4096)
-            other = st.weights[i].view(torch.int16)[lo:s].cpu().numpy()
-            assert not other.any(), f"tensor {i}: weights outside the slice were written"
+        # the other rank's part of every tensor (full layout) or the padding
+        # between slices (packed shard) is never written
+        if packed:
+            wp = st.w_packed.view(torch.int16)
+            ends = sorted((off, off + ln) for _, _, ln, off in st.slices() if ln)
+            gaps = [(0, ends[0][0])] + [(e0, s1) for (_, e0), (s1, _) in zip(ends, ends[1:])]
+            gaps.append((ends[-1][1], wp.numel()))
+            for lo, hi in gaps:
+                assert not bool(wp[lo:hi].any()), f"packed padding [{lo}, {hi}) written"
+        else:
+            for i, s, ln, _ in st.slices():
+                lo = max(0, s - 4096)
+                other = st.weights[i].view(torch.int16)[lo:s].cpu().numpy()
+                assert not other.any(), f"tensor {i}: weights outside the slice were written"
     finally:
         st.close()
         del st
