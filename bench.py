@@ -39,7 +39,9 @@ BYTES_ACC_FIRST = 6              # read bf16 g (2); write acc (4)
 BYTES_ACC_NEXT = 10              # read bf16 g (2) + acc (4); write acc (4)
 MAX_SLOTS = 16                   # micro-batch slots per multi-slot pass
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "z1_kernels.hip")
+# the kernels and the constants that fix their launch shapes
+KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
+                    for f in ("z1_internal.h", "z1_kernels.hip"))
 
 
 def accum_bytes(K: int, resident: bool) -> int:
@@ -99,11 +101,14 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the kernel source with comments and whitespace removed,
-    so that counters taken on a kernel stay attached to it through comment
-    edits and are dropped after any change to the code."""
-    with open(KERNEL_SRC) as f:
-        src = f.read()
+    """sha256[:16] of the kernel sources (z1_internal.h, then z1_kernels.hip)
+    with comments and whitespace removed, so that counters taken on a kernel
+    stay attached to it through comment edits and are dropped after any
+    change to the code."""
+    src = ""
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = re.sub(r"\s+", "", src)

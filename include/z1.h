@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define Z1_ABI_VERSION 9
+#define Z1_ABI_VERSION 10
 
 typedef enum z1_status {
     Z1_OK = 0,
@@ -191,8 +191,9 @@ typedef struct z1_bind {
                                (4096); otherwise a multiple of 1024 in
                                [1024, 1048576]                              */
     int32_t max_blocks;     /* 0 = one workgroup per chunk; otherwise the
-                               grid size of the accumulation and AdamW
-                               kernels (each workgroup loops over chunks)  */
+                               grid size of the accumulation kernels, and
+                               4 x max_blocks one-wave workgroups for AdamW
+                               (each workgroup loops over its work)        */
     int32_t plan_kind;      /* z1_plan_kind (0 = per tensor)                */
     const int64_t *rows;    /* host [n_tensors] dim-0 sizes for
                                Z1_PLAN_DIM0, else NULL                      */
@@ -219,10 +220,12 @@ typedef enum z1_layout {
 } z1_layout;
 
 /* How the AdamW step walks the shard (z1_bind.walk); the arithmetic and the
- * bits stored are the same either way.
- *   Z1_WALK_CHUNKS       one workgroup per entry of the chunk table (the
- *                        accumulation and norm kernels always walk it).
- *   Z1_WALK_ARENA_TILES  packed layout only: one workgroup per 4096-element
+ * bits stored are the same either way.  AdamW runs one-wave workgroups of 256
+ * elements (one 4-element vector per lane), chunk_elems / 256 of them per
+ * piece, at most 16 resident per compute unit.
+ *   Z1_WALK_CHUNKS       the workgroups of each entry of the chunk table
+ *                        (the accumulation and norm kernels always walk it).
+ *   Z1_WALK_ARENA_TILES  packed layout only: 16 workgroups per 4096-element
  *                        tile of the arena, every stream addressed by arena
  *                        position, so a tile's loads depend on nothing
  *                        fetched first.  A tile inside one slice takes its
@@ -234,7 +237,7 @@ typedef enum z1_layout {
  *                        its tiles crossing a slice boundary (the loads of
  *                        such a tile are issued before its tag is known and
  *                        then discarded), otherwise the chunk table.
- * The arena walk runs one workgroup per tile, so AUTO keeps the chunk table
+ * The arena walk runs 16 workgroups per tile, so AUTO keeps the chunk table
  * when max_blocks caps the grid.  Z1_WALK_ARENA_TILES with the full layout or
  * with max_blocks > 0, or any other value, is Z1_EINVAL at plan creation. */
 typedef enum z1_walk {
@@ -607,13 +610,14 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
  *                           (G = n_bufs - 1 in [2, 16]): 2G + 4 B per element,
  *                           the first resident-slot accumulation pass
  *   Z1_PROBE_ADAMW_TRAFFIC_WAVE  as Z1_PROBE_ADAMW_TRAFFIC, in one-wave (64-lane)
- *                           workgroups: the shape at which this mix streams
- *                           fastest without arithmetic
+ *                           workgroups of one vector per lane, at most 12 of
+ *                           them resident per compute unit: the shape at
+ *                           which this mix streams fastest without arithmetic
  *   Z1_PROBE_SLOTS_TRAFFIC_ONE   as Z1_PROBE_SLOTS_TRAFFIC, one vector per lane
  *                           (256 vectors per workgroup)
- * The step kernels' own shape is the default: 256-lane workgroups with 4
+ * The default shape is the accumulation kernels': 256-lane workgroups with 4
  * vectors per lane.  The contents written are meaningless.  Z1_EINVAL also
- * when n_vec needs more than 2^31 - 1 workgroups of 256 vectors.  Errors:
+ * when n_vec needs more than 2^31 - 1 workgroups of 64 vectors.  Errors:
  * Z1_EINVAL, Z1_EALIGN, Z1_EHIP.
  * ------------------------------------------------------------------------ */
 enum {

@@ -23,6 +23,9 @@ struct z1_plan {
     int32_t n = 0, K = 0, dp = 0, rank = 0;
     int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
     int grid = 0;
+    int32_t adam_sub = 1;   // AdamW workgroups per piece
+    int64_t adam_grid = 0;  // AdamW's chunk-walk grid
+    uint32_t adam_lds = 0;  // LDS reserved per AdamW workgroup
     std::vector<int64_t> start, len, arena_off;
     // device memory owned by the plan
     Chunk *d_chunks = nullptr;
@@ -267,6 +270,9 @@ z1_status device_alloc(T **out, size_t count)
 z1::LaunchGeom geom(const z1_plan *p)
 {
     z1::LaunchGeom g{p->d_chunks, p->n_chunks, p->grid};
+    g.adam_sub = p->adam_sub;
+    g.adam_grid = p->adam_grid;
+    g.adam_lds = p->adam_lds;
     if (p->n_tiles > 0) {
         g.arena.tags = p->d_tags;
         g.arena.segs = p->d_segs;
@@ -624,6 +630,15 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if (b->max_blocks > 0 && grid > b->max_blocks)
         grid = b->max_blocks;
     p->grid = (int)(grid > 0 ? grid : 1);
+    // AdamW: chunk / kAdamBlockElems one-wave workgroups per piece; a capped
+    // grid keeps the lanes of max_blocks 256-lane workgroups
+    p->adam_sub = (int32_t)(chunk / z1::kAdamBlockElems);
+    int64_t adam_grid = p->n_chunks * p->adam_sub;
+    if (b->max_blocks > 0 && adam_grid > (int64_t)b->max_blocks * (z1::kBlock / z1::kWave))
+        adam_grid = (int64_t)b->max_blocks * (z1::kBlock / z1::kWave);
+    if (adam_grid > INT32_MAX)
+        adam_grid = INT32_MAX;
+    p->adam_grid = adam_grid > 0 ? adam_grid : 1;
 
     // AdamW's arena walk: forced, or chosen for a packed plan whose tiles
     // cross slice boundaries rarely (at most 1 in 100; the loads such a tile
@@ -635,7 +650,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         arena_walk(n, p->start.data(), p->len.data(), p->arena_off.data(), p->arena_elems, tags,
                    segs, n_full, n_boundary);
         const int64_t n_tiles = (int64_t)tags.size();
-        const bool fits = n_tiles + (int64_t)segs.size() <= INT32_MAX;
+        const bool fits = (n_tiles + (int64_t)segs.size()) * z1::kAdamTileBlocks <= INT32_MAX;
         if (b->walk == Z1_WALK_ARENA_TILES && !fits)
             return Z1_EINVAL;
         if (fits && (b->walk == Z1_WALK_ARENA_TILES || n_boundary * 100 <= n_tiles)) {
@@ -654,6 +669,11 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         return Z1_EHIP;
     if (!stream_on(p->device, stream))
         return Z1_EINVAL;
+    int lds_per_cu = 0;
+    if (hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              p->device) != hipSuccess || lds_per_cu < 0)
+        return Z1_EHIP;
+    p->adam_lds = (uint32_t)(lds_per_cu / z1::kAdamPerCU);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||

@@ -20,9 +20,15 @@ constexpr int64_t kMaxChunk = 1 << 20;
 // land on different XCDs, each XCD walking one contiguous region); AdamW
 // issues it in table order.
 constexpr int kInterleave = 8;
-// AdamW's straight-line unit: 4 vectors of 4 elements per lane.  A piece of
-// exactly this many elements starting on a vector boundary is a whole tile.
+// A whole tile: 4 vectors of 4 elements per lane of a kBlock workgroup (the
+// default piece, AdamW's arena tile, the flat norm's unit).
 constexpr int64_t kTileElems = 4 * kBlock * kVec;
+// AdamW runs one-wave workgroups of one vector per lane: a block of
+// kWave * kVec elements, kAdamTileBlocks of them per tile, at most kAdamPerCU
+// workgroups resident per compute unit (held there by an LDS reservation).
+constexpr int kAdamBlockElems = kWave * kVec;
+constexpr int kAdamTileBlocks = (int)(kTileElems / kAdamBlockElems);
+constexpr int kAdamPerCU = 16;
 constexpr int kMaxSlots = 16;    // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
@@ -85,6 +91,9 @@ struct LaunchGeom {
     int64_t n_chunks;
     int grid;             // workgroups for the chunk kernels
     ArenaWalk arena{};    // AdamW's arena walk, when n_tiles > 0
+    int32_t adam_sub = 1;    // AdamW workgroups per piece (chunk_elems / kAdamBlockElems)
+    int64_t adam_grid = 0;   // AdamW's chunk-walk grid (< n_chunks * adam_sub: it loops)
+    uint32_t adam_lds = 0;   // LDS bytes each AdamW workgroup reserves (the residency cap)
 };
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,

@@ -699,78 +699,72 @@ __device__ __forceinline__ bool step_consts(const AdamConsts &k_arg,
     return true;
 }
 
-// U consecutive vectors per lane (vector q0 + u * kBlock + t for u < U) of
-// the piece ch: all loads issued first, then the step's constants, the clip
-// coefficient, the tensor's rate and its bf16 pointer (lookups whose latency
-// then hides behind the loads), then update and store vector by vector.
-// False (nothing stored) when the per-step table is exhausted.  MATH = false
-// is the measurement twin (traffic_vec).
-template <int U, bool MATH, bool TABLE>
-__device__ __forceinline__ bool adamw_vectors(int q0, const Chunk &ch, int lead,
-                                              const f32x4 *__restrict__ av,
-                                              f32x4 *__restrict__ pv, f32x4 *__restrict__ mv,
-                                              f32x4 *__restrict__ vv,
-                                              uint16_t *const *__restrict__ wtab,
-                                              const Scale *__restrict__ scales,
-                                              const AdamConsts &k_arg,
-                                              const AdamConsts *__restrict__ table, int64_t row,
-                                              int64_t n_rows, const double *__restrict__ S)
+// AdamW runs on one-wave workgroups with one vector (4 elements) per lane: a
+// block is kWave consecutive vectors, and a 4096-element piece or arena tile
+// is kAdamTileBlocks blocks on as many workgroups.  Each launch reserves
+// dynamic LDS (which no lane touches) so that at most kAdamPerCU of its
+// workgroups share a compute unit.  This mix is half writes: with the chip
+// full of loads the memory controller's write credits run short, and a lower,
+// steady number of waves in flight streams it faster.  Measured on the 7B
+// shard's buffers with the update in place: 256-lane workgroups with 4
+// vectors per lane 5.5-6.1 TB/s, one-wave workgroups with 1 vector per lane
+// 6.1-6.6 TB/s at 14-16 per compute unit (6 per CU: 4.3; no cap: 6.1-6.4).
+
+// Lane t's vector of the four fp32 streams of a block, at byte offset o from
+// the block's bases, loads issued back to back.
+struct LaneVec {
+    f32x4 a, p, m, v;
+};
+
+__device__ __forceinline__ LaneVec load_lane(const char *ab, const char *pb, const char *mb,
+                                             const char *vb, uint32_t o)
 {
-    // every access is a workgroup-uniform base (vector q0 of the stream) plus
-    // a 32-bit byte offset that depends only on the lane and u, so all of them
-    // take a scalar base and the lanes share U offset registers
-    const int t = (int)threadIdx.x;
-    const char *ab = reinterpret_cast<const char *>(av + q0);
-    char *pb = reinterpret_cast<char *>(pv + q0);
-    char *mb = reinterpret_cast<char *>(mv + q0);
-    char *vb = reinterpret_cast<char *>(vv + q0);
-    f32x4 ar[U], pr[U], mr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
-        ar[u] = ld_stream(reinterpret_cast<const f32x4 *>(ab + o));
-        pr[u] = ld_stream(reinterpret_cast<const f32x4 *>(pb + o));
-        mr[u] = ld_stream(reinterpret_cast<const f32x4 *>(mb + o));
-        vr[u] = ld_stream(reinterpret_cast<const f32x4 *>(vb + o));
-        // loads issued vector by vector, all ahead of the arithmetic: left to
-        // itself the scheduler reorders them and sinks the last ones below the
-        // first update, and the waits then drain every load before the rest
-        // of the tile is issued; in this order the update of vector u waits
-        // only for its own four loads
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    AdamConsts k;
-    if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
-        return false;
-    const double c = MATH ? clip_coef(k, S) : 1.0;
-    const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
-    gmem<char> *wb8 = reinterpret_cast<gmem<char> *>(to_global(wtab[ch.tensor]) + (ch.src - lead)) +
-                      (int64_t)q0 * 8;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
-        u32x2 wb;
-        if constexpr (MATH)
-            adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
-        else
-            traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
-        st_stream(reinterpret_cast<f32x4 *>(pb + o), pr[u]);
-        st_stream(reinterpret_cast<f32x4 *>(mb + o), mr[u]);
-        st_stream(reinterpret_cast<f32x4 *>(vb + o), vr[u]);
-        st_stream(reinterpret_cast<gmem<u32x2> *>(wb8 + o / 2), wb);
-    }
-    return true;
+    LaneVec x;
+    x.a = ld_stream(reinterpret_cast<const f32x4 *>(ab + o));
+    x.p = ld_stream(reinterpret_cast<const f32x4 *>(pb + o));
+    x.m = ld_stream(reinterpret_cast<const f32x4 *>(mb + o));
+    x.v = ld_stream(reinterpret_cast<const f32x4 *>(vb + o));
+    return x;
 }
 
-// One piece of AdamW, on the whole workgroup.  A whole tile (exactly
-// kTileElems elements from a vector boundary: every piece of the 7B-shaped
-// lists but the norm weights' slices, every interior piece at the default
-// chunk size) runs as one straight-line tile of 4 vectors per lane; any other
-// piece runs whole tiles in a loop or 2 vectors, then 1, per lane, and its
-// partial head and tail vectors element by element.  False (nothing more
-// stored) when the per-step table is exhausted.
+// An exit that stores nothing still consumes the loaded registers, so the
+// compiler keeps the loads ahead of the test that leads to it.
+__device__ __forceinline__ void discard_lane(const LaneVec &x)
+{
+    __asm__ volatile("" ::"v"(x.a), "v"(x.p), "v"(x.m), "v"(x.v));
+}
+
+// The update of lane t's vector and its four stores (the bf16 stream at half
+// the fp32 offset).  MATH = false is the measurement twin (traffic_vec).
+template <bool MATH>
+__device__ __forceinline__ void update_store_lane(LaneVec x, char *pb, char *mb, char *vb,
+                                                  gmem<char> *wb, uint32_t o,
+                                                  const AdamConsts &k, const TensorRate &tr,
+                                                  double c)
+{
+    u32x2 w;
+    if constexpr (MATH)
+        adamw_vec(x.a, x.p, x.m, x.v, w, k, tr, c);
+    else
+        traffic_vec(x.a, x.p, x.m, x.v, w);
+    st_stream(reinterpret_cast<f32x4 *>(pb + o), x.p);
+    st_stream(reinterpret_cast<f32x4 *>(mb + o), x.m);
+    st_stream(reinterpret_cast<f32x4 *>(vb + o), x.v);
+    st_stream(reinterpret_cast<gmem<u32x2> *>(wb + o / 2), w);
+}
+
+// The blocks sub, sub + nsub, ... of the piece ch (vector q of the piece
+// covers piece-relative elements [4q - lead, 4q + 4 - lead), as in Span).
+// A block of full vectors runs straight-line: its loads first, then the
+// step's constants, the clip coefficient, the tensor's rate and its bf16
+// pointer (lookups whose latency hides behind the loads), then the update
+// and the stores.  A block holding a slice's partial head or tail vector,
+// or the piece's end, runs lane by lane, each lane its own vector: full ones
+// whole, partial ones element by element.  False (nothing more stored) when
+// the per-step table is exhausted.
 template <bool MATH, bool TABLE>
-__device__ __forceinline__ bool adamw_piece(const Chunk &ch, uint16_t *const *__restrict__ wtab,
+__device__ __forceinline__ bool adamw_piece(const Chunk &ch, int sub, int nsub,
+                                            uint16_t *const *__restrict__ wtab,
                                             const Scale *__restrict__ scales,
                                             const float *__restrict__ acc,
                                             float *__restrict__ master,
@@ -783,42 +777,50 @@ __device__ __forceinline__ bool adamw_piece(const Chunk &ch, uint16_t *const *__
 {
     const int t = (int)threadIdx.x;
     const Span sp = span_of(ch);
+    const int nvec = (sp.end + kVec - 1) / kVec;
+    // lead-adjusted bases: vector 0 of the piece, on a 16-byte boundary of
+    // every fp32 arena (the arena offset shares the source's residue)
     const int64_t off = ch.dst - sp.lead;
-    const f32x4 *av = reinterpret_cast<const f32x4 *>(acc + off);
-    f32x4 *pv = reinterpret_cast<f32x4 *>(master + off);
-    f32x4 *mv = reinterpret_cast<f32x4 *>(exp_avg + off);
-    f32x4 *vv = reinterpret_cast<f32x4 *>(exp_avg_sq + off);
-    if (sp.lead == 0 && ch.count == kTileElems)
-        return adamw_vectors<4, MATH, TABLE>(0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg, table,
-                                             row, n_rows, S);
-    if (sp.lead == 0 && ch.count % kTileElems == 0) {
-        for (int q0 = 0; q0 < sp.qe; q0 += (int)(kTileElems / kVec))
-            if (!adamw_vectors<4, MATH, TABLE>(q0, ch, 0, av, pv, mv, vv, wtab, scales, k_arg,
-                                               table, row, n_rows, S))
-                return false;
-        return true;
-    }
-    int q0 = sp.qb;
-    for (; q0 + 2 * kBlock <= sp.qe; q0 += 2 * kBlock)
-        if (!adamw_vectors<2, MATH, TABLE>(q0, ch, sp.lead, av, pv, mv, vv, wtab, scales, k_arg,
-                                           table, row, n_rows, S))
-            return false;
-    for (int q = q0 + t; q < sp.qe; q += kBlock)
-        if (!adamw_vectors<1, MATH, TABLE>(q - t, ch, sp.lead, av, pv, mv, vv, wtab, scales,
-                                           k_arg, table, row, n_rows, S))
-            return false;
-    if (sp.lead != 0 || sp.end % kVec != 0) {
+    const char *ab = reinterpret_cast<const char *>(acc + off);
+    char *pb = reinterpret_cast<char *>(master + off);
+    char *mb = reinterpret_cast<char *>(exp_avg + off);
+    char *vb = reinterpret_cast<char *>(exp_avg_sq + off);
+    for (int q0 = sub * kWave; q0 < nvec; q0 += nsub * kWave) {
+        const uint32_t o = (uint32_t)(q0 + t) * 16u;
         AdamConsts k;
+        if (q0 >= sp.qb && q0 + kWave <= sp.qe) {
+            const LaneVec x = load_lane(ab, pb, mb, vb, o);
+            __builtin_amdgcn_sched_barrier(0);
+            if (!step_consts<TABLE>(k_arg, table, row, n_rows, k)) {
+                discard_lane(x);
+                return false;
+            }
+            const double c = MATH ? clip_coef(k, S) : 1.0;
+            const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
+            gmem<char> *wb = reinterpret_cast<gmem<char> *>(to_global(wtab[ch.tensor]) +
+                                                            (ch.src - sp.lead));
+            update_store_lane<MATH>(x, pb, mb, vb, wb, o, k, tr, c);
+            continue;
+        }
         if (!step_consts<TABLE>(k_arg, table, row, n_rows, k))
             return false;
         const double c = MATH ? clip_coef(k, S) : 1.0;
         const TensorRate tr = MATH ? tensor_rate(k, scales[ch.tensor]) : TensorRate{};
         gmem<uint16_t> *w = to_global(wtab[ch.tensor]) + (ch.src - sp.lead);
+        const int q = q0 + t;
+        if (q >= sp.qb && q < sp.qe) {
+            update_store_lane<MATH>(load_lane(ab, pb, mb, vb, o), pb, mb, vb,
+                                    reinterpret_cast<gmem<char> *>(w), o, k, tr, c);
+            continue;
+        }
+        // a partial vector: its elements inside [lead, end), one by one
         const float *a = acc + off;
         float *p = master + off;
         float *m = exp_avg + off;
         float *v = exp_avg_sq + off;
-        for_partial_elems(sp, [&](int e) {
+        const int e0 = q * kVec > sp.lead ? q * kVec : sp.lead;
+        const int e1 = q * kVec + kVec < sp.end ? q * kVec + kVec : sp.end;
+        for (int e = e0; e < e1; ++e) {
             if constexpr (MATH) {
                 const Elem r = adamw_elem(a[e], p[e], m[e], v[e], k, tr, c);
                 p[e] = r.p;
@@ -832,61 +834,58 @@ __device__ __forceinline__ bool adamw_piece(const Chunk &ch, uint16_t *const *__
                 v[e] = v[e] + a[e];
                 w[e] = (uint16_t)(__float_as_uint(x) >> 16);
             }
-        });
+        }
     }
     return true;
 }
 
-// AdamW over the chunk table: one workgroup per piece, pieces in table
-// (tensor) order.  The only lookup before the first vector load is the
-// piece's descriptor; with every access global, the update of each vector
-// waits only for its own loads.
-// ONE: one workgroup per piece and no loop over pieces, so no store of an
-// earlier piece is in flight when the loads are consumed (loads and stores
-// share one counter).  Measured on the 7B shard against the earlier kernel
-// (8-way interleaved issue order, 3 waves per SIMD): an 8-way order was 1-4%
-// slower for this kernel, whose five streams already spread every XCD over
-// the whole shard.
+// AdamW over the chunk table: workgroup b takes blocks of piece b / nsub
+// (nsub = chunk_elems / 256 per piece), pieces in table (tensor) order.  The
+// only lookup before the first vector load is the piece's descriptor.
+// ONE: one workgroup per (piece, sub) and no loop, so no store of an earlier
+// block is in flight when the loads are consumed (loads and stores share one
+// counter); otherwise the grid strides over the n_pieces * nsub indices.
 // MATH = false is a measurement twin: the same walk, loads and stores over
 // the same buffers, with the arithmetic replaced by traffic_vec, so the cost
 // of the update itself can be read off on the step's own buffers.
 // TABLE = true takes the step's constants from row state[0] of the per-step
-// table.  The row index is read as the kernel starts, next to the piece's
-// descriptor, and the row itself after the piece's loads are issued; when
-// the table is exhausted every workgroup returns before its first store.
+// table.  The row index is read as the kernel starts, and the row itself
+// after the block's loads are issued; when the table is exhausted every
+// workgroup returns before its first store.
 template <bool MATH, bool TABLE, bool ONE>
-__global__ __launch_bounds__(kBlock) void k_adamw(
-    const Chunk *__restrict__ chunks, int64_t n, uint16_t *const *__restrict__ wtab,
-    const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
-    float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
-    const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
-    const int64_t *__restrict__ state)
+__global__ __launch_bounds__(kWave) void k_adamw(
+    const Chunk *__restrict__ chunks, int64_t n_work, int32_t nsub,
+    uint16_t *const *__restrict__ wtab, const Scale *__restrict__ scales,
+    const float *__restrict__ acc, float *__restrict__ master, float *__restrict__ exp_avg,
+    float *__restrict__ exp_avg_sq, const AdamConsts k_arg, const double *__restrict__ S,
+    const AdamConsts *__restrict__ table, int64_t n_rows, const int64_t *__restrict__ state)
 {
     const int64_t row = TABLE ? state[0] : 0;
-    for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
-        if (!adamw_piece<MATH, TABLE>(chunks[ci], wtab, scales, acc, master, exp_avg, exp_avg_sq,
-                                      k_arg, S, table, row, n_rows))
+    for (int64_t b = blockIdx.x; b < n_work; b += gridDim.x) {
+        const int64_t ci = b / nsub;
+        if (!adamw_piece<MATH, TABLE>(chunks[ci], (int)(b - ci * nsub), nsub, wtab, scales, acc,
+                                      master, exp_avg, exp_avg_sq, k_arg, S, table, row,
+                                      n_rows))
             return;
         if constexpr (ONE)
             break;
     }
 }
 
-// AdamW over the arena of a packed plan (ArenaWalk): workgroup j < n_tiles
-// takes 4096-element tile j, workgroup n_tiles + i the i-th boundary segment.
-// Every stream of a packed plan is addressed by arena position, so a tile
-// that ends inside the arena is loaded whole first, at addresses that depend
-// on nothing fetched; its tag, read after the loads are issued, names the
-// tensor whose slice holds the tile.  A tile that crosses a slice boundary
-// (or the arena's end) stores nothing, and neither does any tile when the
-// per-step table is exhausted; those leave through a branch that consumes
-// the loaded registers, so the compiler keeps the loads ahead of the tag
-// test, and the update and stores of a live tile stay one unconditional
-// sequence whose waits count its own stores.  The slice segments of boundary
-// tiles run on their own workgroups as chunk-table pieces.  Same arithmetic,
-// constants, table handling and twin (MATH = false) as k_adamw.
+// AdamW over the arena of a packed plan (ArenaWalk): workgroup b takes block
+// b mod kAdamTileBlocks of tile b / kAdamTileBlocks; past the tiles, the
+// workgroups take the blocks of the boundary segments in turn.  Every stream
+// of a packed plan is addressed by arena position, so a block of a tile that
+// ends inside the arena is loaded first, at addresses that depend on nothing
+// fetched; the tile's tag, read after the loads are issued, names the tensor
+// whose slice holds it.  A tile that crosses a slice boundary (or the
+// arena's end) stores nothing, and neither does any tile when the per-step
+// table is exhausted; those leave through discard_lane, so the update and
+// stores of a live tile stay one unconditional sequence whose waits count its
+// own stores.  Same arithmetic, constants, table handling and twin
+// (MATH = false) as k_adamw.
 template <bool MATH, bool TABLE>
-__global__ __launch_bounds__(kBlock) void k_adamw_tiles(
+__global__ __launch_bounds__(kWave) void k_adamw_tiles(
     const int32_t *__restrict__ tags, const Chunk *__restrict__ segs, int64_t n_tiles,
     int64_t n_full, uint16_t *__restrict__ wbase, uint16_t *const *__restrict__ wtab,
     const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
@@ -895,54 +894,34 @@ __global__ __launch_bounds__(kBlock) void k_adamw_tiles(
     const int64_t *__restrict__ state)
 {
     const int64_t row = TABLE ? state[0] : 0;
-    const int t = (int)threadIdx.x;
-    const int64_t j = blockIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t j = b / kAdamTileBlocks;
     if (j >= n_tiles) {
-        adamw_piece<MATH, TABLE>(segs[j - n_tiles], wtab, scales, acc, master, exp_avg,
-                                 exp_avg_sq, k_arg, S, table, row, n_rows);
+        adamw_piece<MATH, TABLE>(segs[j - n_tiles], (int)(b % kAdamTileBlocks), kAdamTileBlocks,
+                                 wtab, scales, acc, master, exp_avg, exp_avg_sq, k_arg, S, table,
+                                 row, n_rows);
         return;
     }
     if (j >= n_full)
         return;
-    const int64_t q0 = j * (kTileElems / kVec);
+    const uint32_t o = (uint32_t)threadIdx.x * 16u;
+    const int64_t q0 = b * kWave;
     const char *ab = reinterpret_cast<const char *>(reinterpret_cast<const f32x4 *>(acc) + q0);
     char *pb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(master) + q0);
     char *mb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(exp_avg) + q0);
     char *vb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(exp_avg_sq) + q0);
-    f32x4 ar[4], pr[4], mr[4], vr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
-        ar[u] = ld_stream(reinterpret_cast<const f32x4 *>(ab + o));
-        pr[u] = ld_stream(reinterpret_cast<const f32x4 *>(pb + o));
-        mr[u] = ld_stream(reinterpret_cast<const f32x4 *>(mb + o));
-        vr[u] = ld_stream(reinterpret_cast<const f32x4 *>(vb + o));
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    const LaneVec x = load_lane(ab, pb, mb, vb, o);
+    __builtin_amdgcn_sched_barrier(0);
     const int32_t tag = tags[j];
     AdamConsts k;
     if (!step_consts<TABLE>(k_arg, table, row, n_rows, k) || tag < 0) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            __asm__ volatile("" ::"v"(ar[u]), "v"(pr[u]), "v"(mr[u]), "v"(vr[u]));
+        discard_lane(x);
         return;
     }
     const double c = MATH ? clip_coef(k, S) : 1.0;
     const TensorRate tr = MATH ? tensor_rate(k, scales[tag]) : TensorRate{};
-    gmem<char> *wb8 = reinterpret_cast<gmem<char> *>(to_global(wbase)) + q0 * 8;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t o = (uint32_t)(u * kBlock + t) * 16u;
-        u32x2 wb;
-        if constexpr (MATH)
-            adamw_vec(ar[u], pr[u], mr[u], vr[u], wb, k, tr, c);
-        else
-            traffic_vec(ar[u], pr[u], mr[u], vr[u], wb);
-        st_stream(reinterpret_cast<f32x4 *>(pb + o), pr[u]);
-        st_stream(reinterpret_cast<f32x4 *>(mb + o), mr[u]);
-        st_stream(reinterpret_cast<f32x4 *>(vb + o), vr[u]);
-        st_stream(reinterpret_cast<gmem<u32x2> *>(wb8 + o / 2), wb);
-    }
+    gmem<char> *wb = reinterpret_cast<gmem<char> *>(to_global(wbase)) + q0 * 8;
+    update_store_lane<MATH>(x, pb, mb, vb, wb, o, k, tr, c);
 }
 
 // Runs after the scheduled AdamW launch on the same stream: the next replay
@@ -1119,29 +1098,34 @@ hipError_t launch_norm_combine(const DD *pairs, int32_t n, double *S, hipStream_
     return hipGetLastError();
 }
 
-// AdamW over a plan's table: one workgroup per piece (the loop-free
-// variant), or max_blocks workgroups looping over the pieces.
+// AdamW over a plan: the arena walk, or the chunk table with one workgroup
+// per (piece, sub) (the loop-free variant) or a capped grid looping over
+// them; every launch reserves geo.adam_lds bytes of LDS per workgroup.
 template <bool MATH, bool TABLE>
 void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,
                          const float *acc, float *master, float *m, float *v,
                          const AdamConsts &k, const double *S, const AdamConsts *table,
                          int64_t n_rows, const int64_t *state, hipStream_t s)
 {
-    const dim3 block(kBlock);
-    const int64_t n = geo.n_chunks;
+    const dim3 block(kWave);
+    const size_t lds = geo.adam_lds;
     if (geo.arena.n_tiles > 0) {
         const ArenaWalk &aw = geo.arena;
-        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)(aw.n_tiles + aw.n_segs)), block, 0, s>>>(
+        const int64_t grid = (aw.n_tiles + aw.n_segs) * kAdamTileBlocks;
+        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)grid), block, lds, s>>>(
             aw.tags, aw.segs, aw.n_tiles, aw.n_full, aw.wbase, weight_tab, scales, acc, master, m,
             v, k, S, table, n_rows, state);
         return;
     }
-    if (geo.grid < n)
-        k_adamw<MATH, TABLE, false><<<dim3((unsigned)geo.grid), block, 0, s>>>(
-            geo.chunks, n, weight_tab, scales, acc, master, m, v, k, S, table, n_rows, state);
+    const int64_t n_work = geo.n_chunks * geo.adam_sub;
+    if (geo.adam_grid < n_work)
+        k_adamw<MATH, TABLE, false><<<dim3((unsigned)geo.adam_grid), block, lds, s>>>(
+            geo.chunks, n_work, geo.adam_sub, weight_tab, scales, acc, master, m, v, k, S, table,
+            n_rows, state);
     else
-        k_adamw<MATH, TABLE, true><<<dim3((unsigned)n), block, 0, s>>>(
-            geo.chunks, n, weight_tab, scales, acc, master, m, v, k, S, table, n_rows, state);
+        k_adamw<MATH, TABLE, true><<<dim3((unsigned)n_work), block, lds, s>>>(
+            geo.chunks, n_work, geo.adam_sub, weight_tab, scales, acc, master, m, v, k, S, table,
+            n_rows, state);
 }
 
 hipError_t launch_adamw(const LaunchGeom &geo, uint16_t *const *weight_tab, const Scale *scales,

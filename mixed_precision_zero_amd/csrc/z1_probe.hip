@@ -89,6 +89,32 @@ __global__ __launch_bounds__(NT) void k_probe_adamw(const f32x4 *__restrict__ a,
     }
 }
 
+// The same traffic in one-wave workgroups with one vector per lane, the
+// launch reserving LDS so that at most kProbeAdamPerCU workgroups share a
+// compute unit: the shape and residency at which this mix streams fastest
+// without arithmetic (measured on the 7B shard's buffers: 10-12 per compute
+// unit best, 6.3-6.6 TB/s, against 5.8-6.2 with no cap).
+constexpr int kProbeAdamPerCU = 12;
+
+__global__ __launch_bounds__(kWave) void k_probe_adamw_one(const f32x4 *__restrict__ a,
+                                                           f32x4 *__restrict__ p,
+                                                           f32x4 *__restrict__ m,
+                                                           f32x4 *__restrict__ v,
+                                                           u32x2 *__restrict__ w, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kWave + threadIdx.x;
+    if (i < n) {
+        const f32x4 ar = ld(a + i), pr = ld(p + i), mr = ld(m + i), vr = ld(v + i);
+        st(p + i, pr + ar);
+        st(m + i, mr + ar);
+        st(v + i, vr + ar);
+        u32x2 wb;
+        wb.x = __float_as_uint(pr.x);
+        wb.y = __float_as_uint(pr.y);
+        st(w + i, wb);
+    }
+}
+
 // k_accum's traffic (k >= 1): read a half-width g and acc, write acc.
 __global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict__ g,
                                                         f32x4 *__restrict__ acc, int64_t n)
@@ -199,9 +225,9 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
     }
     if (n_vec == 0)
         return Z1_OK;
-    // workgroups of the finest shape (256 vectors each) must fit the grid
+    // workgroups of the finest shape (64 vectors each) must fit the grid
     const int64_t blocks = (n_vec + kTileVec - 1) / kTileVec;
-    if ((n_vec + kBlock - 1) / kBlock > INT32_MAX)
+    if ((n_vec + kWave - 1) / kWave > INT32_MAX)
         return Z1_EINVAL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(kBlock);
@@ -219,13 +245,19 @@ extern "C" z1_status z1_probe(int32_t kind, void *const *bufs, int32_t n_bufs, i
             static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
             static_cast<u32x2 *>(bufs[4]), n_vec);
         break;
-    case Z1_PROBE_ADAMW_TRAFFIC_WAVE:
-        k_probe_adamw<kWave><<<dim3((unsigned)((n_vec + 4 * kWave - 1) / (4 * kWave))),
-                                dim3(kWave), 0, s>>>(
+    case Z1_PROBE_ADAMW_TRAFFIC_WAVE: {
+        int dev = 0, lds_per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                  dev) != hipSuccess || lds_per_cu < 0)
+            return Z1_EHIP;
+        k_probe_adamw_one<<<dim3((unsigned)((n_vec + kWave - 1) / kWave)), dim3(kWave),
+                            (size_t)(lds_per_cu / kProbeAdamPerCU), s>>>(
             static_cast<const f32x4 *>(bufs[0]), static_cast<f32x4 *>(bufs[1]),
             static_cast<f32x4 *>(bufs[2]), static_cast<f32x4 *>(bufs[3]),
             static_cast<u32x2 *>(bufs[4]), n_vec);
         break;
+    }
     case Z1_PROBE_ACCUM_TRAFFIC:
         k_probe_accum<<<grid, block, 0, s>>>(static_cast<const u32x2 *>(bufs[0]),
                                              static_cast<f32x4 *>(bufs[1]), n_vec);

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert B.z1_abi_version() == 9
+    assert B.z1_abi_version() == 10
     for s in range(6):
         assert B.strerror(s)
     assert B.strerror(99) == "unknown status"
@@ -176,6 +176,7 @@ def test_null_plan_calls():
     assert L.z1_probe(6, many, 18, 16, None) == B.Z1_EINVAL       # G = 17 > 16
     assert L.z1_probe(4, many, 18, 16, None) == B.Z1_EINVAL
     assert L.z1_probe(2, bufs, 5, (1 << 31) * 256, None) == B.Z1_EINVAL   # grid too large
+    assert L.z1_probe(2, bufs, 5, (1 << 31) * 64, None) == B.Z1_EINVAL    # 2^31 one-wave groups
 
 
 @pytest.mark.parametrize("over,n_steps", [

@@ -191,6 +191,16 @@ def test_traffic_probes_run():
             assert float(out[n * 4:].abs().sum()) == 0.0
     with pytest.raises(B.Z1Error):
         B.z1_probe("adamw_traffic", [bufs[0]], n)
+    # both AdamW-mix shapes add a to p, m and v over exactly n vectors
+    for kind in ("adamw_traffic", "adamw_traffic_wave"):
+        a = torch.ones(n * 4 + 8, device="cuda")
+        pmv = [torch.full((n * 4 + 8,), 2.0, device="cuda") for _ in range(3)]
+        wh = torch.zeros(n * 4 + 8, dtype=torch.bfloat16, device="cuda")
+        B.z1_probe(kind, [a] + pmv + [wh], n)
+        torch.cuda.synchronize()
+        for t in pmv:
+            assert bool((t[:n * 4] == 3.0).all()) and bool((t[n * 4:] == 2.0).all())
+        assert float(wh[n * 4:].float().abs().sum()) == 0.0
 
 
 def test_plan_probe_covers_exactly_the_slices():
