@@ -221,11 +221,12 @@ typedef enum z1_layout {
 
 /* How the AdamW step walks the shard (z1_bind.walk); the arithmetic and the
  * bits stored are the same either way.  AdamW runs one-wave workgroups of 256
- * elements (one 4-element vector per lane), chunk_elems / 256 of them per
- * piece, at most 16 resident per compute unit.
- *   Z1_WALK_CHUNKS       the workgroups of each entry of the chunk table
- *                        (the accumulation and norm kernels always walk it).
- *   Z1_WALK_ARENA_TILES  packed layout only: 16 workgroups per 4096-element
+ * elements (one 4-element vector per lane), at most 14 (arena tiles) or 20
+ * (chunk table) resident per compute unit.
+ *   Z1_WALK_CHUNKS       chunk_elems / 256 workgroups per entry of the chunk
+ *                        table (the accumulation and norm kernels always
+ *                        walk it).
+ *   Z1_WALK_ARENA_TILES  packed layout only: one workgroup per 256-element
  *                        tile of the arena, every stream addressed by arena
  *                        position, so a tile's loads depend on nothing
  *                        fetched first.  A tile inside one slice takes its
@@ -237,7 +238,7 @@ typedef enum z1_layout {
  *                        its tiles crossing a slice boundary (the loads of
  *                        such a tile are issued before its tag is known and
  *                        then discarded), otherwise the chunk table.
- * The arena walk runs 16 workgroups per tile, so AUTO keeps the chunk table
+ * The arena walk runs one workgroup per tile, so AUTO keeps the chunk table
  * when max_blocks caps the grid.  Z1_WALK_ARENA_TILES with the full layout or
  * with max_blocks > 0, or any other value, is Z1_EINVAL at plan creation. */
 typedef enum z1_walk {
@@ -254,9 +255,9 @@ typedef struct z1_plan_info {
     int64_t arena_elems;    /* arena length required                      */
     int64_t chunk_elems;    /* work unit in elements                      */
     int64_t n_chunks;       /* entries of the device chunk table          */
-    int64_t adamw_tiles;    /* arena tiles the AdamW step walks
-                               (Z1_WALK_ARENA_TILES), 0 when it walks the
-                               chunk table                                */
+    int64_t adamw_tiles;    /* 256-element arena tiles the AdamW step
+                               walks (Z1_WALK_ARENA_TILES), 0 when it
+                               walks the chunk table                      */
     int64_t boundary_tiles; /* of those, tiles that cross a slice boundary
                                or the arena's end                         */
 } z1_plan_info;

@@ -285,7 +285,8 @@ z1::LaunchGeom geom(const z1_plan *p)
 }
 
 // AdamW's arena walk of a packed plan: tile j covers arena elements
-// [j * T, (j + 1) * T) with T = kTileElems.  tags[j] is the tensor whose
+// [j * T, (j + 1) * T) with T = kAdamBlockElems (one AdamW workgroup's
+// block).  tags[j] is the tensor whose
 // slice holds the whole tile, -1 for a tile that crosses a slice boundary or
 // the arena's end (and for a tile no slice touches); the parts of slices in
 // such tiles become segments in the chunk table's format (src, dst, tensor,
@@ -294,7 +295,7 @@ void arena_walk(int32_t n, const int64_t *start, const int64_t *len, const int64
                 int64_t arena_elems, std::vector<int32_t> &tags, std::vector<Chunk> &segs,
                 int64_t &n_full, int64_t &n_boundary)
 {
-    const int64_t T = z1::kTileElems;
+    const int64_t T = z1::kAdamBlockElems;
     const int64_t n_tiles = (arena_elems + T - 1) / T;
     n_full = arena_elems / T;
     tags.assign((size_t)n_tiles, -1);
@@ -650,7 +651,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
         arena_walk(n, p->start.data(), p->len.data(), p->arena_off.data(), p->arena_elems, tags,
                    segs, n_full, n_boundary);
         const int64_t n_tiles = (int64_t)tags.size();
-        const bool fits = (n_tiles + (int64_t)segs.size()) * z1::kAdamTileBlocks <= INT32_MAX;
+        const bool fits = n_tiles + (int64_t)segs.size() <= INT32_MAX;
         if (b->walk == Z1_WALK_ARENA_TILES && !fits)
             return Z1_EINVAL;
         if (fits && (b->walk == Z1_WALK_ARENA_TILES || n_boundary * 100 <= n_tiles)) {
@@ -673,7 +674,8 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if (hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
                               p->device) != hipSuccess || lds_per_cu < 0)
         return Z1_EHIP;
-    p->adam_lds = (uint32_t)(lds_per_cu / z1::kAdamPerCU);
+    p->adam_lds = (uint32_t)(lds_per_cu / (p->n_tiles > 0 ? z1::kAdamPerCUTiles
+                                                           : z1::kAdamPerCUChunks));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||

@@ -21,14 +21,17 @@ constexpr int64_t kMaxChunk = 1 << 20;
 // issues it in table order.
 constexpr int kInterleave = 8;
 // A whole tile: 4 vectors of 4 elements per lane of a kBlock workgroup (the
-// default piece, AdamW's arena tile, the flat norm's unit).
+// default piece, the flat norm's unit).
 constexpr int64_t kTileElems = 4 * kBlock * kVec;
 // AdamW runs one-wave workgroups of one vector per lane: a block of
-// kWave * kVec elements, kAdamTileBlocks of them per tile, at most kAdamPerCU
-// workgroups resident per compute unit (held there by an LDS reservation).
+// kWave * kVec elements (also the arena walk's tile).  Each workgroup
+// reserves 1/N of a compute unit's LDS, so at most N are resident per compute
+// unit: N = kAdamPerCUTiles on the arena walk, whose loads wait for nothing,
+// and kAdamPerCUChunks on the chunk walk, whose loads wait for the piece's
+// descriptor (measured on the 7B shard: 14 and 20 are the best of 10-24).
 constexpr int kAdamBlockElems = kWave * kVec;
-constexpr int kAdamTileBlocks = (int)(kTileElems / kAdamBlockElems);
-constexpr int kAdamPerCU = 16;
+constexpr int kAdamPerCUTiles = 14;
+constexpr int kAdamPerCUChunks = 20;
 constexpr int kMaxSlots = 16;    // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
@@ -73,10 +76,11 @@ struct alignas(16) Scale {
 };
 
 // The arena walk of a packed plan: tile j covers arena elements
-// [j * kTileElems, (j + 1) * kTileElems).  tags[j] >= 0 is the tensor whose
-// slice holds the whole tile; -1 marks a tile that crosses a slice boundary
-// or the arena's end, whose slice segments (pieces in the chunk table's
-// format) are listed in segs, each run by a workgroup of its own.
+// [j * kAdamBlockElems, (j + 1) * kAdamBlockElems).  tags[j] >= 0 is the
+// tensor whose slice holds the whole tile; -1 marks a tile that crosses a
+// slice boundary or the arena's end, whose slice segments (pieces in the
+// chunk table's format) are listed in segs, each run by a workgroup of its
+// own.
 struct ArenaWalk {
     const int32_t *tags = nullptr;   // device [n_tiles]
     const Chunk *segs = nullptr;     // device [n_segs]

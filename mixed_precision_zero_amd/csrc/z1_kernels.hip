@@ -700,15 +700,16 @@ __device__ __forceinline__ bool step_consts(const AdamConsts &k_arg,
 }
 
 // AdamW runs on one-wave workgroups with one vector (4 elements) per lane: a
-// block is kWave consecutive vectors, and a 4096-element piece or arena tile
-// is kAdamTileBlocks blocks on as many workgroups.  Each launch reserves
-// dynamic LDS (which no lane touches) so that at most kAdamPerCU of its
-// workgroups share a compute unit.  This mix is half writes: with the chip
-// full of loads the memory controller's write credits run short, and a lower,
-// steady number of waves in flight streams it faster.  Measured on the 7B
-// shard's buffers with the update in place: 256-lane workgroups with 4
-// vectors per lane 5.5-6.1 TB/s, one-wave workgroups with 1 vector per lane
-// 6.1-6.6 TB/s at 14-16 per compute unit (6 per CU: 4.3; no cap: 6.1-6.4).
+// block is kWave consecutive vectors; a 4096-element piece is 16 blocks on as
+// many workgroups, and an arena tile is one block.  Each launch reserves
+// dynamic LDS (which no lane touches) so that only a few of its workgroups
+// share a compute unit (kAdamPerCUTiles on the arena walk, kAdamPerCUChunks
+// on the chunk walk).  This mix is half writes: with the chip full of loads
+// the memory controller's write credits run short, and a lower, steady number
+// of waves in flight streams it faster.  Measured on the 7B shard's buffers
+// with the update in place: 256-lane workgroups with 4 vectors per lane
+// 5.5-6.1 TB/s, one-wave workgroups with 1 vector per lane 6.1-6.6 TB/s at
+// 14-16 per compute unit (6 per CU: 4.3; no cap: 6.1-6.4).
 
 // Lane t's vector of the four fp32 streams of a block, at byte offset o from
 // the block's bases, loads issued back to back.
@@ -872,13 +873,12 @@ __global__ __launch_bounds__(kWave) void k_adamw(
     }
 }
 
-// AdamW over the arena of a packed plan (ArenaWalk): workgroup b takes block
-// b mod kAdamTileBlocks of tile b / kAdamTileBlocks; past the tiles, the
-// workgroups take the blocks of the boundary segments in turn.  Every stream
-// of a packed plan is addressed by arena position, so a block of a tile that
-// ends inside the arena is loaded first, at addresses that depend on nothing
-// fetched; the tile's tag, read after the loads are issued, names the tensor
-// whose slice holds it.  A tile that crosses a slice boundary (or the
+// AdamW over the arena of a packed plan (ArenaWalk): workgroup b takes tile b
+// (one block); past the tiles, workgroup n_tiles + i takes the i-th boundary
+// segment.  Every stream of a packed plan is addressed by arena position, so
+// a tile that ends inside the arena is loaded first, at addresses that depend
+// on nothing fetched; its tag, read after the loads are issued, names the
+// tensor whose slice holds it.  A tile that crosses a slice boundary (or the
 // arena's end) stores nothing, and neither does any tile when the per-step
 // table is exhausted; those leave through discard_lane, so the update and
 // stores of a live tile stay one unconditional sequence whose waits count its
@@ -895,14 +895,12 @@ __global__ __launch_bounds__(kWave) void k_adamw_tiles(
 {
     const int64_t row = TABLE ? state[0] : 0;
     const int64_t b = blockIdx.x;
-    const int64_t j = b / kAdamTileBlocks;
-    if (j >= n_tiles) {
-        adamw_piece<MATH, TABLE>(segs[j - n_tiles], (int)(b % kAdamTileBlocks), kAdamTileBlocks,
-                                 wtab, scales, acc, master, exp_avg, exp_avg_sq, k_arg, S, table,
-                                 row, n_rows);
+    if (b >= n_tiles) {
+        adamw_piece<MATH, TABLE>(segs[b - n_tiles], 0, 1, wtab, scales, acc, master, exp_avg,
+                                 exp_avg_sq, k_arg, S, table, row, n_rows);
         return;
     }
-    if (j >= n_full)
+    if (b >= n_full)
         return;
     const uint32_t o = (uint32_t)threadIdx.x * 16u;
     const int64_t q0 = b * kWave;
@@ -912,7 +910,7 @@ __global__ __launch_bounds__(kWave) void k_adamw_tiles(
     char *vb = reinterpret_cast<char *>(reinterpret_cast<f32x4 *>(exp_avg_sq) + q0);
     const LaneVec x = load_lane(ab, pb, mb, vb, o);
     __builtin_amdgcn_sched_barrier(0);
-    const int32_t tag = tags[j];
+    const int32_t tag = tags[b];
     AdamConsts k;
     if (!step_consts<TABLE>(k_arg, table, row, n_rows, k) || tag < 0) {
         discard_lane(x);
@@ -1111,8 +1109,7 @@ void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, con
     const size_t lds = geo.adam_lds;
     if (geo.arena.n_tiles > 0) {
         const ArenaWalk &aw = geo.arena;
-        const int64_t grid = (aw.n_tiles + aw.n_segs) * kAdamTileBlocks;
-        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)grid), block, lds, s>>>(
+        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)(aw.n_tiles + aw.n_segs)), block, lds, s>>>(
             aw.tags, aw.segs, aw.n_tiles, aw.n_full, aw.wbase, weight_tab, scales, acc, master, m,
             v, k, S, table, n_rows, state);
         return;
