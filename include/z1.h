@@ -614,8 +614,8 @@ z1_status z1_probe_copy(const void *src, void *dst, int64_t n_bytes, z1_stream s
  *                           workgroups of one vector per lane, at most 12 of
  *                           them resident per compute unit: the shape at
  *                           which this mix streams fastest without arithmetic
- *   Z1_PROBE_SLOTS_TRAFFIC_ONE   as Z1_PROBE_SLOTS_TRAFFIC, one vector per lane
- *                           (256 vectors per workgroup)
+ *   Z1_PROBE_SLOTS_TRAFFIC_ONE   as Z1_PROBE_SLOTS_TRAFFIC, in one-wave (64-lane)
+ *                           workgroups of one vector per lane
  * The default shape is the accumulation kernels': 256-lane workgroups with 4
  * vectors per lane.  The contents written are meaningless.  Z1_EINVAL also
  * when n_vec needs more than 2^31 - 1 workgroups of 64 vectors.  Errors:

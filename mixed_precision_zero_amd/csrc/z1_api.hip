@@ -23,7 +23,8 @@ struct z1_plan {
     int32_t n = 0, K = 0, dp = 0, rank = 0;
     int64_t L = 0, arena_elems = 0, chunk_elems = 0, n_chunks = 0;
     int grid = 0;
-    int32_t adam_sub = 1;   // AdamW workgroups per piece
+    int32_t sub = 1;        // one-wave workgroups per piece (AdamW, wide slot passes)
+    int64_t n_partials = 0; // norm partials the last accumulation or norm pass left
     int64_t adam_grid = 0;  // AdamW's chunk-walk grid
     uint32_t adam_lds = 0;  // LDS reserved per AdamW workgroup
     std::vector<int64_t> start, len, arena_off;
@@ -60,6 +61,7 @@ struct z1_pack {
     int device = -1;
     int32_t n = 0, K = 0, dp = 0;
     int64_t seg = 0, n_chunks = 0;
+    int32_t sub = 1;  // one-wave workgroups per piece of a wide slot pass
     bool divide = false;
     float *send = nullptr;
     Chunk *d_chunks = nullptr;
@@ -270,7 +272,7 @@ z1_status device_alloc(T **out, size_t count)
 z1::LaunchGeom geom(const z1_plan *p)
 {
     z1::LaunchGeom g{p->d_chunks, p->n_chunks, p->grid};
-    g.adam_sub = p->adam_sub;
+    g.sub = p->sub;
     g.adam_grid = p->adam_grid;
     g.adam_lds = p->adam_lds;
     if (p->n_tiles > 0) {
@@ -633,8 +635,8 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     p->grid = (int)(grid > 0 ? grid : 1);
     // AdamW: chunk / kAdamBlockElems one-wave workgroups per piece; a capped
     // grid keeps the lanes of max_blocks 256-lane workgroups
-    p->adam_sub = (int32_t)(chunk / z1::kAdamBlockElems);
-    int64_t adam_grid = p->n_chunks * p->adam_sub;
+    p->sub = (int32_t)(chunk / z1::kAdamBlockElems);
+    int64_t adam_grid = p->n_chunks * p->sub;
     if (b->max_blocks > 0 && adam_grid > (int64_t)b->max_blocks * (z1::kBlock / z1::kWave))
         adam_grid = (int64_t)b->max_blocks * (z1::kBlock / z1::kWave);
     if (adam_grid > INT32_MAX)
@@ -680,7 +682,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||
         (st = device_alloc(&p->d_weights, wptr.size())) != Z1_OK ||
-        (st = device_alloc(&p->d_partials, (size_t)p->n_chunks)) != Z1_OK ||
+        (st = device_alloc(&p->d_partials, (size_t)(p->n_chunks * p->sub))) != Z1_OK ||
         (st = device_alloc(&p->d_stage, (size_t)z1::kFinStages)) != Z1_OK ||
         (st = device_alloc(&p->d_scales, scales.size())) != Z1_OK ||
         (st = device_alloc(&p->d_counter, 1)) != Z1_OK ||
@@ -778,6 +780,8 @@ z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
         p->norm_done = false;
         return Z1_EHIP;
     }
+    if (last)
+        p->n_partials = p->n_chunks;
     p->next_k = k + 1;
     p->acc_complete = last;
     p->norm_done = false;
@@ -810,6 +814,8 @@ z1_status z1_accum_grads_range(z1_plan *p, int32_t k_begin, int32_t k_end, z1_st
             p->norm_done = false;
             return Z1_EHIP;
         }
+        if (last)
+            p->n_partials = g == 1 ? p->n_chunks : z1::pass_partials(geom(p), g);
         k += g;
     }
     p->next_k = k_end;
@@ -828,7 +834,7 @@ z1_status z1_grad_norm_sq(z1_plan *p, double *d_S, z1_stream stream)
         return Z1_EALIGN;
     if (!p->acc_complete)
         return Z1_ESTATE;
-    if (z1::launch_norm_fin(p->d_partials, p->n_chunks, p->d_stage, p->d_counter, d_S,
+    if (z1::launch_norm_fin(p->d_partials, p->n_partials, p->d_stage, p->d_counter, d_S,
                             reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return Z1_EHIP;
     p->norm_done = true;
@@ -845,7 +851,7 @@ z1_status z1_grad_norm_sq_pair(z1_plan *p, double *d_pair, z1_stream stream)
         return Z1_EALIGN;
     if (!p->acc_complete)
         return Z1_ESTATE;
-    if (z1::launch_norm_fin(p->d_partials, p->n_chunks, p->d_stage, p->d_counter, nullptr,
+    if (z1::launch_norm_fin(p->d_partials, p->n_partials, p->d_stage, p->d_counter, nullptr,
                             reinterpret_cast<hipStream_t>(stream),
                             reinterpret_cast<DD *>(d_pair)) != hipSuccess)
         return Z1_EHIP;
@@ -915,6 +921,7 @@ z1_status z1_grad_norm_sq_acc(z1_plan *p, double *d_S, z1_stream stream)
         p->norm_done = false;
         return Z1_EHIP;
     }
+    p->n_partials = p->n_chunks;
     p->next_k = 0;
     p->acc_complete = true;
     p->norm_done = true;
@@ -981,6 +988,7 @@ static z1_status pack_create_body(z1_pack **out, const z1_pack_bind *b, z1_strea
     p->K = K;
     p->dp = D;
     p->seg = seg;
+    p->sub = (int32_t)(chunk / z1::kAdamBlockElems);
     p->divide = b->divide != 0;
     p->send = b->send;
     std::vector<Chunk> chunks;
@@ -1050,7 +1058,8 @@ z1_status z1_pack_accum(z1_pack *p, int32_t k, z1_stream stream)
     if (k != 0 && k != p->next_k)
         return Z1_ESTATE;
     const bool last = k == p->K - 1;
-    const z1::LaunchGeom g{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    z1::LaunchGeom g{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    g.sub = p->sub;
     if (z1::launch_pack(g, p->d_grads + (size_t)k * p->n, p->send, k == 0, last && p->divide,
                         (float)p->dp, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
         p->next_k = 0;
@@ -1068,7 +1077,8 @@ z1_status z1_pack_accum_range(z1_pack *p, int32_t k_begin, int32_t k_end, z1_str
         return Z1_EINVAL;
     if (k_begin != 0 && k_begin != p->next_k)
         return Z1_ESTATE;
-    const z1::LaunchGeom geo{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    z1::LaunchGeom geo{p->d_chunks, p->n_chunks, (int)(p->n_chunks > 0 ? p->n_chunks : 1)};
+    geo.sub = p->sub;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int32_t k = k_begin; k < k_end;) {
         const int32_t left = k_end - k;

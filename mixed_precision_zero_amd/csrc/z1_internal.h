@@ -95,10 +95,30 @@ struct LaunchGeom {
     int64_t n_chunks;
     int grid;             // workgroups for the chunk kernels
     ArenaWalk arena{};    // AdamW's arena walk, when n_tiles > 0
-    int32_t adam_sub = 1;    // AdamW workgroups per piece (chunk_elems / kAdamBlockElems)
-    int64_t adam_grid = 0;   // AdamW's chunk-walk grid (< n_chunks * adam_sub: it loops)
+    int32_t sub = 1;         // one-wave workgroups per piece (chunk_elems / kAdamBlockElems)
+    int64_t adam_grid = 0;   // AdamW's chunk-walk grid (< n_chunks * sub: it loops)
     uint32_t adam_lds = 0;   // LDS bytes each AdamW workgroup reserves (the residency cap)
 };
+
+// Slot passes of at least kSlotsOneWave slots (with an uncapped grid) run
+// one-wave workgroups of one vector per lane, sub of them per piece, and a
+// last pass of them leaves one norm partial per workgroup; every other last
+// pass leaves one per piece.  Measured on packed slots against 256-lane
+// workgroups: 8 slots +10%, 16 slots +8%; 4 slots -7% (too few loads per
+// lane to cover each workgroup's descriptor and pointer lookups).
+constexpr int kSlotsOneWave = 8;
+
+inline bool slots_one_wave(const LaunchGeom &geo, int n_slots)
+{
+    return n_slots >= kSlotsOneWave && geo.grid >= geo.n_chunks &&
+           geo.n_chunks * geo.sub <= INT32_MAX;
+}
+
+// norm partials a last accumulation pass of n_slots slots leaves
+inline int64_t pass_partials(const LaunchGeom &geo, int n_slots)
+{
+    return slots_one_wave(geo, n_slots) ? geo.n_chunks * geo.sub : geo.n_chunks;
+}
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,
                         DD *partials, bool first, bool last, hipStream_t s);
@@ -107,7 +127,7 @@ hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, f
                        bool first, bool divide, float dp, hipStream_t s);
 // slots 0..n_slots-1 of grad_tab (slot j's pointers at grad_tab + j * slot_stride)
 // in one pass, 2 <= n_slots <= kMaxSlots; first overwrites, last writes the
-// norm partials, divide divides the final sum by dp
+// norm partials (pass_partials of them), divide divides the final sum by dp
 hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad_tab,
                               int32_t slot_stride, int n_slots, float *acc, DD *partials,
                               bool first, bool last, bool divide, float dp, hipStream_t s);

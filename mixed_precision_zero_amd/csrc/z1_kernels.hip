@@ -450,6 +450,85 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
     }
 }
 
+// The same pass on one-wave workgroups of one vector per lane, for wide
+// passes (slots_one_wave): workgroup w takes block b = issue_order(w, n_chunks
+// * nsub) -- piece b / nsub, its vectors (b mod nsub) * kWave + t, + nsub *
+// kWave, ... -- so each XCD walks one contiguous region of blocks.  A lane
+// whose vector is partial (a slice's head or tail) adds its elements one by
+// one.  LAST writes the block's double-double partial to partials[b] (zero for
+// a block with no elements), so the finalise sums them in table order.
+template <bool FIRST, bool LAST, bool DIV, int G>
+__global__ __launch_bounds__(kWave) void k_accum_slots_wave(
+    const Chunk *__restrict__ chunks, int64_t n_chunks, int32_t nsub,
+    const uint16_t *const *__restrict__ gtab, int32_t slot_stride, float *__restrict__ acc,
+    DD *__restrict__ partials, float dp)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t b = issue_order(blockIdx.x, n_chunks * nsub);
+    const int64_t ci = b / nsub;
+    const int sub = (int)(b - ci * nsub);
+    const Chunk ch = chunks[ci];
+    const Span sp = span_of(ch);
+    const int nvec = (sp.end + kVec - 1) / kVec;
+    const gmem<const uint16_t> *g[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        g[j] = to_global(gtab[(int64_t)j * slot_stride + ch.tensor]) + (ch.src - sp.lead);
+    float *a = acc + (ch.dst - sp.lead);
+    f32x4 *av = reinterpret_cast<f32x4 *>(a);
+    double hi = 0.0, lo = 0.0;
+    for (int q0 = sub * kWave; q0 < nvec; q0 += nsub * kWave) {
+        const int q = q0 + t;
+        if (q >= sp.qb && q < sp.qe) {
+            u32x2 gr[G];
+            f32x4 ar = {};
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                gr[j] = ld_stream(reinterpret_cast<const gmem<const u32x2> *>(g[j]) + q);
+            if (!FIRST)
+                ar = ld_stream(av + q);
+            f32x4 sv = accum_vec<FIRST, false>(gr[0], ar);
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                sv = accum_vec<false, false>(gr[j], sv);
+            sv = divide_vec<DIV>(sv, dp);
+            st_stream(av + q, sv);
+            if (LAST) {
+                dd_add_sq(hi, lo, sv.x);
+                dd_add_sq(hi, lo, sv.y);
+                dd_add_sq(hi, lo, sv.z);
+                dd_add_sq(hi, lo, sv.w);
+            }
+            continue;
+        }
+        const int e0 = q * kVec > sp.lead ? q * kVec : sp.lead;
+        const int e1 = q * kVec + kVec < sp.end ? q * kVec + kVec : sp.end;
+        for (int e = e0; e < e1; ++e) {
+            float sv = __uint_as_float((uint32_t)g[0][e] << 16);
+            if (!FIRST)
+                sv = a[e] + sv;
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                sv = sv + __uint_as_float((uint32_t)g[j][e] << 16);
+            if (DIV)
+                sv = sv / dp;
+            a[e] = sv;
+            if (LAST)
+                dd_add_sq(hi, lo, sv);
+        }
+    }
+    if (LAST) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double ohi = shfl_xor_d(hi, off);
+            const double olo = shfl_xor_d(lo, off);
+            dd_add(hi, lo, ohi, olo);
+        }
+        if (t == 0)
+            partials[b] = DD{hi, lo};
+    }
+}
+
 template <int U>
 __global__ __launch_bounds__(kBlock) void k_norm_acc(const Chunk *__restrict__ chunks,
                                                      int64_t n_chunks,
@@ -980,6 +1059,31 @@ void launch_slots_g(const LaunchGeom &geo, const uint16_t *const *grad_tab, int3
                     float *acc, DD *partials, bool first, bool last, bool divide, float dp,
                     hipStream_t s)
 {
+    if constexpr (G >= kSlotsOneWave) {
+        if (slots_one_wave(geo, G)) {
+            const dim3 g1((unsigned)(geo.n_chunks * geo.sub)), b1(kWave);
+            const int32_t ns = geo.sub;
+            if (first && last)
+                k_accum_slots_wave<true, true, false, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            else if (last)
+                k_accum_slots_wave<false, true, false, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            else if (first && divide)
+                k_accum_slots_wave<true, false, true, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            else if (divide)
+                k_accum_slots_wave<false, false, true, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            else if (first)
+                k_accum_slots_wave<true, false, false, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            else
+                k_accum_slots_wave<false, false, false, G><<<g1, b1, 0, s>>>(
+                    geo.chunks, geo.n_chunks, ns, grad_tab, stride, acc, partials, dp);
+            return;
+        }
+    }
     const dim3 grid(geo.grid), block(kBlock);
     constexpr int U = G <= 6 ? Z1_UNROLL_ACC : Z1_UNROLL_SLOTS_WIDE;
     // the norm (last) and the division (divide) are never asked for together
@@ -1114,14 +1218,14 @@ void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, con
             v, k, S, table, n_rows, state);
         return;
     }
-    const int64_t n_work = geo.n_chunks * geo.adam_sub;
+    const int64_t n_work = geo.n_chunks * geo.sub;
     if (geo.adam_grid < n_work)
         k_adamw<MATH, TABLE, false><<<dim3((unsigned)geo.adam_grid), block, lds, s>>>(
-            geo.chunks, n_work, geo.adam_sub, weight_tab, scales, acc, master, m, v, k, S, table,
+            geo.chunks, n_work, geo.sub, weight_tab, scales, acc, master, m, v, k, S, table,
             n_rows, state);
     else
         k_adamw<MATH, TABLE, true><<<dim3((unsigned)n_work), block, lds, s>>>(
-            geo.chunks, n_work, geo.adam_sub, weight_tab, scales, acc, master, m, v, k, S, table,
+            geo.chunks, n_work, geo.sub, weight_tab, scales, acc, master, m, v, k, S, table,
             n_rows, state);
 }
 

@@ -144,25 +144,26 @@ __global__ __launch_bounds__(kBlock) void k_probe_accum(const u32x2 *__restrict_
 
 // The first resident-slot pass's traffic: read G half-width streams, write
 // one fp32 stream (2G + 4 bytes per element); the G pointers come by value.
-// R rounds of U vectors per lane over an R * U * 256-vector tile per
-// workgroup: as in the accumulation kernel (U = 4 up to 6 slots, 2 above, over
-// a 1024-vector tile), or one vector per lane and one round.
+// R rounds of U vectors per lane over an R * U * NT-vector tile per
+// workgroup of NT lanes: as in the 256-lane accumulation kernel (U = 4 up to
+// 6 slots, 2 above, over a 1024-vector tile), or one-wave workgroups of one
+// vector per lane and one round (the shape of the wide passes).
 struct SlotPtrs {
     const u32x2 *p[kMaxSlots];
 };
 
-template <int G, int U, int R>
-__global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__restrict__ acc,
-                                                             int64_t n)
+template <int G, int U, int R, int NT>
+__global__ __launch_bounds__(NT) void k_probe_slots(SlotPtrs sp, f32x4 *__restrict__ acc,
+                                                    int64_t n)
 {
-    const int64_t tile = (int64_t)blockIdx.x * (R * U * kBlock) + threadIdx.x;
+    const int64_t tile = (int64_t)blockIdx.x * (R * U * NT) + threadIdx.x;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int64_t base = tile + (int64_t)r * U * kBlock;
+        const int64_t base = tile + (int64_t)r * U * NT;
         u32x2 gr[G][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * kBlock;
+            const int64_t i = base + u * NT;
             if (i < n) {
 #pragma unroll
                 for (int j = 0; j < G; ++j)
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void k_probe_slots(SlotPtrs sp, f32x4 *__re
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * kBlock;
+            const int64_t i = base + u * NT;
             if (i < n) {
                 f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -193,12 +194,12 @@ void launch_slots_probe(void *const *bufs, int64_t n_vec, bool one, hipStream_t 
         sp.p[j] = static_cast<const u32x2 *>(bufs[j]);
     f32x4 *acc = static_cast<f32x4 *>(bufs[G]);
     if (one) {
-        k_probe_slots<G, 1, 1><<<dim3((unsigned)((n_vec + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                                 s>>>(sp, acc, n_vec);
+        k_probe_slots<G, 1, 1, kWave><<<dim3((unsigned)((n_vec + kWave - 1) / kWave)),
+                                        dim3(kWave), 0, s>>>(sp, acc, n_vec);
     } else {
         constexpr int U = G <= 6 ? 4 : 2;
-        k_probe_slots<G, U, 4 / U><<<dim3((unsigned)((n_vec + kTileVec - 1) / kTileVec)),
-                                     dim3(kBlock), 0, s>>>(sp, acc, n_vec);
+        k_probe_slots<G, U, 4 / U, kBlock><<<dim3((unsigned)((n_vec + kTileVec - 1) / kTileVec)),
+                                             dim3(kBlock), 0, s>>>(sp, acc, n_vec);
     }
 }
 
