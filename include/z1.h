@@ -174,13 +174,17 @@ typedef struct z1_bind {
      * [n_micro * n_tensors] of device pointers; grads[k*n_tensors + i]
      * points to element 0 of the FULL gradient of tensor i for micro-batch
      * k, of which only this rank's slice is read.  Z1_LAYOUT_PACKED: host
-     * array [n_micro], grads[k] one packed bf16 shard in arena order (for
-     * example the output of an equal-count reduce-scatter).               */
+     * array [n_micro], grads[k] one packed bf16 shard of arena_elems values
+     * (the value z1_shard_plan returns) in arena order (for example the
+     * output of an equal-count reduce-scatter); its padding may be read,
+     * as the fp32 arenas' may.                                             */
     const void *const *grads;
     /* fp32 arenas, device, arena_elems floats each (see z1_shard_plan).
      * master holds the fp32 master weights, exp_avg / exp_avg_sq the Adam
      * moments (zero before the first step), acc receives the accumulated
-     * gradient.  Padding elements are never read or written.             */
+     * gradient.  Padding elements are never written; the arena walks
+     * (packed plans) may read them, in a tile that holds a slice boundary,
+     * and discard what they read.                                          */
     float *master;
     float *exp_avg;
     float *exp_avg_sq;

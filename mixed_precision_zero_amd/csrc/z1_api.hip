@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <memory>
 #include <mutex>
 #include <new>
@@ -28,6 +29,7 @@ struct z1_plan {
     int64_t adam_grid = 0;  // AdamW's chunk-walk grid
     uint32_t adam_lds = 0;  // LDS reserved per AdamW workgroup
     std::vector<int64_t> start, len, arena_off;
+    std::vector<const uint16_t *> gbase;  // packed plans: the K gradient shards, arena-indexed
     // device memory owned by the plan
     Chunk *d_chunks = nullptr;
     const uint16_t **d_grads = nullptr;  // [K][n]
@@ -583,6 +585,7 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
                 return Z1_EINVAL;
             if (!aligned(b->grads[k], 16))
                 return Z1_EALIGN;
+            p->gbase.push_back(static_cast<const uint16_t *>(b->grads[k]));
         }
         auto at = [&](const void *base, int32_t i) {
             return reinterpret_cast<uintptr_t>(base) +
@@ -682,7 +685,8 @@ static z1_status plan_create_body(z1_plan **out, const z1_bind *b, z1_stream str
     if ((st = device_alloc(&p->d_chunks, chunks.size())) != Z1_OK ||
         (st = device_alloc(&p->d_grads, gptr.size())) != Z1_OK ||
         (st = device_alloc(&p->d_weights, wptr.size())) != Z1_OK ||
-        (st = device_alloc(&p->d_partials, (size_t)(p->n_chunks * p->sub))) != Z1_OK ||
+        (st = device_alloc(&p->d_partials, (size_t)std::max(p->n_chunks * p->sub,
+                                                            p->n_tiles + p->n_segs))) != Z1_OK ||
         (st = device_alloc(&p->d_stage, (size_t)z1::kFinStages)) != Z1_OK ||
         (st = device_alloc(&p->d_scales, scales.size())) != Z1_OK ||
         (st = device_alloc(&p->d_counter, 1)) != Z1_OK ||
@@ -762,6 +766,35 @@ z1_status z1_plan_layout(const z1_plan *p, int64_t *start, int64_t *len, int64_t
     return Z1_OK;
 }
 
+namespace {
+
+// One accumulation pass over slots k .. k + g - 1: on the arena walk when the
+// plan has one and the pass is a single or a wide one (slot addresses from
+// the packed shards' bases), else over the chunk table.  A last pass records
+// how many norm partials it leaves.
+hipError_t accum_pass(z1_plan *p, int32_t k, int32_t g, bool first, bool last, hipStream_t s)
+{
+    const z1::LaunchGeom geo = geom(p);
+    const bool on_arena = z1::slots_arena(geo, g) && p->gbase.size() == (size_t)p->K;
+    hipError_t e;
+    if (on_arena) {
+        z1::SlotBases sb{};
+        for (int32_t j = 0; j < g; ++j)
+            sb.g[j] = p->gbase[(size_t)(k + j)];
+        e = z1::launch_accum_arena(geo, sb, g, p->acc, p->d_partials, first, last, s);
+    } else {
+        const uint16_t *const *tab = p->d_grads + (size_t)k * p->n;
+        e = g == 1 ? z1::launch_accum(geo, tab, p->acc, p->d_partials, first, last, s)
+                   : z1::launch_accum_slots(geo, tab, p->n, g, p->acc, p->d_partials, first,
+                                            last, false, 1.0f, s);
+    }
+    if (e == hipSuccess && last)
+        p->n_partials = z1::pass_partials(geo, g, on_arena);
+    return e;
+}
+
+}  // namespace
+
 z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
 {
     if (!p || k < 0 || k >= p->K)
@@ -771,17 +804,13 @@ z1_status z1_accum_grads(z1_plan *p, int32_t k, z1_stream stream)
     if (k != 0 && k != p->next_k)
         return Z1_ESTATE;
     const bool first = k == 0, last = k == p->K - 1;
-    hipError_t e = z1::launch_accum(geom(p), p->d_grads + (size_t)k * p->n, p->acc,
-                                    p->d_partials, first, last,
-                                    reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = accum_pass(p, k, 1, first, last, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         p->next_k = 0;
         p->acc_complete = false;
         p->norm_done = false;
         return Z1_EHIP;
     }
-    if (last)
-        p->n_partials = p->n_chunks;
     p->next_k = k + 1;
     p->acc_complete = last;
     p->norm_done = false;
@@ -803,19 +832,13 @@ z1_status z1_accum_grads_range(z1_plan *p, int32_t k_begin, int32_t k_end, z1_st
         const int32_t passes = (left + z1::kMaxSlots - 1) / z1::kMaxSlots;
         const int32_t g = (left + passes - 1) / passes;
         const bool first = k == 0, last = k + g == p->K;
-        const uint16_t *const *tab = p->d_grads + (size_t)k * p->n;
-        const hipError_t e =
-            g == 1 ? z1::launch_accum(geom(p), tab, p->acc, p->d_partials, first, last, s)
-                   : z1::launch_accum_slots(geom(p), tab, p->n, g, p->acc, p->d_partials, first,
-                                            last, false, 1.0f, s);
+        const hipError_t e = accum_pass(p, k, g, first, last, s);
         if (e != hipSuccess) {
             p->next_k = 0;
             p->acc_complete = false;
             p->norm_done = false;
             return Z1_EHIP;
         }
-        if (last)
-            p->n_partials = g == 1 ? p->n_chunks : z1::pass_partials(geom(p), g);
         k += g;
     }
     p->next_k = k_end;

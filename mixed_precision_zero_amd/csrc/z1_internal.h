@@ -100,25 +100,51 @@ struct LaunchGeom {
     uint32_t adam_lds = 0;   // LDS bytes each AdamW workgroup reserves (the residency cap)
 };
 
-// Slot passes of at least kSlotsOneWave slots (with an uncapped grid) run
-// one-wave workgroups of one vector per lane, sub of them per piece, and a
-// last pass of them leaves one norm partial per workgroup; every other last
-// pass leaves one per piece.  Measured on packed slots against 256-lane
-// workgroups: 8 slots +10%, 16 slots +8%; 4 slots -7% (too few loads per
-// lane to cover each workgroup's descriptor and pointer lookups).
+// Accumulation passes of one slot or of at least kSlotsOneWave slots run
+// one-wave workgroups of one vector per lane: on the arena walk when the
+// plan has one (packed plans; every slot's element at its arena position,
+// one workgroup per tile, one norm partial per tile and per boundary
+// segment), else on the chunk table with sub workgroups per piece (one norm
+// partial per workgroup; uncapped grids only).  Passes of 2 to
+// kSlotsOneWave - 1 slots, and capped grids, keep 256-lane workgroups (one
+// partial per piece).  Measured on packed slots against 256-lane workgroups,
+// alternating: one slot (per call) 5-11% faster on the arena walk and 1-7%
+// on the chunk table; 8 and 16 slots 10% and 8% on the chunk table and
+// 2-6% more on the arena walk; 4 slots 7% slower on the chunk table and the
+// same or 3-5% slower on the arena walk (too few loads per lane to cover
+// each workgroup's lookups or its norm).
 constexpr int kSlotsOneWave = 8;
+
+inline bool slots_wide_or_single(int n_slots)
+{
+    return n_slots == 1 || n_slots >= kSlotsOneWave;
+}
+
+inline bool slots_arena(const LaunchGeom &geo, int n_slots)
+{
+    return geo.arena.n_tiles > 0 && slots_wide_or_single(n_slots);
+}
 
 inline bool slots_one_wave(const LaunchGeom &geo, int n_slots)
 {
-    return n_slots >= kSlotsOneWave && geo.grid >= geo.n_chunks &&
+    return slots_wide_or_single(n_slots) && geo.grid >= geo.n_chunks &&
            geo.n_chunks * geo.sub <= INT32_MAX;
 }
 
-// norm partials a last accumulation pass of n_slots slots leaves
-inline int64_t pass_partials(const LaunchGeom &geo, int n_slots)
+// norm partials a last accumulation pass of n_slots slots leaves (the arena
+// walk when on_arena, else the chunk table)
+inline int64_t pass_partials(const LaunchGeom &geo, int n_slots, bool on_arena)
 {
+    if (on_arena)
+        return geo.arena.n_tiles + geo.arena.n_segs;
     return slots_one_wave(geo, n_slots) ? geo.n_chunks * geo.sub : geo.n_chunks;
 }
+
+// The bases of a pass's slots in a packed plan: slot j's element at arena
+// position x is slots[j][x].
+struct SlotBases {
+    const uint16_t *g[kMaxSlots];
+};
 
 hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, float *acc,
                         DD *partials, bool first, bool last, hipStream_t s);
@@ -131,6 +157,10 @@ hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, f
 hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad_tab,
                               int32_t slot_stride, int n_slots, float *acc, DD *partials,
                               bool first, bool last, bool divide, float dp, hipStream_t s);
+// the same on the arena walk of a packed plan (slots_arena): slot j of the
+// pass at sb.g[j]
+hipError_t launch_accum_arena(const LaunchGeom &geo, const SlotBases &sb, int n_slots,
+                              float *acc, DD *partials, bool first, bool last, hipStream_t s);
 // norm partials of an acc arena filled by the caller
 hipError_t launch_norm_acc(const LaunchGeom &geo, const float *acc, DD *partials, hipStream_t s);
 // S (when S != nullptr) and/or the unrounded pair (when pair != nullptr)

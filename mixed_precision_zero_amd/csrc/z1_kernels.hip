@@ -450,8 +450,8 @@ __global__ __launch_bounds__(kBlock) void k_accum_slots(const Chunk *__restrict_
     }
 }
 
-// The same pass on one-wave workgroups of one vector per lane, for wide
-// passes (slots_one_wave): workgroup w takes block b = issue_order(w, n_chunks
+// The same pass on one-wave workgroups of one vector per lane, for single
+// and wide passes (slots_one_wave): workgroup w takes block b = issue_order(w, n_chunks
 // * nsub) -- piece b / nsub, its vectors (b mod nsub) * kWave + t, + nsub *
 // kWave, ... -- so each XCD walks one contiguous region of blocks.  A lane
 // whose vector is partial (a slice's head or tail) adds its elements one by
@@ -515,6 +515,83 @@ __global__ __launch_bounds__(kWave) void k_accum_slots_wave(
             a[e] = sv;
             if (LAST)
                 dd_add_sq(hi, lo, sv);
+        }
+    }
+    if (LAST) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double ohi = shfl_xor_d(hi, off);
+            const double olo = shfl_xor_d(lo, off);
+            dd_add(hi, lo, ohi, olo);
+        }
+        if (t == 0)
+            partials[b] = DD{hi, lo};
+    }
+}
+
+// The same pass on the arena walk of a packed plan (slots_arena): workgroup
+// b < n_tiles takes 256-element tile b, its lanes one vector each of every
+// slot (and of acc after the first pass) at the tile's arena position, all
+// issued before the tile's tag is read; a tile inside one slice sums and
+// stores, a boundary tile (tag -1) leaves through a branch that consumes the
+// loaded registers.  Workgroup n_tiles + i adds the i-th boundary segment
+// element by element.  Every addition is the same binary32 addition in slot
+// order as in the chunk-table kernels.  LAST writes the workgroup's
+// double-double partial to partials[b] (zero for a boundary tile), the
+// tiles' partials then the segments', in arena order.
+template <bool FIRST, bool LAST, int G>
+__global__ __launch_bounds__(kWave) void k_accum_arena(SlotBases sb,
+                                                       const int32_t *__restrict__ tags,
+                                                       const Chunk *__restrict__ segs,
+                                                       int64_t n_tiles, int64_t n_full,
+                                                       float *__restrict__ acc,
+                                                       DD *__restrict__ partials)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t b = blockIdx.x;
+    double hi = 0.0, lo = 0.0;
+    if (b >= n_tiles) {
+        const Chunk ch = segs[b - n_tiles];
+        for (int e = t; e < ch.count; e += kWave) {
+            const int64_t x = ch.dst + e;
+            float sv = __uint_as_float((uint32_t)to_global(sb.g[0])[x] << 16);
+            if (!FIRST)
+                sv = acc[x] + sv;
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                sv = sv + __uint_as_float((uint32_t)to_global(sb.g[j])[x] << 16);
+            acc[x] = sv;
+            if (LAST)
+                dd_add_sq(hi, lo, sv);
+        }
+    } else if (b < n_full) {
+        const int64_t q = b * kWave + t;
+        f32x4 *av = reinterpret_cast<f32x4 *>(acc) + q;
+        u32x2 gr[G];
+        f32x4 ar = {};
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            gr[j] = ld_stream(reinterpret_cast<const gmem<const u32x2> *>(to_global(sb.g[j])) + q);
+        if (!FIRST)
+            ar = ld_stream(av);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tags[b] >= 0) {
+            f32x4 sv = accum_vec<FIRST, false>(gr[0], ar);
+#pragma unroll
+            for (int j = 1; j < G; ++j)
+                sv = accum_vec<false, false>(gr[j], sv);
+            st_stream(av, sv);
+            if (LAST) {
+                dd_add_sq(hi, lo, sv.x);
+                dd_add_sq(hi, lo, sv.y);
+                dd_add_sq(hi, lo, sv.z);
+                dd_add_sq(hi, lo, sv.w);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                __asm__ volatile("" ::"v"(gr[j]));
+            __asm__ volatile("" ::"v"(ar));
         }
     }
     if (LAST) {
@@ -1037,6 +1114,23 @@ hipError_t launch_accum(const LaunchGeom &geo, const uint16_t *const *grad_tab, 
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
+    if (slots_one_wave(geo, 1)) {
+        const dim3 g1((unsigned)(geo.n_chunks * geo.sub)), b1(kWave);
+        const int32_t ns = geo.sub;
+        if (first && last)
+            k_accum_slots_wave<true, true, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, acc, partials, 1.0f);
+        else if (first)
+            k_accum_slots_wave<true, false, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, acc, partials, 1.0f);
+        else if (last)
+            k_accum_slots_wave<false, true, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, acc, partials, 1.0f);
+        else
+            k_accum_slots_wave<false, false, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, acc, partials, 1.0f);
+        return hipGetLastError();
+    }
     const dim3 grid(geo.grid), block(kBlock);
     constexpr int U = Z1_UNROLL_ACC;
     if (first && last)
@@ -1154,6 +1248,48 @@ hipError_t launch_accum_slots(const LaunchGeom &geo, const uint16_t *const *grad
     case 14: launch_slots_g<14>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     case 15: launch_slots_g<15>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
     case 16: launch_slots_g<16>(geo, grad_tab, slot_stride, acc, partials, first, last, divide, dp, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int G>
+void launch_arena_g(const LaunchGeom &geo, const SlotBases &sb, float *acc, DD *partials,
+                    bool first, bool last, hipStream_t s)
+{
+    const ArenaWalk &aw = geo.arena;
+    const dim3 grid((unsigned)(aw.n_tiles + aw.n_segs)), block(kWave);
+    if (first && last)
+        k_accum_arena<true, true, G><<<grid, block, 0, s>>>(sb, aw.tags, aw.segs, aw.n_tiles,
+                                                             aw.n_full, acc, partials);
+    else if (first)
+        k_accum_arena<true, false, G><<<grid, block, 0, s>>>(sb, aw.tags, aw.segs, aw.n_tiles,
+                                                              aw.n_full, acc, partials);
+    else if (last)
+        k_accum_arena<false, true, G><<<grid, block, 0, s>>>(sb, aw.tags, aw.segs, aw.n_tiles,
+                                                              aw.n_full, acc, partials);
+    else
+        k_accum_arena<false, false, G><<<grid, block, 0, s>>>(sb, aw.tags, aw.segs, aw.n_tiles,
+                                                               aw.n_full, acc, partials);
+}
+
+hipError_t launch_accum_arena(const LaunchGeom &geo, const SlotBases &sb, int n_slots,
+                              float *acc, DD *partials, bool first, bool last, hipStream_t s)
+{
+    if (!slots_arena(geo, n_slots))
+        return hipErrorInvalidValue;
+    static_assert(kMaxSlots == 16 && kSlotsOneWave == 8, "one case per slot count 1, 8..16");
+    switch (n_slots) {
+    case 1: launch_arena_g<1>(geo, sb, acc, partials, first, last, s); break;
+    case 8: launch_arena_g<8>(geo, sb, acc, partials, first, last, s); break;
+    case 9: launch_arena_g<9>(geo, sb, acc, partials, first, last, s); break;
+    case 10: launch_arena_g<10>(geo, sb, acc, partials, first, last, s); break;
+    case 11: launch_arena_g<11>(geo, sb, acc, partials, first, last, s); break;
+    case 12: launch_arena_g<12>(geo, sb, acc, partials, first, last, s); break;
+    case 13: launch_arena_g<13>(geo, sb, acc, partials, first, last, s); break;
+    case 14: launch_arena_g<14>(geo, sb, acc, partials, first, last, s); break;
+    case 15: launch_arena_g<15>(geo, sb, acc, partials, first, last, s); break;
+    case 16: launch_arena_g<16>(geo, sb, acc, partials, first, last, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
