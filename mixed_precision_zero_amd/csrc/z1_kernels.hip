@@ -1206,6 +1206,23 @@ hipError_t launch_pack(const LaunchGeom &geo, const uint16_t *const *grad_tab, f
 {
     if (geo.n_chunks == 0)
         return hipSuccess;
+    if (slots_one_wave(geo, 1)) {
+        const dim3 g1((unsigned)(geo.n_chunks * geo.sub)), b1(kWave);
+        const int32_t ns = geo.sub;
+        if (first && divide)
+            k_accum_slots_wave<true, false, true, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, send, nullptr, dp);
+        else if (first)
+            k_accum_slots_wave<true, false, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, send, nullptr, dp);
+        else if (divide)
+            k_accum_slots_wave<false, false, true, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, send, nullptr, dp);
+        else
+            k_accum_slots_wave<false, false, false, 1><<<g1, b1, 0, s>>>(
+                geo.chunks, geo.n_chunks, ns, grad_tab, 0, send, nullptr, dp);
+        return hipGetLastError();
+    }
     const dim3 grid(geo.grid), block(kBlock);
     constexpr int U = Z1_UNROLL_ACC;
     if (first && divide)
