@@ -549,6 +549,14 @@ __global__ __launch_bounds__(kWave) void k_accum_arena(SlotBases sb,
 {
     const int t = (int)threadIdx.x;
     const int64_t b = blockIdx.x;
+    // A single pass's slot base and the tag table pointer are kernel
+    // arguments; used here, their loads join the first batch with n_tiles
+    // and n_full instead of waiting behind the branch, so one scalar round
+    // trip precedes the first vector load instead of two.  (Wide passes keep
+    // the compiler's placement: one such use per slot pointer makes it wait
+    // after every few of their loads.)
+    if constexpr (G == 1)
+        __asm__ volatile("" ::"s"(sb.g[0]), "s"(tags), "s"(acc));
     double hi = 0.0, lo = 0.0;
     if (b >= n_tiles) {
         const Chunk ch = segs[b - n_tiles];
