@@ -56,18 +56,25 @@ def test_tiny_fifteen_slots_wide_pass():
     _run(w, 2, [(0, 15)], chunk_elems=1024)
 
 
+# the full-size layout on the chunk table, and packed shards with the arena
+# walk forced (single and wide passes then run on the arena kernels; the
+# list's slices leave most 256-element tiles on slice boundaries)
+WALKS = {"chunks": {}, "arena": dict(layout="packed", walk="arena_tiles")}
+
+
+@pytest.mark.parametrize("walk", list(WALKS))
 @pytest.mark.parametrize("K,ranges", [
     (33, [(0, 33)]),                     # three passes of 11 slots
     (64, [(0, 64)]),                     # four passes of 16 slots
     (37, [(0, 3), (3, 20), (20, 37)]),   # three calls: 3; 9 + 8; 9 + 8 slots
 ], ids=["k33", "k64", "k37_three_calls"])
-def test_tiny_many_slots_many_passes(K, ranges):
+def test_tiny_many_slots_many_passes(K, ranges, walk):
     """Many resident micro-batches: a range longer than 16 slots is split into
     as many passes as it needs, of nearly equal size; every split stores the
     bits of one call per micro-batch (the oracle's in-order binary32 sum)."""
     w = dataclasses.replace(W.TINY, name=f"tiny_k{K}", n_micro=K,
                             shapes=((257, 63), (61,), (1030,)))
-    _run(w, 2, ranges, chunk_elems=1024)
+    _run(w, 2, ranges, chunk_elems=1024, **WALKS[walk])
 
 
 def _wide_pass_partitions(K):
@@ -82,7 +89,8 @@ def _wide_pass_partitions(K):
     return steps
 
 
-def test_tiny_wide_passes_every_size_and_position():
+@pytest.mark.parametrize("walk", list(WALKS))
+def test_tiny_wide_passes_every_size_and_position(walk):
     """K = 18 on 1024-element chunks: each of the 9- to 16-slot passes as the
     first, a middle and the last pass of a step, 24 steps in a row, every step
     bit-exact against the oracle."""
@@ -90,7 +98,7 @@ def test_tiny_wide_passes_every_size_and_position():
     K = 18
     w = dataclasses.replace(W.TINY, name="tiny_k18", n_micro=K, shapes=((257, 63), (61,), (1030,)))
     steps = _wide_pass_partitions(K)
-    h = harness.Parity(w, ranges=steps[0], chunk_elems=1024)
+    h = harness.Parity(w, ranges=steps[0], chunk_elems=1024, **WALKS[walk])
     try:
         assert h.plan_matches()
         for ranges in steps:
