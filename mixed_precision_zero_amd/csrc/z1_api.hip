@@ -288,12 +288,12 @@ z1::LaunchGeom geom(const z1_plan *p)
     return g;
 }
 
-// AdamW's arena walk of a packed plan: tile j covers arena elements
-// [j * T, (j + 1) * T) with T = kAdamBlockElems (one AdamW workgroup's
-// block).  tags[j] is the tensor whose
-// slice holds the whole tile, -1 for a tile that crosses a slice boundary or
-// the arena's end (and for a tile no slice touches); the parts of slices in
-// such tiles become segments in the chunk table's format (src, dst, tensor,
+// The arena walk of a packed plan (AdamW's, and the single and wide
+// accumulation passes'): tile j covers arena elements [j * T, (j + 1) * T)
+// with T = kAdamBlockElems (one one-wave workgroup's block).  tags[j] is the
+// tensor whose slice holds the whole tile, -1 for a tile that crosses a slice
+// boundary or the arena's end (and for a tile no slice touches); the parts
+// of slices in such tiles become segments in the chunk table's format (src, dst, tensor,
 // count), in arena order.  Padding between slices is in no segment.
 void arena_walk(int32_t n, const int64_t *start, const int64_t *len, const int64_t *arena_off,
                 int64_t arena_elems, std::vector<int32_t> &tags, std::vector<Chunk> &segs,

@@ -7,9 +7,11 @@
 
 namespace z1 {
 
-// Workgroup of four wave64s; every lane moves 4 elements per vector
-// (16-byte fp32 accesses, 8-byte bf16 accesses), so one workgroup touches
-// 1024 consecutive elements per vector step.
+// Workgroup of four wave64s (the chunk-table kernels of narrow passes and
+// the norm; AdamW and single or wide passes run one-wave workgroups); every
+// lane moves 4 elements per vector (16-byte fp32 accesses, 8-byte bf16
+// accesses), so one such workgroup touches 1024 consecutive elements per
+// vector step.
 constexpr int kBlock = 256;
 constexpr int kWave = 64;       // lanes of one wavefront
 constexpr int kVec = 4;

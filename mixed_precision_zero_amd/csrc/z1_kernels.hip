@@ -2,10 +2,11 @@
 //
 // The step is a streaming, HBM-bound pass over one rank's shard (about 0.5
 // flop per byte), so nothing here uses MFMA.  Each kernel walks a
-// device-resident chunk table: a workgroup takes one piece of one tensor's
-// slice, its lanes move 4 consecutive elements each with one 16-byte fp32
-// access per arena and one 8-byte bf16 access, consecutive lanes on
-// consecutive addresses.  The fp32 arenas are laid out so that an arena
+// device-resident chunk table (a workgroup takes one piece of one tensor's
+// slice, or a 256-element block of it) or, in packed plans, the arena itself
+// in 256-element tiles; its lanes move 4 consecutive elements each with one
+// 16-byte fp32 access per arena and one 8-byte bf16 access, consecutive lanes
+// on consecutive addresses.  The fp32 arenas are laid out so that an arena
 // element and its bf16 element share their position within a vector (the
 // arena offset matches the slice start mod 64 elements), so the pieces cut
 // at multiples of the chunk size inside a tensor start on whole 128-byte
