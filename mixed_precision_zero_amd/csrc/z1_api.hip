@@ -364,7 +364,8 @@ bool hp_ok(const z1_adamw_hp *hp)
 }
 
 // The binary64 constants of one step, derived on the host (bias corrections
-// from libm pow, as the oracle derives them).
+// from libm pow, as the oracle derives them, and their reciprocals, which the
+// kernels divide by exactly).
 AdamConsts consts_of(const z1_adamw_hp *hp)
 {
     AdamConsts k;
@@ -378,6 +379,8 @@ AdamConsts consts_of(const z1_adamw_hp *hp)
     k.weight_decay = hp->weight_decay;
     k.bc1 = 1.0 - pow(hp->beta1, t);
     k.bc2 = 1.0 - pow(hp->beta2, t);
+    k.rbc1 = 1.0 / k.bc1;
+    k.rbc2 = 1.0 / k.bc2;
     k.clip = hp->clip > 0.0 ? hp->clip : 0.0;
     return k;
 }

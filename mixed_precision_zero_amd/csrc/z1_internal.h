@@ -30,10 +30,17 @@ constexpr int64_t kTileElems = 4 * kBlock * kVec;
 // reserves 1/N of a compute unit's LDS, so at most N are resident per compute
 // unit: N = kAdamPerCUTiles on the arena walk, whose loads wait for nothing,
 // and kAdamPerCUChunks on the chunk walk, whose loads wait for the piece's
-// descriptor (measured on the 7B shard: 14 and 20 are the best of 10-24).
+// descriptor (measured on the 7B shard, 10-24: 14 for both; the chunk walk
+// wanted 20 until the bias corrections were divided with their reciprocals).
 constexpr int kAdamBlockElems = kWave * kVec;
-constexpr int kAdamPerCUTiles = 14;
-constexpr int kAdamPerCUChunks = 20;
+#ifndef Z1_ADAM_CAP_TILES
+#define Z1_ADAM_CAP_TILES 14
+#endif
+#ifndef Z1_ADAM_CAP_CHUNKS
+#define Z1_ADAM_CAP_CHUNKS 14
+#endif
+constexpr int kAdamPerCUTiles = Z1_ADAM_CAP_TILES;
+constexpr int kAdamPerCUChunks = Z1_ADAM_CAP_CHUNKS;
 constexpr int kMaxSlots = 16;    // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
 constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
@@ -69,6 +76,7 @@ struct AdamConsts {
     double eps;
     double weight_decay;
     double bc1, bc2;       // 1 - beta1^t, 1 - beta2^t
+    double rbc1, rbc2;     // 1 / bc1, 1 / bc2, each rounded once
     double clip;           // <= 0: no clipping
 };
 

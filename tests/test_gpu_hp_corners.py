@@ -1,6 +1,9 @@
 """GPU parity at hyperparameter corners of the binary64 update: beta = 0,
 lr = 0, a negative lr, wd = 0, eps = 1, beta2 next to 1, a clip so small
-that every clipped square underflows the fp32 store of v, and clipping off.
+that every clipped square underflows the fp32 store of v, a clip and an eps
+so small that m lies below 2^-960 (the bias correction of m then takes the
+IEEE division instead of the reciprocal with exact remainders) while the
+update still moves the weights, and clipping off.
 Each runs three steps on a 300-tensor ragged list (K = 3), bit-exact against
 the oracle: the GPU evaluates the same IEEE operation sequence whatever the
 constants are."""
@@ -24,6 +27,7 @@ CORNERS = {
     "eps_one": dict(eps=1.0),
     "beta2_near_one": dict(beta2=0.999999),
     "clip_tiny": dict(clip=1e-30),
+    "clip_eps_below_2e-960": dict(clip=1e-300, eps=1e-300, lr=1.0),
     "clip_off": dict(clip=0.0),
 }
 
