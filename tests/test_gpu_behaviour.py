@@ -498,6 +498,66 @@ def test_adamw_wide_range_matches_oracle(clip, step):
         st.close()
 
 
+# (beta1, beta2, step): bias-correction divisors 1 - beta^t from 0.5 down to
+# about 1e-6 and up to 1 - 1e-300 (the kernel divides by them through their
+# reciprocals with exact remainders); beta2 = 0 keeps v finite where m is
+# infinite, so an infinite quotient there reaches the weight as an infinity.
+BIAS_DIVISORS = [(0.9, 0.95, 1), (0.9, 0.95, 2), (0.9, 0.95, 3), (0.9, 0.95, 13),
+                 (0.9, 0.95, 1000), (0.9, 0.999, 10), (0.9, 0.999, 65537),
+                 (0.5, 0.999999, 1), (0.5, 0.999999, 3000), (0.3, 0.99, 7),
+                 (0.99, 0.0, 5), (0.0, 0.999, 1_000_000)]
+
+
+def test_adamw_bias_divisors_match_oracle():
+    """m / (1 - beta1^t) and v / (1 - beta2^t) for many divisors: p, m and v
+    over every finite fp32 exponent plus 0.1% infinities in m and v, one
+    step each, the oracle's bits for every element that is not NaN and NaN
+    exactly where the oracle has NaN (clipping off, so the infinities reach
+    the quotients)."""
+    import oracle
+    o = oracle.get()
+    n = 1 << 20
+    st = ShardStep([(n,)], 1, 0, 1, device="cuda")
+    try:
+        for i, (b1, b2, step) in enumerate(BIAS_DIVISORS):
+            rng = np.random.default_rng(500 + i)
+            p = _finite_patterns(rng, n, 32).view(np.float32)
+            m = _finite_patterns(rng, n, 32).view(np.float32)
+            v = _finite_patterns(rng, n, 32, nonneg_frac=0.99).view(np.float32)
+            g = _finite_patterns(rng, n, 16)
+            for x in (m, v):
+                hit = rng.random(n) < 1e-3
+                x[hit] = np.where(rng.random(int(hit.sum())) < 0.5, np.inf, -np.inf)
+            st.master[:n].copy_(torch.from_numpy(p.copy()))
+            st.exp_avg[:n].copy_(torch.from_numpy(m.copy()))
+            st.exp_avg_sq[:n].copy_(torch.from_numpy(v.copy()))
+            st.grads[0][0].view(torch.int16).copy_(torch.from_numpy(g.view(np.int16).copy()))
+            hp = dict(lr=1e-3, beta1=b1, beta2=b2, eps=1e-8, weight_decay=0.1, clip=0.0)
+            st.accumulate(0)
+            st.norm()
+            st.adamw(hp, step=step)
+            torch.cuda.synchronize()
+            wb = np.zeros(n, np.uint16)
+            with np.errstate(all="ignore"):
+                o.step(g.reshape(1, n), p, m, v, step=step, w=wb, **hp)
+            for name, gpu, ref in (("master", st.master, p), ("exp_avg", st.exp_avg, m),
+                                   ("exp_avg_sq", st.exp_avg_sq, v)):
+                x = gpu[:n].cpu().numpy()
+                assert np.array_equal(np.isnan(x), np.isnan(ref)), \
+                    f"{name}: NaN positions differ (beta1 {b1}, beta2 {b2}, t {step})"
+                keep = ~np.isnan(ref)
+                assert np.array_equal(x[keep].view(np.uint32), ref[keep].view(np.uint32)), \
+                    f"{name} (beta1 {b1}, beta2 {b2}, t {step})"
+            wg = st.weights[0].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(_bf16_nan(wg), _bf16_nan(wb))
+            keep = ~_bf16_nan(wb)
+            assert np.array_equal(wg[keep], wb[keep]), f"weights (beta1 {b1}, beta2 {b2}, t {step})"
+            if b2 == 0.0:
+                assert np.isinf(p).any()    # an infinite m over a finite v: an infinite weight
+    finally:
+        st.close()
+
+
 def _plan_from_temporaries(w):
     """A plan over tensors that nothing but the plan references."""
     start, ln, off, ae = B.z1_shard_plan(w.numel, w.dp_size, w.rank)
