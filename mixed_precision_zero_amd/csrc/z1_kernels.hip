@@ -144,23 +144,97 @@ __device__ __forceinline__ void dd_add_sq(double &hi, double &lo, float a)
     lo = lo + e;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double x, int mask)
+// Cross-lane moves of a binary64 value, as two 32-bit halves.  pair32 and
+// pair16 give, in every lane, the values of the two lanes l and l ^ 32 (or
+// l ^ 16) in lane order (v_permlane32_swap / v_permlane16_swap with the
+// value as both operands); dpp_d<CTRL> reads the lane that the DPP control
+// names (row_ror:N rotates within a row of 16 lanes, quad_perm permutes
+// within a quad).  All of them run on the vector ALU; none goes through the
+// LDS crossbar as a generic lane shuffle does.
+__device__ __forceinline__ void pair32(double x, double &a, double &b)
 {
-    return __shfl_xor(x, mask, 64);
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                    false, false);
+    a = __longlong_as_double((long long)(((uint64_t)h[0] << 32) | l[0]));
+    b = __longlong_as_double((long long)(((uint64_t)h[1] << 32) | l[1]));
 }
 
-// Fixed-order reduction of a double-double across the workgroup; every
-// combine is symmetric in its operands, so the butterfly leaves the same
-// value in every lane and the result depends only on the inputs' placement.
-template <int NT>
-__device__ __forceinline__ void block_reduce_dd(double &hi, double &lo, DD *lds)
+__device__ __forceinline__ void pair16(double x, double &a, double &b)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                    false, false);
+    a = __longlong_as_double((long long)(((uint64_t)h[0] << 32) | l[0]));
+    b = __longlong_as_double((long long)(((uint64_t)h[1] << 32) | l[1]));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF,
+                                                              0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                              0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+constexpr int kDppRowRor8 = 0x128;  // lane p of a row reads lane (p - 8) mod 16
+constexpr int kDppRowRor4 = 0x124;  // ... (p - 4) mod 16
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+
+// Fixed-order sum of a double-double over the 64 lanes of a wave (all lanes
+// active), left in every lane: a butterfly over lane distances 32, 16, 8, 4,
+// 2 and 1, each step adding the value of lane l ^ d.  Every combine is
+// symmetric in its operands, so after each step all lanes of a group hold
+// the same value; that is why the row rotations meet the right partners
+// (after distances 32 and 16 a lane's value depends only on its position p
+// in the row, and p - 8 mod 16 is p ^ 8; after 8 it depends on p mod 8, and
+// p - 4 is p ^ 4 mod 8).  The result depends only on the inputs' placement.
+__device__ __forceinline__ void wave_reduce_dd(double &hi, double &lo)
+{
+    double ah, bh, al, bl;
+    pair32(hi, ah, bh);
+    pair32(lo, al, bl);
+    hi = ah;
+    lo = al;
+    dd_add(hi, lo, bh, bl);
+    pair16(hi, ah, bh);
+    pair16(lo, al, bl);
+    hi = ah;
+    lo = al;
+    dd_add(hi, lo, bh, bl);
+    dd_add(hi, lo, dpp_d<kDppRowRor8>(hi), dpp_d<kDppRowRor8>(lo));
+    dd_add(hi, lo, dpp_d<kDppRowRor4>(hi), dpp_d<kDppRowRor4>(lo));
+    dd_add(hi, lo, dpp_d<kDppQuadXor2>(hi), dpp_d<kDppQuadXor2>(lo));
+    dd_add(hi, lo, dpp_d<kDppQuadXor1>(hi), dpp_d<kDppQuadXor1>(lo));
+}
+
+// The same butterfly with generic lane shuffles (ds_bpermute through the LDS
+// crossbar): the bits of wave_reduce_dd.  The multi-wave kernels keep it:
+// their waves have more vector work to overlap, and on the resident 4-slot
+// pass the vector-ALU form ran 0.1-0.3% slower (7B shard, four alternations),
+// while on the one-wave passes it took 35-40 us off the 7B last pass.
+__device__ __forceinline__ void wave_reduce_dd_lds(double &hi, double &lo)
 {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        const double ohi = shfl_xor_d(hi, off);
-        const double olo = shfl_xor_d(lo, off);
+        const double ohi = __shfl_xor(hi, off, 64);
+        const double olo = __shfl_xor(lo, off, 64);
         dd_add(hi, lo, ohi, olo);
     }
+}
+
+// Fixed-order reduction of a double-double across the workgroup: each wave's
+// sum, then the waves' sums in wave order.
+template <int NT>
+__device__ __forceinline__ void block_reduce_dd(double &hi, double &lo, DD *lds)
+{
+    wave_reduce_dd_lds(hi, lo);
     constexpr int kWaves = NT / 64;
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
@@ -520,12 +594,7 @@ __global__ __launch_bounds__(kWave) void k_accum_slots_wave(
         }
     }
     if (LAST) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double ohi = shfl_xor_d(hi, off);
-            const double olo = shfl_xor_d(lo, off);
-            dd_add(hi, lo, ohi, olo);
-        }
+        wave_reduce_dd(hi, lo);
         if (t == 0)
             partials[b] = DD{hi, lo};
     }
@@ -605,12 +674,7 @@ __global__ __launch_bounds__(kWave) void k_accum_arena(SlotBases sb,
         }
     }
     if (LAST) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double ohi = shfl_xor_d(hi, off);
-            const double olo = shfl_xor_d(lo, off);
-            dd_add(hi, lo, ohi, olo);
-        }
+        wave_reduce_dd(hi, lo);
         if (t == 0)
             partials[b] = DD{hi, lo};
     }
