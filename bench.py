@@ -444,6 +444,12 @@ def main():
              "adamw": rate(BYTES_ADAMW * L, adam_avg, adam_probes),
              "H1_norm_plus_adamw": rate(BYTES_ADAMW * L, adam_avg + norm_avg, adam_probes),
              "H3_step": rate(acc_b + BYTES_ADAMW * L, ms_step)}
+    if "slot" in variants:
+        # the step with one accumulation call per micro-batch (10K + 26 bytes
+        # per element), timed in the same process beside the headline
+        x = alt if head_resident else r
+        rates["H3_per_call"] = rate((accum_bytes(w.n_micro, False) + BYTES_ADAMW) * L,
+                                    x["ms_step"])
 
     out = {
         "metric": ("optimizer-step params/s and achieved HBM GB/s (% of MI355X peak), 7B shard"

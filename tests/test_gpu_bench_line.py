@@ -42,3 +42,8 @@ def test_bench_line_contract(walk):
     assert cb["unit"] == "params/s" and "whole-shard" in cb["sample"]
     rates = d["rates"]
     assert rates["adamw"]["same_mix_probe"] in ("adamw_traffic", "adamw_traffic_wave")
+    # both forms of the whole step: the headline (resident slots) and the one
+    # with an accumulation call per micro-batch, each over its own bytes
+    v = d["accum_variants"]
+    assert abs(rates["H3_step"]["GBps"] - v["resident"]["step_hbm_GBps"]) < 1e-9 * v["resident"]["step_hbm_GBps"]
+    assert abs(rates["H3_per_call"]["GBps"] - v["slot"]["step_hbm_GBps"]) < 1e-9 * v["slot"]["step_hbm_GBps"]
