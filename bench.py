@@ -14,11 +14,18 @@ same step with one z1_accum_grads call per micro-batch (36 bytes per element)
 is timed after it and reported under accum_variants.  Both store the same
 bits.  --accum slot makes the per-micro-batch form the headline.
 
-Prints ONE JSON line (rank 0).  Besides the driver's fields it carries
+Prints ONE JSON line (rank 0).  Besides metric, value, unit, timing and the
+workload's config it carries
   roofline      the dominant kernel (AdamW) against the 8 TB/s HBM peak, with
                 algorithmic bytes per launch / its mean duration measured with
-                events on the launch stream;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+                events on the launch stream, and the HBM bytes the committed
+                counter runs measured for the same kernel source;
+  rates         each part of the step (accumulation, AdamW, norm + AdamW, the
+                whole step in both accumulation forms) against the peak and
+                against the fastest traffic-only probe of the same mix run on
+                the step's own buffers;
+  cpu_baseline  the CPU oracle timed on --cpu-steps whole-shard steps of the
+                same workload on the host's cores.
 """
 from __future__ import annotations
 
