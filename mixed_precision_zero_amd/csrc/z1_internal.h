@@ -43,7 +43,10 @@ constexpr int kAdamPerCUTiles = Z1_ADAM_CAP_TILES;
 constexpr int kAdamPerCUChunks = Z1_ADAM_CAP_CHUNKS;
 constexpr int kMaxSlots = 16;    // micro-batch slots one multi-slot pass reads
 constexpr int kFinBlock = 256;
-constexpr int kFinStages = 256;  // first-level workgroups of the norm reduction
+// first-level workgroups of the norm reduction (1024 were slower: 40 against
+// 20 us for the 3.3M partials of a one-wave last pass on the 7B shard)
+constexpr int kFinStages = 256;
+constexpr int kFinUnroll = 8;    // partials each finalise thread loads at once
 // Arena offsets share the slice start's residue mod kArenaResidue elements:
 // 64 elements are one 128-byte cache line of bf16 (two of fp32), so a piece
 // that starts at a multiple of chunk_elems inside its tensor starts on a line
@@ -116,13 +119,14 @@ struct LaunchGeom {
 // one workgroup per tile, one norm partial per tile and per boundary
 // segment), else on the chunk table with sub workgroups per piece (one norm
 // partial per workgroup; uncapped grids only).  Passes of 2 to
-// kSlotsOneWave - 1 slots, and capped grids, keep 256-lane workgroups (one
-// partial per piece).  Measured on packed slots against 256-lane workgroups,
-// alternating: one slot (per call) 5-11% faster on the arena walk and 1-7%
-// on the chunk table; 8 and 16 slots 10% and 8% on the chunk table and
-// 2-6% more on the arena walk; 4 slots 7% slower on the chunk table and the
-// same or 3-5% slower on the arena walk (too few loads per lane to cover
-// each workgroup's lookups or its norm).
+// kSlotsOneWave - 1 slots take the arena walk too when its arena has no
+// boundary segment (slots_arena); otherwise, and on capped grids, they keep
+// 256-lane workgroups (one partial per piece).  Measured on packed slots
+// against 256-lane workgroups, alternating: one slot (per call) 5-11% faster
+// on the arena walk and 1-7% on the chunk table; 8 and 16 slots 10% and 8%
+// on the chunk table and 2-6% more on the arena walk; 4 slots 7% slower on
+// the one-wave chunk walk (too few loads per lane to cover each
+// workgroup's lookups).
 constexpr int kSlotsOneWave = 8;
 
 inline bool slots_wide_or_single(int n_slots)
@@ -130,9 +134,18 @@ inline bool slots_wide_or_single(int n_slots)
     return n_slots == 1 || n_slots >= kSlotsOneWave;
 }
 
+// The arena walk (packed plans that have one) takes single and wide passes,
+// and passes of 2 to kSlotsOneWave - 1 slots when the arena has no boundary
+// segments.  Measured against the 256-lane chunk-table kernel on the same
+// packed slots, alternating in one process: the 4-slot pass of the 7B shard
+// (no boundary tile) 0.6-2.8% faster in seven processes (with its finalise,
+// which then sums one partial per tile, 3.3M instead of 206K, 0.1-1.5%),
+// that of SmolLM-135M (211 boundary tiles) 1.4-8.5% slower in five, and no
+// faster with its boundary segments dispatched first or with two tiles per
+// workgroup.
 inline bool slots_arena(const LaunchGeom &geo, int n_slots)
 {
-    return geo.arena.n_tiles > 0 && slots_wide_or_single(n_slots);
+    return geo.arena.n_tiles > 0 && (slots_wide_or_single(n_slots) || geo.arena.n_segs == 0);
 }
 
 inline bool slots_one_wave(const LaunchGeom &geo, int n_slots)

@@ -94,6 +94,31 @@ def test_ragged_small_arena_tiles_random_multipliers():
          wd_scale=[float(x) for x in rng.choice([0.0, 0.5, 1.0], n)])
 
 
+# A list whose slices are all whole arena tiles (every numel a multiple of
+# dp_size * 256): its arena has no boundary segment, so passes of 2 to 7
+# resident slots take the arena walk as well.
+TILED = W.Workload(name="tiled", shapes=((1024, 64), (4096,), (512, 512), (2048,), (3072, 8)),
+                   dp_size=4, rank=2, n_micro=27, grad_sigma=1e-2, lr=1e-3, weight_decay=0.1,
+                   clip=1.0, steps=2)
+
+
+@pytest.mark.parametrize("ranges", [[(0, 2), (2, 5), (5, 9), (9, 14), (14, 20), (20, 27)],
+                                    [(0, 7), (7, 13), (13, 18), (18, 22), (22, 25), (25, 27)]])
+def test_narrow_passes_on_the_arena_walk(ranges):
+    """Passes of 2, 3, 4, 5, 6 and 7 resident slots on the arena walk, each as
+    a step's first, a middle or its last pass: the oracle's bits."""
+    import harness
+    h = harness.Parity(TILED, layout="packed", walk="arena_tiles", ranges=ranges)
+    try:
+        info = h.st.plan.info
+        assert info.adamw_tiles > 0 and info.boundary_tiles == 0
+        for _ in range(TILED.steps):
+            harness.assert_report(h.step())
+        assert h.canaries_intact()
+    finally:
+        h.close()
+
+
 def test_walks_agree_on_the_same_buffers():
     """The chunk walk and the arena walk over the same buffers store the same
     bits (one step from the same state with each)."""
