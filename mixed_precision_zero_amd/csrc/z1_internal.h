@@ -119,14 +119,13 @@ struct LaunchGeom {
 // one workgroup per tile, one norm partial per tile and per boundary
 // segment), else on the chunk table with sub workgroups per piece (one norm
 // partial per workgroup; uncapped grids only).  Passes of 2 to
-// kSlotsOneWave - 1 slots take the arena walk too when its arena has no
-// boundary segment (slots_arena); otherwise, and on capped grids, they keep
-// 256-lane workgroups (one partial per piece).  Measured on packed slots
-// against 256-lane workgroups, alternating: one slot (per call) 5-11% faster
-// on the arena walk and 1-7% on the chunk table; 8 and 16 slots 10% and 8%
-// on the chunk table and 2-6% more on the arena walk; 4 slots 7% slower on
-// the one-wave chunk walk (too few loads per lane to cover each
-// workgroup's lookups).
+// kSlotsOneWave - 1 slots, and capped grids, keep 256-lane workgroups (one
+// partial per piece).  Measured on packed slots against 256-lane
+// workgroups, alternating: one slot (per call) 5-11% faster on the arena
+// walk and 1-7% on the chunk table; 8 and 16 slots 10% and 8% on the chunk
+// table and 2-6% more on the arena walk; 4 slots 7% slower on the one-wave
+// chunk walk (too few loads per lane to cover each workgroup's lookups) and
+// no faster on the arena walk (below).
 constexpr int kSlotsOneWave = 8;
 
 inline bool slots_wide_or_single(int n_slots)
@@ -134,18 +133,16 @@ inline bool slots_wide_or_single(int n_slots)
     return n_slots == 1 || n_slots >= kSlotsOneWave;
 }
 
-// The arena walk (packed plans that have one) takes single and wide passes,
-// and passes of 2 to kSlotsOneWave - 1 slots when the arena has no boundary
-// segments.  Measured against the 256-lane chunk-table kernel on the same
-// packed slots, alternating in one process: the 4-slot pass of the 7B shard
-// (no boundary tile) 0.6-2.8% faster in seven processes (with its finalise,
-// which then sums one partial per tile, 3.3M instead of 206K, 0.1-1.5%),
-// that of SmolLM-135M (211 boundary tiles) 1.4-8.5% slower in five, and no
-// faster with its boundary segments dispatched first or with two tiles per
-// workgroup.
+// The arena walk (packed plans that have one) takes single and wide passes.
+// Passes of 2 to kSlotsOneWave - 1 slots keep the 256-lane chunk kernel:
+// on the arena walk the 7B shard's 4-slot pass (no boundary tile) ran
+// 0.3-2.8% faster, but its finalise then sums one partial per tile (3.3M
+// instead of 206K, 21 against 12 us), which left pass and finalise together
+// even (three processes with the model's full-size gradients allocated, as
+// in the benchmark); SmolLM-135M's (211 boundary tiles) ran 1.4-8.5% slower.
 inline bool slots_arena(const LaunchGeom &geo, int n_slots)
 {
-    return geo.arena.n_tiles > 0 && (slots_wide_or_single(n_slots) || geo.arena.n_segs == 0);
+    return geo.arena.n_tiles > 0 && slots_wide_or_single(n_slots);
 }
 
 inline bool slots_one_wave(const LaunchGeom &geo, int n_slots)

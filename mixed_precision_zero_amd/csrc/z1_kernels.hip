@@ -1405,15 +1405,9 @@ hipError_t launch_accum_arena(const LaunchGeom &geo, const SlotBases &sb, int n_
 {
     if (!slots_arena(geo, n_slots))
         return hipErrorInvalidValue;
-    static_assert(kMaxSlots == 16, "one case per slot count 1..16");
+    static_assert(kMaxSlots == 16 && kSlotsOneWave == 8, "one case per slot count 1, 8..16");
     switch (n_slots) {
     case 1: launch_arena_g<1>(geo, sb, acc, partials, first, last, s); break;
-    case 2: launch_arena_g<2>(geo, sb, acc, partials, first, last, s); break;
-    case 3: launch_arena_g<3>(geo, sb, acc, partials, first, last, s); break;
-    case 4: launch_arena_g<4>(geo, sb, acc, partials, first, last, s); break;
-    case 5: launch_arena_g<5>(geo, sb, acc, partials, first, last, s); break;
-    case 6: launch_arena_g<6>(geo, sb, acc, partials, first, last, s); break;
-    case 7: launch_arena_g<7>(geo, sb, acc, partials, first, last, s); break;
     case 8: launch_arena_g<8>(geo, sb, acc, partials, first, last, s); break;
     case 9: launch_arena_g<9>(geo, sb, acc, partials, first, last, s); break;
     case 10: launch_arena_g<10>(geo, sb, acc, partials, first, last, s); break;

@@ -95,8 +95,7 @@ def test_ragged_small_arena_tiles_random_multipliers():
 
 
 # A list whose slices are all whole arena tiles (every numel a multiple of
-# dp_size * 256): its arena has no boundary segment, so passes of 2 to 7
-# resident slots take the arena walk as well.
+# dp_size * 256): no boundary tile at all.
 TILED = W.Workload(name="tiled", shapes=((1024, 64), (4096,), (512, 512), (2048,), (3072, 8)),
                    dp_size=4, rank=2, n_micro=27, grad_sigma=1e-2, lr=1e-3, weight_decay=0.1,
                    clip=1.0, steps=2)
@@ -104,9 +103,10 @@ TILED = W.Workload(name="tiled", shapes=((1024, 64), (4096,), (512, 512), (2048,
 
 @pytest.mark.parametrize("ranges", [[(0, 2), (2, 5), (5, 9), (9, 14), (14, 20), (20, 27)],
                                     [(0, 7), (7, 13), (13, 18), (18, 22), (22, 25), (25, 27)]])
-def test_narrow_passes_on_the_arena_walk(ranges):
-    """Passes of 2, 3, 4, 5, 6 and 7 resident slots on the arena walk, each as
-    a step's first, a middle or its last pass: the oracle's bits."""
+def test_narrow_passes_in_a_plan_without_boundary_tiles(ranges):
+    """Passes of 2, 3, 4, 5, 6 and 7 resident slots (256-lane chunk kernels)
+    in a packed plan whose AdamW takes the arena walk, each pass size as a
+    step's first, a middle or its last pass: the oracle's bits."""
     import harness
     h = harness.Parity(TILED, layout="packed", walk="arena_tiles", ranges=ranges)
     try:
