@@ -225,8 +225,8 @@ typedef enum z1_layout {
 
 /* How the AdamW step walks the shard (z1_bind.walk); the arithmetic and the
  * bits stored are the same either way.  AdamW runs one-wave workgroups of 256
- * elements (one 4-element vector per lane), at most 14 (arena tiles) or 20
- * (chunk table) resident per compute unit.
+ * elements (one 4-element vector per lane), at most 14 resident per compute
+ * unit on either walk.
  *   Z1_WALK_CHUNKS       chunk_elems / 256 workgroups per entry of the chunk
  *                        table (the accumulation and norm kernels always
  *                        walk it).
