@@ -228,8 +228,11 @@ typedef enum z1_layout {
  * elements (one 4-element vector per lane), at most 14 resident per compute
  * unit on either walk.
  *   Z1_WALK_CHUNKS       chunk_elems / 256 workgroups per entry of the chunk
- *                        table (the accumulation and norm kernels always
- *                        walk it).
+ *                        table.  (The walk also decides the accumulation:
+ *                        passes of one slot or of 8-16 slots take the
+ *                        arena tiles when the plan has them; passes of 2-7
+ *                        slots and the norm of a given acc always walk the
+ *                        chunk table.)
  *   Z1_WALK_ARENA_TILES  packed layout only: one workgroup per 256-element
  *                        tile of the arena, every stream addressed by arena
  *                        position, so a tile's loads depend on nothing
