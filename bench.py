@@ -93,8 +93,8 @@ def parse():
                          "reported beside")
     ap.add_argument("--walk", default="auto", choices=["auto", "chunks", "arena_tiles"],
                     help="how the AdamW step walks the shard (z1_walk; auto: the arena "
-                         "tiles of a packed plan with at most 1%% boundary tiles, else the "
-                         "chunk table)")
+                         "tiles of a plan with at most 1%% boundary tiles, else the chunk "
+                         "table)")
     ap.add_argument("--layout-steps", type=int, default=10,
                     help="steps timed with the other bf16 layout over the same arenas, "
                          "reported beside the headline (0 = skip)")

@@ -233,21 +233,24 @@ typedef enum z1_layout {
  *                        arena tiles when the plan has them; passes of 2-7
  *                        slots and the norm of a given acc always walk the
  *                        chunk table.)
- *   Z1_WALK_ARENA_TILES  packed layout only: one workgroup per 256-element
- *                        tile of the arena, every stream addressed by arena
- *                        position, so a tile's loads depend on nothing
- *                        fetched first.  A tile inside one slice takes its
- *                        tensor from a per-tile tag read after its loads are
- *                        issued; a tile that crosses a slice boundary (or
- *                        the arena's end) runs its slice segments one by one
- *                        (padding is never written).
- *   Z1_WALK_AUTO         arena tiles for a packed plan with at most 1% of
- *                        its tiles crossing a slice boundary (the loads of
- *                        such a tile are issued before its tag is known and
- *                        then discarded), otherwise the chunk table.
+ *   Z1_WALK_ARENA_TILES  one workgroup per 256-element tile of the arena;
+ *                        every fp32 stream is addressed by arena position,
+ *                        so a tile's loads depend on nothing fetched first.
+ *                        A tile inside one slice takes its tensor from a
+ *                        per-tile tag read after its loads are issued (with
+ *                        full-size bf16 tensors, also the tensor's entry of
+ *                        a per-tensor table for its bf16 store); a tile that
+ *                        crosses a slice boundary (or the arena's end) runs
+ *                        its slice segments one by one (padding is never
+ *                        written).
+ *   Z1_WALK_AUTO         arena tiles for a plan (either layout) with at
+ *                        most 1% of its tiles crossing a slice boundary (the
+ *                        loads of such a tile are issued before its tag is
+ *                        known and then discarded), otherwise the chunk
+ *                        table.
  * The arena walk runs one workgroup per tile, so AUTO keeps the chunk table
- * when max_blocks caps the grid.  Z1_WALK_ARENA_TILES with the full layout or
- * with max_blocks > 0, or any other value, is Z1_EINVAL at plan creation. */
+ * when max_blocks caps the grid.  Z1_WALK_ARENA_TILES with max_blocks > 0,
+ * or any other value, is Z1_EINVAL at plan creation. */
 typedef enum z1_walk {
     Z1_WALK_AUTO = 0,
     Z1_WALK_CHUNKS = 1,

@@ -101,6 +101,10 @@ struct ArenaWalk {
     int64_t n_full = 0;              // tiles that end inside the arena
     int64_t n_segs = 0;
     uint16_t *wbase = nullptr;       // the packed bf16 weight shard
+    // full-size bf16 tensors: device [n_tensors], the byte address of arena
+    // element 0 as tensor i's slice maps it (weights[i] + 2 (start_i -
+    // arena_off_i)); nullptr for packed plans
+    const int64_t *wdelta = nullptr;
 };
 
 struct LaunchGeom {

@@ -3,10 +3,11 @@
 // The step is a streaming, HBM-bound pass over one rank's shard (about 0.5
 // flop per byte), so nothing here uses MFMA.  Each kernel walks a
 // device-resident chunk table (a workgroup takes one piece of one tensor's
-// slice, or a 256-element block of it) or, in packed plans, the arena itself
-// in 256-element tiles; its lanes move 4 consecutive elements each with one
-// 16-byte fp32 access per arena and one 8-byte bf16 access, consecutive lanes
-// on consecutive addresses.  The fp32 arenas are laid out so that an arena
+// slice, or a 256-element block of it) or the arena itself in 256-element
+// tiles (AdamW, and in packed plans single and wide accumulation passes);
+// its lanes move 4 consecutive elements each with one 16-byte fp32 access
+// per arena and one 8-byte bf16 access, consecutive lanes on consecutive
+// addresses.  The fp32 arenas are laid out so that an arena
 // element and its bf16 element share their position within a vector (the
 // arena offset matches the slice start mod 64 elements), so the pieces cut
 // at multiples of the chunk size inside a tensor start on whole 128-byte
@@ -1139,21 +1140,24 @@ __global__ __launch_bounds__(kWave) void k_adamw(
     }
 }
 
-// AdamW over the arena of a packed plan (ArenaWalk): workgroup b takes tile b
-// (one block); past the tiles, workgroup n_tiles + i takes the i-th boundary
-// segment.  Every stream of a packed plan is addressed by arena position, so
-// a tile that ends inside the arena is loaded first, at addresses that depend
-// on nothing fetched; its tag, read after the loads are issued, names the
-// tensor whose slice holds it.  A tile that crosses a slice boundary (or the
+// AdamW over the arena of a plan (ArenaWalk): workgroup b takes tile b (one
+// block); past the tiles, workgroup n_tiles + i takes the i-th boundary
+// segment.  Every fp32 stream is addressed by arena position, so a tile that
+// ends inside the arena is loaded first, at addresses that depend on nothing
+// fetched; its tag, read after the loads are issued, names the tensor whose
+// slice holds it (and, FULL, with full-size bf16 tensors, the entry of the
+// per-tensor table that places its bf16 store; a packed shard is addressed
+// by arena position too).  A tile that crosses a slice boundary (or the
 // arena's end) stores nothing, and neither does any tile when the per-step
 // table is exhausted; those leave through discard_lane, so the update and
 // stores of a live tile stay one unconditional sequence whose waits count its
 // own stores.  Same arithmetic, constants, table handling and twin
 // (MATH = false) as k_adamw.
-template <bool MATH, bool TABLE>
+template <bool MATH, bool TABLE, bool FULL>
 __global__ __launch_bounds__(kWave) void k_adamw_tiles(
     const int32_t *__restrict__ tags, const Chunk *__restrict__ segs, int64_t n_tiles,
-    int64_t n_full, uint16_t *__restrict__ wbase, uint16_t *const *__restrict__ wtab,
+    int64_t n_full, uint16_t *__restrict__ wbase, const int64_t *__restrict__ wdelta,
+    uint16_t *const *__restrict__ wtab,
     const Scale *__restrict__ scales, const float *__restrict__ acc, float *__restrict__ master,
     float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq, const AdamConsts k_arg,
     const double *__restrict__ S, const AdamConsts *__restrict__ table, int64_t n_rows,
@@ -1184,7 +1188,14 @@ __global__ __launch_bounds__(kWave) void k_adamw_tiles(
     }
     const double c = MATH ? clip_coef(k, S) : 1.0;
     const TensorRate tr = MATH ? tensor_rate(k, scales[tag]) : TensorRate{};
-    gmem<char> *wb = reinterpret_cast<gmem<char> *>(to_global(wbase)) + q0 * 8;
+    // the bf16 weight of arena element e: the packed shard's element e, or
+    // (full-size tensors) byte wdelta[tag] + 2e, the tensor's element
+    // start + (e - arena offset)
+    gmem<char> *wb;
+    if constexpr (FULL)
+        wb = reinterpret_cast<gmem<char> *>(wdelta[tag]) + q0 * 8;
+    else
+        wb = reinterpret_cast<gmem<char> *>(to_global(wbase)) + q0 * 8;
     update_store_lane<MATH>(x, pb, mb, vb, wb, o, k, tr, c);
 }
 
@@ -1476,9 +1487,15 @@ void launch_adamw_kernel(const LaunchGeom &geo, uint16_t *const *weight_tab, con
     const size_t lds = geo.adam_lds;
     if (geo.arena.n_tiles > 0) {
         const ArenaWalk &aw = geo.arena;
-        k_adamw_tiles<MATH, TABLE><<<dim3((unsigned)(aw.n_tiles + aw.n_segs)), block, lds, s>>>(
-            aw.tags, aw.segs, aw.n_tiles, aw.n_full, aw.wbase, weight_tab, scales, acc, master, m,
-            v, k, S, table, n_rows, state);
+        const dim3 grid((unsigned)(aw.n_tiles + aw.n_segs));
+        if (aw.wdelta)
+            k_adamw_tiles<MATH, TABLE, true><<<grid, block, lds, s>>>(
+                aw.tags, aw.segs, aw.n_tiles, aw.n_full, nullptr, aw.wdelta, weight_tab, scales,
+                acc, master, m, v, k, S, table, n_rows, state);
+        else
+            k_adamw_tiles<MATH, TABLE, false><<<grid, block, lds, s>>>(
+                aw.tags, aw.segs, aw.n_tiles, aw.n_full, aw.wbase, nullptr, weight_tab, scales,
+                acc, master, m, v, k, S, table, n_rows, state);
         return;
     }
     const int64_t n_work = geo.n_chunks * geo.sub;

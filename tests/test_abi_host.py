@@ -126,8 +126,8 @@ def _bind(**over):
     (dict(w0=0x10008), B.Z1_EALIGN), (dict(g1=0x30002), B.Z1_EALIGN),
     (dict(acc=0x70004), B.Z1_EALIGN),
     (dict(layout=2), B.Z1_EINVAL), (dict(walk=3), B.Z1_EINVAL), (dict(walk=-1), B.Z1_EINVAL),
-    (dict(walk=2), B.Z1_EINVAL),                       # arena tiles need the packed layout
-    (dict(walk=2, layout=1, max_blocks=4), B.Z1_EINVAL),   # ... and one workgroup per tile
+    (dict(walk=2, max_blocks=4), B.Z1_EINVAL),             # arena tiles run one workgroup
+    (dict(walk=2, layout=1, max_blocks=4), B.Z1_EINVAL),   # per tile, in either layout
     (dict(layout=1, w0=0), B.Z1_EINVAL), (dict(layout=1, g1=0), B.Z1_EINVAL),
     (dict(layout=1, w0=0x10008), B.Z1_EALIGN), (dict(layout=1, g1=0x30002), B.Z1_EALIGN),
 ])

@@ -43,9 +43,9 @@ def _tiles(st):
     return n_tiles, int((~inside).sum())
 
 
-def _run(w, steps, **kw):
+def _run(w, steps, layout="packed", **kw):
     import harness
-    h = harness.Parity(w, layout="packed", walk="arena_tiles", **kw)
+    h = harness.Parity(w, layout=layout, walk="arena_tiles", **kw)
     try:
         info = h.st.plan.info
         assert info.adamw_tiles > 0
@@ -74,6 +74,27 @@ def test_ragged_full_arena_tiles():
     """4096 tensors, 533 empty and 181 single-element slices: 2832 boundary
     tiles with their segments."""
     _run(W.RAGGED, 2, ranges=[(0, 16)])
+
+
+# Full-size bf16 tensors on the arena walk: the fp32 streams at arena
+# positions, each tile's bf16 store through its tensor's entry of the
+# per-tensor table; weights outside the rank's slices untouched.
+def test_full_layout_tiny_arena_tiles():
+    _run(W.TINY, 3, layout="full")
+
+
+def test_full_layout_ragged_small_arena_tiles():
+    _run(RAGGED_SMALL, 2, layout="full", ranges=[(0, 1), (1, 3)])
+
+
+def test_full_layout_dim0_smollm_arena_tiles_with_multipliers():
+    w = dataclasses.replace(W.SMOLLM_135M, name="smollm_dim0_full", dp_size=8, rank=5, n_micro=2)
+    lr_s, wd_s = W.mup_multipliers(w.shapes, 576)
+    _run(w, 2, layout="full", kind="dim0", lr_scale=lr_s, wd_scale=wd_s)
+
+
+def test_full_layout_llama1p7b_arena_tiles():
+    _run(W.LLAMA_1P7B, 2, layout="full", ranges=[(0, 8)])
 
 
 def test_flat_plan_arena_tiles():
@@ -218,8 +239,9 @@ def test_twin_touches_exactly_the_slices():
 @pytest.mark.parametrize("w,expect_tiles", [(W.LLAMA_7B, True), (W.RAGGED, True),
                                             (W.TINY, False)], ids=["llama7b", "ragged", "tiny"])
 def test_automatic_walk(w, expect_tiles):
-    """A packed plan takes the arena walk by itself when at most 1% of its
-    tiles cross a slice boundary; a full-layout plan never does."""
+    """A plan takes the arena walk by itself when at most 1% of its tiles
+    cross a slice boundary, with packed shards and with full-size tensors
+    alike."""
     from mixed_precision_zero_amd.shard import ShardStep
     st = ShardStep(w.shapes, w.dp_size, w.rank, 1, device="cuda", layout="packed")
     try:
@@ -231,6 +253,6 @@ def test_automatic_walk(w, expect_tiles):
         st.close()
     full = ShardStep(w.shapes, w.dp_size, w.rank, 1, device="cuda")
     try:
-        assert full.plan.info.adamw_tiles == 0
+        assert full.plan.info.adamw_tiles == (n_tiles if expect_tiles else 0)
     finally:
         full.close()

@@ -58,8 +58,9 @@ def random_case(i: int):
     if rng.random() < 0.3:
         kw["lr_scale"] = [float(x) for x in rng.uniform(0.1, 2.0, n)]
         kw["wd_scale"] = [float(x) for x in rng.choice([0.0, 1.0], n)]
-    # AdamW's walk, from a stream of its own (the draws above stay as they were)
-    if kw["layout"] == "packed" and kw["max_blocks"] == 0:
+    # AdamW's walk, from a stream of its own (the draws above stay as they were);
+    # both layouts take the arena walk when asked (AUTO only for packed plans)
+    if kw["max_blocks"] == 0:
         kw["walk"] = str(np.random.default_rng(5000 + i).choice(["auto", "chunks", "arena_tiles"]))
     return w, kw
 
