@@ -338,10 +338,11 @@ def test_two_plans_on_two_streams_are_independent():
 
 def test_adamw_runs_at_the_memory_limit_of_its_buffers():
     """Performance guard that does not depend on where the buffers land:
-    k_adamw must take no more than 15% longer than its no-arithmetic twin
-    (z1_probe_plan: the same chunk walk, loads and stores) on the same
-    buffers.  Measured ratios are 0.99-1.01; an update that became
-    compute-bound or a broken access pattern would fail this."""
+    AdamW must take no more than 15% longer than its no-arithmetic twin
+    (z1_probe_plan: the same walk, loads and stores; here the arena walk of
+    a full-size-tensor plan) on the same buffers.  Measured ratios are
+    1.0-1.03; an update that became compute-bound or a broken access
+    pattern would fail this."""
     w = dataclasses.replace(W.LLAMA_1P7B, n_micro=1)
     st = _fresh(w)
     try:
