@@ -1,10 +1,12 @@
-"""GPU parity of AdamW's arena walk (Z1_WALK_ARENA_TILES): packed plans whose
-AdamW step runs one workgroup per 256-element arena tile, tiles inside one
-slice straight-line and the slice segments of boundary tiles on workgroups of
-their own.  Same bar as the chunk walk (bit-exact against the oracle; padding
-never written), here on lists where most tiles are boundary tiles, with
-per-tensor multipliers, with an exhausted per-step table, and for the
-no-arithmetic twin.  Also checks the walk each plan picks by itself."""
+"""GPU parity of AdamW's arena walk (Z1_WALK_ARENA_TILES): plans whose AdamW
+step runs one workgroup per 256-element arena tile, tiles inside one slice
+straight-line and the slice segments of boundary tiles on workgroups of their
+own, with packed bf16 shards and with full-size bf16 tensors (stores placed
+through the per-tensor table).  Same bar as the chunk walk (bit-exact against
+the oracle; padding and weights outside the slices never written), here on
+lists where most tiles are boundary tiles, with per-tensor multipliers, with
+an exhausted per-step table, and for the no-arithmetic twin.  Also checks the
+walk each plan picks by itself."""
 import dataclasses
 
 import numpy as np
@@ -29,7 +31,7 @@ def _gpu():
 
 
 def _tiles(st):
-    """(tiles, boundary tiles) of a packed plan's arena, recounted here."""
+    """(tiles, boundary tiles) of a plan's arena, recounted here."""
     T = 256
     ae = int(st.arena_elems)
     n_tiles, n_full = (ae + T - 1) // T, ae // T

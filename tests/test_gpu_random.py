@@ -59,7 +59,7 @@ def random_case(i: int):
         kw["lr_scale"] = [float(x) for x in rng.uniform(0.1, 2.0, n)]
         kw["wd_scale"] = [float(x) for x in rng.choice([0.0, 1.0], n)]
     # AdamW's walk, from a stream of its own (the draws above stay as they were);
-    # both layouts take the arena walk when asked (AUTO only for packed plans)
+    # both layouts take the arena walk when asked, and under AUTO when boundaries are rare
     if kw["max_blocks"] == 0:
         kw["walk"] = str(np.random.default_rng(5000 + i).choice(["auto", "chunks", "arena_tiles"]))
     return w, kw
