@@ -1,4 +1,4 @@
-"""GPU-vs-oracle parity driver shared by the GPU tests.
+"""GPU-vs-oracle parity harness shared by the GPU tests.
 
 Inputs come from ``mixed_precision_zero_amd.workloads`` (seeded, full-size,
 generated on the device by torch); the HIP library reads the bound device
