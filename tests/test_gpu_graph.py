@@ -228,18 +228,19 @@ def _random_multipliers(n, seed):
     return lr_s, wd_s
 
 
-@pytest.mark.parametrize("w,mult,style,walk", [
-    (W.TINY, None, "cosine", None),
-    (W.TINY, "mup", "cosine", None),
-    (RAGGED_SMALL, None, "linear", None),
-    (RAGGED_SMALL, "random", "cosine", None),
-    (W.SMOLLM_135M, "mup", "cosine", None),
-    (W.TINY, "mup", "cosine", "arena_tiles"),
-    (RAGGED_SMALL, "random", "linear", "arena_tiles"),
+@pytest.mark.parametrize("w,mult,style,walk,layout", [
+    (W.TINY, None, "cosine", None, "full"),
+    (W.TINY, "mup", "cosine", None, "full"),
+    (RAGGED_SMALL, None, "linear", None, "full"),
+    (RAGGED_SMALL, "random", "cosine", None, "full"),
+    (W.SMOLLM_135M, "mup", "cosine", None, "full"),
+    (W.TINY, "mup", "cosine", "arena_tiles", "packed"),
+    (RAGGED_SMALL, "random", "linear", "arena_tiles", "packed"),
+    (RAGGED_SMALL, "random", "cosine", "arena_tiles", "full"),
 ], ids=["tiny_cosine", "tiny_mup_cosine", "ragged_small_linear", "ragged_small_mult_cosine",
         "smollm135m_mup_cosine", "tiny_mup_cosine_packed_arena",
-        "ragged_small_mult_linear_packed_arena"])
-def test_scheduled_graph_matches_oracle(w, mult, style, walk):
+        "ragged_small_mult_linear_packed_arena", "ragged_small_mult_cosine_full_arena"])
+def test_scheduled_graph_matches_oracle(w, mult, style, walk, layout):
     """[accumulate all slots, norm, z1_adamw_step_scheduled] captured once and
     replayed for 8 steps of a learning-rate schedule (3 warmup steps, 4 decay
     steps, then the minimum), with fresh gradients before every replay.  Each
@@ -247,8 +248,10 @@ def test_scheduled_graph_matches_oracle(w, mult, style, walk):
     oracle's own rate lr_at(t) (Nanotron Guide, config.yaml: learning_rate,
     lr_warmup_steps, lr_decay_steps, min_decay_lr), with the per-tensor
     multipliers as oracle segments: acc, S, master, m, v and the bf16 weights
-    bit for bit.  With walk set, the plan is packed and AdamW takes that
-    walk."""
+    bit for bit.  With walk set, AdamW takes that walk in the given bf16
+    layout (full-size tensors: its bf16 stores placed through the per-tensor
+    table, and its boundary segments by the chunk table); without, the plan
+    chooses."""
     import harness
     from mixed_precision_zero_amd import binding as B
     T, warm, decay = 8, 3, 4
@@ -261,11 +264,13 @@ def test_scheduled_graph_matches_oracle(w, mult, style, walk):
         lr_s, wd_s = W.mup_multipliers(w.shapes, w.shapes[0][1])
     elif mult == "random":
         lr_s, wd_s = _random_multipliers(len(w.shapes), seed=11)
-    layout = dict(layout="packed", walk=walk) if walk else {}
+    layout = dict(layout=layout, walk=walk) if walk else dict(layout=layout)
     h = harness.Parity(w, lr_scale=lr_s, wd_scale=wd_s, ranges=[(0, w.n_micro)], **layout)
     sched = None
     try:
         assert h.plan_matches()
+        if walk == "arena_tiles":
+            assert h.st.plan.info.adamw_tiles > 0
         sched = B.z1_schedule_create(**w.hp(), step=1, n_steps=T, lr_schedule=lr_sched)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -281,6 +286,8 @@ def test_scheduled_graph_matches_oracle(w, mult, style, walk):
             harness.assert_report(rep)
             assert B.z1_schedule_query(sched) == (t + 1, 0)
         assert h.canaries_intact()
+        if layout == "full":
+            assert h.weights_outside_slices_intact()
         del g
     finally:
         if sched is not None:
